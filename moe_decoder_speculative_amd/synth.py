@@ -1,0 +1,292 @@
+"""Seeded synthetic inputs for the MoE verification step.
+
+This module draws random numbers and shapes them; it holds none of the step's
+arithmetic (no normalisation, routing, expert or head computation).  The HIP
+library's tests, the benchmark and the CPU oracle's tests all take their inputs
+from here, so both sides see identical bytes for a given seed.
+
+The workloads mirror the pages' shapes:
+  * the decoder routes each token to 6 of 64 experts plus 2 shared experts over
+    12 layers ("Jina AI releases lightweight OCR model with built-in speculative
+    decoding", section "Lean architecture with a compressed encoder");
+  * a verification step carries the last committed token plus K = 3 FastMTP
+    drafts per sequence (same page, "Speculative decoding without accuracy
+    loss"), at batch 1 and at concurrency 32 (same page, "High throughput on
+    cheap hardware");
+  * a page is at most 1,156 visual tokens (256 global + 9 tiles of 100; same
+    page, "Lean architecture with a compressed encoder").
+Hidden size, SwiGLU width and vocabulary are not on the pages; the values
+below (1280, 896, 129280) are this library's reading of a DeepSeek-3B-MoE-sized
+decoder.  Weights are random N(0, 0.02^2); no trained checkpoint is used.
+"""
+
+from __future__ import annotations
+
+from concurrent.futures import ThreadPoolExecutor
+from dataclasses import dataclass, field, replace
+import os
+
+import numpy as np
+
+WEIGHT_STD = 0.02
+ZIPF_S = 1.1
+# strength of the router-logit shift that produces Zipf-skewed expert
+# popularity; chosen so the top-1 frequency over popularity ranks falls off
+# with a log-log slope near -1.1 at the first layer (checked by the tests).
+ZIPF_ALPHA = 0.33
+DRAFT_ACCEPT_P = 0.576
+
+
+@dataclass(frozen=True)
+class Workload:
+    name: str
+    H: int
+    E: int
+    k: int
+    S: int
+    I: int
+    V: int
+    L: int
+    B: int          # sequences (0 for a prefill workload)
+    K: int          # drafts per sequence
+    T: int          # tokens per step
+    dtype: str      # 'bf16' or 'f32'
+    routing: str    # 'uniform' or 'zipf'
+    drafts: str     # 'independent', 'replace_pos2' or 'none'
+    has_lm_head: bool
+    seed_id: int
+    eps: float = 1e-6
+    accept_p: float = DRAFT_ACCEPT_P
+
+    @property
+    def weight_seed(self) -> int:
+        return 1000 + self.seed_id
+
+    @property
+    def input_seed(self) -> int:
+        return 2000 + self.seed_id
+
+    @property
+    def draft_seed(self) -> int:
+        return 3000 + self.seed_id
+
+    def with_(self, **kw) -> "Workload":
+        return replace(self, **kw)
+
+
+def _verify(name, seed_id, B, **kw):
+    base = dict(H=1280, E=64, k=6, S=2, I=896, V=129280, L=1, K=3, dtype="bf16",
+                routing="uniform", drafts="independent", has_lm_head=True)
+    base.update(kw)
+    return Workload(name=name, B=B, T=B * (base["K"] + 1), seed_id=seed_id, **base)
+
+
+WORKLOADS = {
+    # tiny fp32 block: 8 experts top-2, 1 shared; drafts are the greedy picks
+    # with the second draft replaced by a wrong token
+    "tiny_fp32": Workload("tiny_fp32", H=256, E=8, k=2, S=1, I=128, V=1024, L=1,
+                          B=2, K=3, T=8, dtype="f32", routing="uniform",
+                          drafts="replace_pos2", has_lm_head=True, seed_id=1),
+    # batch-1 decode analogue: one block at the pages' routing shape
+    "decode_b1": _verify("decode_b1", 2, B=1),
+    # concurrency-32 analogue with Zipf-skewed expert popularity
+    "decode_b32_zipf": _verify("decode_b32_zipf", 3, B=32, routing="zipf"),
+    # prefill: 8 pages x (1,156 visual + 64 prompt tokens), no LM head
+    "prefill_8pages": Workload("prefill_8pages", H=1280, E=64, k=6, S=2, I=896,
+                               V=129280, L=1, B=0, K=0, T=8 * (1156 + 64),
+                               dtype="bf16", routing="uniform", drafts="none",
+                               has_lm_head=False, seed_id=4),
+    # 12 blocks with residual between them, then the LM head
+    "stack12_b32_zipf": _verify("stack12_b32_zipf", 5, B=32, L=12, routing="zipf"),
+}
+
+
+# --------------------------------------------------------------------------
+# storage helpers (no arithmetic of the step)
+# --------------------------------------------------------------------------
+
+def to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """float32 -> bfloat16 bit patterns (uint16), round to nearest even, via torch."""
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to(torch.bfloat16)
+    return t.view(torch.int16).numpy().view(np.uint16)
+
+
+def bits_to_f32(u16: np.ndarray) -> np.ndarray:
+    return (np.asarray(u16, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def to_storage(x: np.ndarray, dtype: str) -> np.ndarray:
+    """float32 values in the workload's storage type (uint16 bits for bf16)."""
+    if dtype == "bf16":
+        return to_bf16_bits(x)
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def _rng(seed_seq) -> np.random.Generator:
+    return np.random.Generator(np.random.PCG64(seed_seq))
+
+
+# --------------------------------------------------------------------------
+# weights
+# --------------------------------------------------------------------------
+
+_TENSORS = ("router", "gate", "up", "down", "s_gate", "s_up", "s_down")
+
+
+def _tensor_shape(w: Workload, name: str):
+    return {
+        "router": (w.E, w.H),
+        "gate": (w.E, w.I, w.H),
+        "up": (w.E, w.I, w.H),
+        "down": (w.E, w.H, w.I),
+        "s_gate": (w.S, w.I, w.H),
+        "s_up": (w.S, w.I, w.H),
+        "s_down": (w.S, w.H, w.I),
+        "lm_head": (w.V, w.H),
+    }[name]
+
+
+def _draw_tensor(w: Workload, child, name: str) -> np.ndarray:
+    shape = _tensor_shape(w, name)
+    n = int(np.prod(shape))
+    vals = _rng(child).standard_normal(n, dtype=np.float32)
+    vals *= np.float32(WEIGHT_STD)
+    return to_storage(vals.reshape(shape), w.dtype)
+
+
+def gen_weights(w: Workload, layers=None, threads: int | None = None) -> dict:
+    """Seeded weights: each (layer, tensor) has its own spawned child of
+    SeedSequence(weight_seed), so any tensor is reproducible on its own.
+
+    Returns {'layers': [dict(gamma, router, gate, up, down, s_gate, s_up,
+    s_down)], 'final_gamma', 'lm_head'} with float32 arrays for 'f32' and
+    uint16 bfloat16 bit patterns for 'bf16'.  Norm gains are 1.
+    """
+    children = np.random.SeedSequence(w.weight_seed).spawn(w.L * len(_TENSORS) + 1)
+    layer_ids = list(range(w.L)) if layers is None else list(layers)
+    jobs = []
+    for l in layer_ids:
+        for i, name in enumerate(_TENSORS):
+            jobs.append((l, name, children[l * len(_TENSORS) + i]))
+    if w.has_lm_head:
+        jobs.append((None, "lm_head", children[w.L * len(_TENSORS)]))
+    threads = threads or min(16, len(os.sched_getaffinity(0)))
+    with ThreadPoolExecutor(threads) as ex:
+        outs = list(ex.map(lambda j: _draw_tensor(w, j[2], j[1]), jobs))
+    one = to_storage(np.ones(w.H, np.float32), w.dtype)
+    res = {"layers": [dict(gamma=one.copy()) for _ in layer_ids],
+           "final_gamma": one.copy(), "lm_head": None}
+    pos = {l: i for i, l in enumerate(layer_ids)}
+    for (l, name, _), arr in zip(jobs, outs):
+        if l is None:
+            res["lm_head"] = arr
+        else:
+            res["layers"][pos[l]][name] = arr
+    return res
+
+
+# --------------------------------------------------------------------------
+# hidden states
+# --------------------------------------------------------------------------
+
+class HiddenNoise:
+    """Sequential stream of N(0,1) hidden-state rows from SeedSequence(input_seed).
+
+    Rows are drawn in order; redrawing a row takes the next rows of the same
+    stream, so a fixed sequence of redraw requests gives fixed bytes."""
+
+    def __init__(self, w: Workload):
+        ss = np.random.SeedSequence(w.input_seed)
+        noise_ss, self._perm_ss = ss.spawn(2)
+        self._rng = _rng(noise_ss)
+        self.H = w.H
+
+    def draw(self, n_rows: int) -> np.ndarray:
+        return self._rng.standard_normal((n_rows, self.H), dtype=np.float32)
+
+    def zipf_permutations(self, L: int, E: int):
+        """One seeded permutation per layer: popularity rank -> expert id."""
+        g = _rng(self._perm_ss)
+        return [g.permutation(E) for _ in range(L)]
+
+
+def zipf_offset(w: Workload, routers_f32, perms, alpha: float = ZIPF_ALPHA) -> np.ndarray:
+    """A fixed hidden-state offset v that shifts every layer's router logits
+    towards a Zipf(s) popularity profile.
+
+    Target shift per layer: s_l[e] = alpha * (log p_rank(e) - mean), with
+    p_r proportional to r^-s over ranks r = 1..E and rank(e) given by the
+    layer's permutation.  v is the minimum-norm solution of R v = concat_l s_l,
+    R being the stacked router matrices (full row rank for these shapes).
+    """
+    E = w.E
+    logp = -ZIPF_S * np.log(np.arange(1, E + 1, dtype=np.float64))
+    logp -= logp.mean()
+    rows, rhs = [], []
+    for R_l, pi in zip(routers_f32, perms):
+        shift = np.empty(E)
+        shift[pi] = alpha * logp          # expert pi[r] has popularity rank r+1
+        rows.append(np.asarray(R_l, dtype=np.float64))
+        rhs.append(shift)
+    R = np.concatenate(rows, axis=0)
+    s = np.concatenate(rhs)
+    v, *_ = np.linalg.lstsq(R, s, rcond=None)
+    return v.astype(np.float32)
+
+
+def hidden_offset(w: Workload, weights: dict, noise: HiddenNoise) -> np.ndarray:
+    """Per-row additive offset of the workload: zero for uniform routing, the
+    Zipf offset otherwise."""
+    if w.routing != "zipf":
+        return np.zeros(w.H, dtype=np.float32)
+    routers = [bits_to_f32(lw["router"]) if lw["router"].dtype == np.uint16 else lw["router"]
+               for lw in weights["layers"]]
+    perms = noise.zipf_permutations(w.L, w.E)
+    return zipf_offset(w, routers, perms)
+
+
+# --------------------------------------------------------------------------
+# drafts
+# --------------------------------------------------------------------------
+
+def draft_randoms(w: Workload, B: int | None = None, K: int | None = None):
+    """Random numbers that decide the drafts: u [B,K] uniform in [0,1) and
+    r [B,K] uniform over {0..V-2} (a wrong token is r, skipping the correct one)."""
+    B = w.B if B is None else B
+    K = w.K if K is None else K
+    g = _rng(np.random.SeedSequence(w.draft_seed))
+    u = g.random((B, K))
+    r = g.integers(0, w.V - 1, size=(B, K))
+    return u, r
+
+
+def wrong_token(correct: np.ndarray, r: np.ndarray) -> np.ndarray:
+    """A token different from `correct`: r in {0..V-2} mapped past it."""
+    r = np.asarray(r, dtype=np.int64)
+    return np.where(r < correct, r, r + 1).astype(np.int32)
+
+
+def make_drafts(w: Workload, tstar_bk1: np.ndarray, u=None, r=None) -> np.ndarray:
+    """Drafts [B, K] given the verifier's picks tstar [B, K+1].
+
+    'independent': draft j equals tstar[b, j] with probability accept_p,
+    otherwise a uniformly random wrong token.
+    'replace_pos2': drafts are the picks with the second draft (position 2 of
+    the K+1 frame) replaced by a random wrong token.
+    """
+    tstar_bk1 = np.asarray(tstar_bk1)
+    B, K1 = tstar_bk1.shape
+    K = K1 - 1
+    if K == 0:
+        return np.zeros((B, 0), dtype=np.int32)
+    if u is None or r is None:
+        u, r = draft_randoms(w, B, K)
+    correct = tstar_bk1[:, :K].astype(np.int32)
+    if w.drafts == "replace_pos2":
+        d = correct.copy()
+        d[:, 1] = wrong_token(correct[:, 1], r[:, 1])
+        return d
+    if w.drafts == "independent":
+        return np.where(u < w.accept_p, correct, wrong_token(correct, r)).astype(np.int32)
+    raise ValueError(f"workload {w.name} has no drafts")
