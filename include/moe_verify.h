@@ -1,0 +1,206 @@
+/*
+ * moe_verify.h -- C ABI of the MI355X (gfx950) library that runs one
+ * speculative verification step of a mixture-of-experts decoder.
+ *
+ * What the step computes.  B sequences each carry K+1 positions: the last
+ * committed token and K drafts.  For every position the library runs L
+ * pre-norm MoE-FFN blocks (RMSNorm, a softmax router that keeps the top k of
+ * E routed experts, k routed SwiGLU experts plus S always-on shared experts,
+ * a gate-weighted combine and the residual add), a final RMSNorm, the LM
+ * head and a greedy arg-max; then, per sequence, it accepts the longest
+ * prefix of drafts that agree with those greedy picks and commits one more
+ * token of the verifier's own.  The committed tokens therefore equal plain
+ * greedy decoding.  Sources:
+ *   - page "Jina AI releases lightweight OCR model with built-in speculative
+ *     decoding", section "Lean architecture with a compressed encoder"
+ *     (64 routed + 2 shared experts, top-6 routing, 12 layers) and section
+ *     "Speculative decoding without accuracy loss" (greedy verification,
+ *     longest agreeing prefix plus one extra token, bonus when all drafts
+ *     match, output identical to greedy decoding);
+ *   - page "jina-ocr-v1 : Analyse de documents plus rapide sur des GPU a
+ *     budget limite", section "Modele et entrainement" (K = 3 drafts checked
+ *     greedily, committed sequence equals the verifier's greedy sequence).
+ * The pages give no layer internals: RMSNorm, SwiGLU, softmax-over-selected
+ * gates, combine order and the bf16 rounding points below are this library's
+ * plain reading of them.
+ *
+ * Numerics.  Storage type is float32 or bfloat16 (config.dtype).  All
+ * arithmetic is float32.  With bfloat16 storage, values are rounded to
+ * bfloat16 (nearest, ties to even) at exactly three points: the normalised
+ * activations (router/expert input and LM-head input), the SwiGLU activation
+ * silu(Wg x)*(Wu x), and each block's output x + m.  Top-k ties go to the
+ * lower expert index; arg-max ties to the lower token id.
+ *
+ * Layouts.  Every tensor is dense row-major; weights are [out][in] as in a
+ * linear layer.  T = B*(K+1) token rows, ordered sequence-major
+ * (row b*(K+1)+j is position j of sequence b).
+ *
+ * Streams and ownership.  Every entry point that takes `hip_stream` (a
+ * hipStream_t, NULL = the default stream) enqueues its work on that stream
+ * and returns without synchronising.  Outputs are valid once the stream has
+ * completed the work.  The caller owns every buffer it passes in.  A context
+ * owns repacked copies of the weights and its own workspace: calls on one
+ * context must not overlap (use one stream per context, or synchronise).
+ *
+ * Errors.  0 on success, otherwise a negative MOE_E* code; the message for
+ * the last failure on the calling thread is returned by
+ * moe_verify_last_error().  Argument errors are detected before any HIP
+ * runtime call is made.  No C++ exception crosses this interface.
+ */
+#ifndef MOE_VERIFY_H
+#define MOE_VERIFY_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MOE_OK 0
+#define MOE_EINVAL (-1)       /* null/misaligned pointer, bad size or count */
+#define MOE_EUNSUPPORTED (-2) /* a shape or dtype the kernels do not cover  */
+#define MOE_ENOMEM (-3)       /* device allocation failed                   */
+#define MOE_EHIP (-4)         /* a HIP runtime or launch error              */
+
+#define MOE_DTYPE_F32 0
+#define MOE_DTYPE_BF16 1
+
+/* Opaque context: repacked weights, workspace, launch plan. */
+typedef struct moe_verify_ctx moe_verify_ctx;
+
+/*
+ * Model and capacity description.
+ *   hidden     H, a multiple of 128, at most 1536 (bf16) / 768 (f32)
+ *   n_routed   E routed experts, 1..64 (one router lane per expert)
+ *   top_k      k experts per token, 1..min(E, 8)
+ *   n_shared   S always-on shared experts, 0..4
+ *   inter      I SwiGLU width, a multiple of 128, at most 2048
+ *   vocab      V LM-head rows, >= 1 (ignored without an LM head)
+ *   n_layers   L blocks, 1..64
+ *   max_tokens          largest T = B*(K+1) a verify step may use, 1..65536
+ *   max_prefill_tokens  largest T for moe_block_forward, 0..65536 (0: max_tokens)
+ *   k_max      largest K a verify step may use, 0..7
+ *   rms_eps    RMSNorm epsilon, > 0
+ *   dtype      MOE_DTYPE_F32 or MOE_DTYPE_BF16 (storage of every tensor)
+ *   has_lm_head 1: verify steps available; 0: only moe_block_forward
+ */
+typedef struct moe_verify_config {
+  int32_t hidden;
+  int32_t n_routed;
+  int32_t top_k;
+  int32_t n_shared;
+  int32_t inter;
+  int32_t vocab;
+  int32_t n_layers;
+  int32_t max_tokens;
+  int32_t max_prefill_tokens;
+  int32_t k_max;
+  float rms_eps;
+  int32_t dtype;
+  int32_t has_lm_head;
+} moe_verify_config;
+
+/*
+ * Device pointers to the weights, each 16-byte aligned, in the storage type.
+ *   router      [L][E][H]
+ *   w_gate      [L][E][I][H]      w_up   [L][E][I][H]     w_down [L][E][H][I]
+ *   s_gate      [L][S][I][H]      s_up   [L][S][I][H]     s_down [L][S][H][I]
+ *               (may be NULL when S == 0)
+ *   norm_gamma  [L][H]   pre-block RMSNorm gains
+ *   final_gamma [H]      final RMSNorm gain (NULL when has_lm_head == 0)
+ *   lm_head     [V][H]   (NULL when has_lm_head == 0)
+ * moe_verify_init copies them (repacked); no pointer is kept afterwards.
+ */
+typedef struct moe_verify_weights {
+  const void* router;
+  const void* w_gate;
+  const void* w_up;
+  const void* w_down;
+  const void* s_gate;
+  const void* s_up;
+  const void* s_down;
+  const void* norm_gamma;
+  const void* final_gamma;
+  const void* lm_head;
+} moe_verify_weights;
+
+/*
+ * Optional device outputs for inspection and parity checks (any field may be
+ * NULL; every non-NULL pointer must be 16-byte aligned).  T is the step's
+ * token count; l indexes the layer.
+ *   topk_idx      int32 [L][T][k]  selected experts, descending router logit
+ *   topk_w        float [L][T][k]  gate weights (softmax over the selection)
+ *   expert_count  int32 [L][E]     tokens routed to each expert
+ *   expert_offset int32 [L][E+1]   exclusive prefix sum of expert_count
+ *   perm          int32 [L][T*k]   pair ids t*k+j grouped by expert, stable
+ *   moe_out       float [L][T][H]  block output before the residual add
+ *   hidden_out    storage [T][H]   residual stream after the last block
+ *   tstar         int32 [T]        greedy pick after each position
+ */
+typedef struct moe_verify_aux {
+  int32_t* topk_idx;
+  float* topk_w;
+  int32_t* expert_count;
+  int32_t* expert_offset;
+  int32_t* perm;
+  float* moe_out;
+  void* hidden_out;
+  int32_t* tstar;
+} moe_verify_aux;
+
+/*
+ * Validate `cfg`, allocate the context and repack the weights into it on
+ * `hip_stream`, then synchronise that stream (so the caller may free its
+ * weight tensors as soon as this returns).  On success *out receives the
+ * context; on failure *out is set to NULL and nothing is leaked.
+ * Errors: MOE_EINVAL (NULL cfg/weights/out, a NULL or misaligned required
+ * weight pointer, a size out of the ranges above), MOE_EUNSUPPORTED,
+ * MOE_ENOMEM, MOE_EHIP.
+ */
+int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* weights,
+                    void* hip_stream, moe_verify_ctx** out);
+
+/*
+ * One verification step (the pages' greedy verify of K drafts per sequence).
+ *   hidden    device, storage [B][K+1][H]: residual stream entering block 0
+ *   drafts    device, int32 [B][K]: draft j of sequence b proposes the token
+ *             at position j+1 and is compared with the pick after position j;
+ *             an id outside [0, V) simply never matches.  May be NULL if K == 0.
+ *   committed device out, int32 [B][K+1]: accepted picks, then -1 padding
+ *   counts    device out, int32 [B]: tokens committed, 1..K+1 (K+1 means all
+ *             drafts matched and the last token is the bonus)
+ * Requires has_lm_head; 1 <= B; 0 <= K <= k_max; B*(K+1) <= max_tokens.
+ * Asynchronous; allocates nothing.
+ */
+int moe_verify_step(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
+                    int32_t B, int32_t K, int32_t* committed, int32_t* counts,
+                    void* hip_stream);
+
+/* moe_verify_step plus the optional outputs in `aux` (aux may be NULL). */
+int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
+                       int32_t B, int32_t K, int32_t* committed, int32_t* counts,
+                       const moe_verify_aux* aux, void* hip_stream);
+
+/*
+ * One MoE-FFN block of layer `layer` over T token rows (the prefill path):
+ *   x  device, storage [T][H] in;  y  device, storage [T][H] out = x + MoE(RMSNorm(x)).
+ * x and y may not overlap.  aux (may be NULL) receives layer-0-indexed
+ * topk_idx/topk_w/expert_count/expert_offset/perm/moe_out for this block;
+ * hidden_out and tstar are ignored.  Requires 1 <= T <= max_prefill_tokens
+ * (or <= max_tokens when max_prefill_tokens is 0).  Asynchronous.
+ */
+int moe_block_forward(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, void* y,
+                      const moe_verify_aux* aux, void* hip_stream);
+
+/* Free everything the context owns.  NULL is accepted.  Synchronises the
+ * device work the context may still have in flight. */
+void moe_verify_destroy(moe_verify_ctx* ctx);
+
+/* Message of the last failure on the calling thread ("" if none). */
+const char* moe_verify_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_VERIFY_H */

@@ -1,0 +1,461 @@
+// C ABI of the MoE speculative verification library (declared in
+// include/moe_verify.h): argument validation, context creation with weight
+// repacking, workspace, and the launch sequence of one verification step.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "moe_verify.h"
+
+using moe::bf16_t;
+
+namespace moe {
+int lmhead_row_multiple();
+}
+
+struct moe_verify_ctx {
+  moe_verify_config cfg;
+  moe::Dims d;
+  int device = 0;
+  size_t esize = 0;         // bytes per stored element
+  int64_t tw = 0;           // workspace token capacity
+  std::vector<void*> allocs;
+
+  // repacked weights
+  char* router = nullptr;   // bf16 tiled [L][64/16][H/32][512]; f32 [L][E][H]
+  char* gate = nullptr;     // [L][E+S] experts (tiled or row-major)
+  char* up = nullptr;
+  char* down = nullptr;
+  char* gamma = nullptr;    // [L][H] storage
+  char* final_gamma = nullptr;
+  char* lm = nullptr;       // bf16 tiled [Vpad/16][H/32][512]; f32 [V][H]
+  size_t router_layer = 0, gate_layer = 0, down_layer = 0;
+
+  // workspace
+  char* xres = nullptr;     // [tw][H] storage
+  char* xhat = nullptr;     // [tw][H] storage
+  int* idx[2] = {nullptr, nullptr};   // [tw][k]
+  float* w[2] = {nullptr, nullptr};   // [tw][k]
+  int* cnt = nullptr;       // [E]
+  int* off = nullptr;       // [E+1]
+  int* perm = nullptr;      // [tw*k]
+  int* active = nullptr;    // [E]
+  int* n_active = nullptr;  // [1]
+  char* act = nullptr;      // [tw*(k+S)][I] storage
+  float* y = nullptr;       // [tw*(k+S)][H]
+  unsigned long long* keys = nullptr;  // [tw]
+  unsigned int* done = nullptr;
+};
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define MOE_HIP(expr)                                                                        \
+  do {                                                                                       \
+    hipError_t e_ = (expr);                                                                  \
+    if (e_ != hipSuccess) return fail(MOE_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)
+
+int validate_config(const moe_verify_config& c) {
+  auto bad = [](const std::string& m) { return fail(MOE_EINVAL, "config: " + m); };
+  if (c.dtype != MOE_DTYPE_F32 && c.dtype != MOE_DTYPE_BF16) return bad("dtype must be 0 (f32) or 1 (bf16)");
+  if (c.hidden < 128 || c.hidden % 128 != 0) return bad("hidden must be a multiple of 128");
+  if (c.dtype == MOE_DTYPE_BF16 && c.hidden > 1536) return bad("hidden must be at most 1536 for bf16");
+  if (c.dtype == MOE_DTYPE_F32 && c.hidden > 768) return bad("hidden must be at most 768 for f32");
+  if (c.inter < 128 || c.inter > 2048 || c.inter % 128 != 0) return bad("inter must be a multiple of 128 in [128, 2048]");
+  if (c.n_routed < 1 || c.n_routed > 64) return bad("n_routed must be in [1, 64]");
+  if (c.top_k < 1 || c.top_k > 8 || c.top_k > c.n_routed) return bad("top_k must be in [1, min(n_routed, 8)]");
+  if (c.n_shared < 0 || c.n_shared > 4) return bad("n_shared must be in [0, 4]");
+  if (c.n_layers < 1 || c.n_layers > 64) return bad("n_layers must be in [1, 64]");
+  if (c.max_tokens < 1 || c.max_tokens > 65536) return bad("max_tokens must be in [1, 65536]");
+  if (c.max_prefill_tokens < 0 || c.max_prefill_tokens > 65536) return bad("max_prefill_tokens must be in [0, 65536]");
+  if (c.k_max < 0 || c.k_max > 7) return bad("k_max must be in [0, 7]");
+  if (!(c.rms_eps > 0.0f) || !std::isfinite(c.rms_eps)) return bad("rms_eps must be a positive finite number");
+  if (c.has_lm_head != 0 && c.has_lm_head != 1) return bad("has_lm_head must be 0 or 1");
+  if (c.has_lm_head && (c.vocab < 1 || c.vocab > (1 << 24))) return bad("vocab must be in [1, 2^24]");
+  return MOE_OK;
+}
+
+int validate_weights(const moe_verify_config& c, const moe_verify_weights& w) {
+  struct Item { const void* p; const char* name; bool required; };
+  const Item items[] = {
+      {w.router, "router", true},      {w.w_gate, "w_gate", true},    {w.w_up, "w_up", true},
+      {w.w_down, "w_down", true},      {w.s_gate, "s_gate", c.n_shared > 0},
+      {w.s_up, "s_up", c.n_shared > 0}, {w.s_down, "s_down", c.n_shared > 0},
+      {w.norm_gamma, "norm_gamma", true}, {w.final_gamma, "final_gamma", c.has_lm_head != 0},
+      {w.lm_head, "lm_head", c.has_lm_head != 0},
+  };
+  for (const Item& it : items) {
+    if (!it.required) continue;
+    if (!it.p) return fail(MOE_EINVAL, std::string("weights: ") + it.name + " is NULL");
+    if (!aligned16(it.p)) return fail(MOE_EINVAL, std::string("weights: ") + it.name + " is not 16-byte aligned");
+  }
+  return MOE_OK;
+}
+
+int check_ptr(const void* p, const char* name, bool required) {
+  if (!p) return required ? fail(MOE_EINVAL, std::string(name) + " is NULL") : MOE_OK;
+  if (!aligned16(p)) return fail(MOE_EINVAL, std::string(name) + " is not 16-byte aligned");
+  return MOE_OK;
+}
+
+int check_aux(const moe_verify_aux* a) {
+  if (!a) return MOE_OK;
+  int r;
+  if ((r = check_ptr(a->topk_idx, "aux.topk_idx", false))) return r;
+  if ((r = check_ptr(a->topk_w, "aux.topk_w", false))) return r;
+  if ((r = check_ptr(a->expert_count, "aux.expert_count", false))) return r;
+  if ((r = check_ptr(a->expert_offset, "aux.expert_offset", false))) return r;
+  if ((r = check_ptr(a->perm, "aux.perm", false))) return r;
+  if ((r = check_ptr(a->moe_out, "aux.moe_out", false))) return r;
+  if ((r = check_ptr(a->hidden_out, "aux.hidden_out", false))) return r;
+  if ((r = check_ptr(a->tstar, "aux.tstar", false))) return r;
+  return MOE_OK;
+}
+
+int ctx_alloc(moe_verify_ctx* c, size_t bytes, char** out) {
+  void* p = nullptr;
+  if (bytes == 0) bytes = 16;
+  if (std::getenv("MOE_VERIFY_FAULT") && std::strcmp(std::getenv("MOE_VERIFY_FAULT"), "alloc") == 0)
+    return fail(MOE_ENOMEM, "device allocation failed (injected by MOE_VERIFY_FAULT=alloc)");
+  const hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ENOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
+  }
+  c->allocs.push_back(p);
+  *out = static_cast<char*>(p);
+  return MOE_OK;
+}
+
+template <typename P>
+int ctx_alloc_t(moe_verify_ctx* c, size_t bytes, P** out) {
+  char* p = nullptr;
+  const int r = ctx_alloc(c, bytes, &p);
+  *out = reinterpret_cast<P*>(p);
+  return r;
+}
+
+void ctx_free(moe_verify_ctx* c) {
+  if (!c) return;
+  if (!c->allocs.empty()) {
+    int cur = 0;
+    if (hipGetDevice(&cur) == hipSuccess && cur != c->device) (void)hipSetDevice(c->device);
+    (void)hipDeviceSynchronize();
+    for (void* p : c->allocs) (void)hipFree(p);
+    if (cur != c->device) (void)hipSetDevice(cur);
+  }
+  delete c;
+}
+
+// Repack the weights into the context.
+int repack(moe_verify_ctx* c, const moe_verify_weights& w, hipStream_t s) {
+  const moe_verify_config& g = c->cfg;
+  const int64_t L = g.n_layers, E = g.n_routed, S = g.n_shared, H = g.hidden, I = g.inter;
+  const size_t es = c->esize;
+  if (g.dtype == MOE_DTYPE_BF16) {
+    for (int64_t l = 0; l < L; ++l) {
+      const bf16_t* r = static_cast<const bf16_t*>(w.router) + l * E * H;
+      MOE_HIP(moe::launch_tile_bf16(r, 0, reinterpret_cast<bf16_t*>(c->router + l * c->router_layer), 1, (int)E, (int)H, 64, s));
+      struct Pair { const void* routed; const void* shared; char* dst; size_t layer; int R, C; };
+      const Pair ps[] = {{w.w_gate, w.s_gate, c->gate, c->gate_layer, (int)I, (int)H},
+                         {w.w_up, w.s_up, c->up, c->gate_layer, (int)I, (int)H},
+                         {w.w_down, w.s_down, c->down, c->down_layer, (int)H, (int)I}};
+      for (const Pair& p : ps) {
+        const int64_t mat = static_cast<int64_t>(p.R) * p.C;
+        bf16_t* dst = reinterpret_cast<bf16_t*>(p.dst + l * p.layer);
+        MOE_HIP(moe::launch_tile_bf16(static_cast<const bf16_t*>(p.routed) + l * E * mat, mat, dst, E, p.R, p.C, p.R, s));
+        if (S > 0)
+          MOE_HIP(moe::launch_tile_bf16(static_cast<const bf16_t*>(p.shared) + l * S * mat, mat, dst + E * mat, S, p.R,
+                                        p.C, p.R, s));
+      }
+    }
+    if (g.has_lm_head)
+      MOE_HIP(moe::launch_tile_bf16(static_cast<const bf16_t*>(w.lm_head), 0, reinterpret_cast<bf16_t*>(c->lm), 1,
+                                    g.vocab, (int)H, c->d.Vpad, s));
+  } else {
+    MOE_HIP(hipMemcpyAsync(c->router, w.router, L * E * H * es, hipMemcpyDeviceToDevice, s));
+    struct Pair { const void* routed; const void* shared; char* dst; int64_t mat; };
+    const Pair ps[] = {{w.w_gate, w.s_gate, c->gate, I * H}, {w.w_up, w.s_up, c->up, I * H},
+                       {w.w_down, w.s_down, c->down, H * I}};
+    for (const Pair& p : ps)
+      for (int64_t l = 0; l < L; ++l) {
+        char* dst = p.dst + l * (E + S) * p.mat * es;
+        MOE_HIP(hipMemcpyAsync(dst, static_cast<const char*>(p.routed) + l * E * p.mat * es, E * p.mat * es,
+                               hipMemcpyDeviceToDevice, s));
+        if (S > 0)
+          MOE_HIP(hipMemcpyAsync(dst + E * p.mat * es, static_cast<const char*>(p.shared) + l * S * p.mat * es,
+                                 S * p.mat * es, hipMemcpyDeviceToDevice, s));
+      }
+    if (g.has_lm_head)
+      MOE_HIP(hipMemcpyAsync(c->lm, w.lm_head, static_cast<size_t>(g.vocab) * H * es, hipMemcpyDeviceToDevice, s));
+  }
+  MOE_HIP(hipMemcpyAsync(c->gamma, w.norm_gamma, L * H * es, hipMemcpyDeviceToDevice, s));
+  if (g.has_lm_head) MOE_HIP(hipMemcpyAsync(c->final_gamma, w.final_gamma, H * es, hipMemcpyDeviceToDevice, s));
+  return MOE_OK;
+}
+
+int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t s, moe_verify_ctx* c) {
+  c->cfg = g;
+  c->esize = g.dtype == MOE_DTYPE_BF16 ? 2 : 4;
+  moe::Dims& d = c->d;
+  d.H = g.hidden; d.E = g.n_routed; d.k = g.top_k; d.S = g.n_shared; d.I = g.inter;
+  d.V = g.has_lm_head ? g.vocab : 0; d.L = g.n_layers; d.eps = g.rms_eps; d.bf16 = g.dtype == MOE_DTYPE_BF16;
+  const int mult = moe::lmhead_row_multiple();
+  d.Vpad = g.has_lm_head ? (d.bf16 ? (d.V + mult - 1) / mult * mult : d.V) : 0;
+  MOE_HIP(hipGetDevice(&c->device));
+
+  const int64_t L = g.n_layers, E = g.n_routed, S = g.n_shared, H = g.hidden, I = g.inter;
+  const size_t es = c->esize;
+  c->router_layer = (d.bf16 ? 64 : E) * H * es;
+  c->gate_layer = (E + S) * I * H * es;
+  c->down_layer = (E + S) * H * I * es;
+  int r;
+  if ((r = ctx_alloc(c, L * c->router_layer, &c->router))) return r;
+  if ((r = ctx_alloc(c, L * c->gate_layer, &c->gate))) return r;
+  if ((r = ctx_alloc(c, L * c->gate_layer, &c->up))) return r;
+  if ((r = ctx_alloc(c, L * c->down_layer, &c->down))) return r;
+  if ((r = ctx_alloc(c, L * H * es, &c->gamma))) return r;
+  if (g.has_lm_head) {
+    if ((r = ctx_alloc(c, H * es, &c->final_gamma))) return r;
+    if ((r = ctx_alloc(c, static_cast<size_t>(d.Vpad) * H * es, &c->lm))) return r;
+    if (d.bf16) MOE_HIP(hipMemsetAsync(c->lm, 0, static_cast<size_t>(d.Vpad) * H * es, s));
+  }
+
+  const int64_t tw = std::max<int64_t>(g.max_tokens, g.max_prefill_tokens);
+  c->tw = tw;
+  const int64_t rows = tw * (g.top_k + S);
+  if ((r = ctx_alloc(c, tw * H * es, &c->xres))) return r;
+  if ((r = ctx_alloc(c, tw * H * es, &c->xhat))) return r;
+  for (int i = 0; i < 2; ++i) {
+    if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->idx[i]))) return r;
+    if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(float), &c->w[i]))) return r;
+  }
+  if ((r = ctx_alloc_t(c, E * sizeof(int), &c->cnt))) return r;
+  if ((r = ctx_alloc_t(c, (E + 1) * sizeof(int), &c->off))) return r;
+  if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->perm))) return r;
+  if ((r = ctx_alloc_t(c, E * sizeof(int), &c->active))) return r;
+  if ((r = ctx_alloc_t(c, 16, &c->n_active))) return r;
+  if ((r = ctx_alloc(c, rows * I * es, &c->act))) return r;
+  if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->y))) return r;
+  if ((r = ctx_alloc_t(c, tw * sizeof(unsigned long long), &c->keys))) return r;
+  if ((r = ctx_alloc_t(c, 16, &c->done))) return r;
+  MOE_HIP(hipMemsetAsync(c->done, 0, 16, s));
+
+  if ((r = repack(c, w, s))) return r;
+  MOE_HIP(hipStreamSynchronize(s));
+  return MOE_OK;
+}
+
+// The blocks of a step: for layer l, norm+router (with the combine of layer
+// l-1 when l > 0), permutation, expert up, expert down.
+int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_aux* aux, int layer0, int nlayers,
+               hipStream_t s, const void** x_last) {
+  const moe::Dims& d = c->d;
+  const moe_verify_config& g = c->cfg;
+  const int64_t H = g.hidden, k = g.top_k, E = g.n_routed;
+  const void* x_prev = hidden;  // residual stream entering the previous block
+  for (int li = 0; li < nlayers; ++li) {
+    const int l = layer0 + li;
+    int* idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
+    float* wg = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
+    moe::NormRouterParams nr{};
+    if (li == 0) {
+      nr.x_in = hidden;
+    } else {
+      nr.x_in = x_prev;
+      nr.x_out = c->xres;
+      nr.y = c->y;
+      nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx + (li - 1) * T * k : c->idx[(li - 1) & 1];
+      nr.prev_w = aux && aux->topk_w ? aux->topk_w + (li - 1) * T * k : c->w[(li - 1) & 1];
+      nr.m_out = aux && aux->moe_out ? aux->moe_out + (li - 1) * T * H : nullptr;
+      nr.combine = 1;
+      x_prev = c->xres;
+    }
+    nr.gamma = c->gamma + l * H * c->esize;
+    nr.router = c->router + l * c->router_layer;
+    nr.xhat = c->xhat;
+    nr.idx_out = idx;
+    nr.w_out = wg;
+    nr.T = T;
+    nr.norm = 1;
+    nr.route = 1;
+    MOE_HIP(moe::launch_norm_router(d, nr, s));
+
+    moe::PermuteParams pp{};
+    pp.idx = idx;
+    pp.P = T * static_cast<int>(k);
+    pp.cnt = aux && aux->expert_count ? aux->expert_count + li * E : c->cnt;
+    pp.off = aux && aux->expert_offset ? aux->expert_offset + li * (E + 1) : c->off;
+    pp.perm = aux && aux->perm ? aux->perm + li * T * k : c->perm;
+    pp.active = c->active;
+    pp.n_active = c->n_active;
+    MOE_HIP(moe::launch_permute(d, pp, s));
+
+    moe::ExpertParams ep{};
+    ep.xhat = c->xhat;
+    ep.cnt = pp.cnt;
+    ep.off = pp.off;
+    ep.perm = pp.perm;
+    ep.active = c->active;
+    ep.n_active = c->n_active;
+    ep.w_gate = c->gate + l * c->gate_layer;
+    ep.w_up = c->up + l * c->gate_layer;
+    ep.w_down = c->down + l * c->down_layer;
+    ep.act = c->act;
+    ep.y = c->y;
+    ep.T = T;
+    MOE_HIP(moe::launch_expert_up(d, ep, s));
+    MOE_HIP(moe::launch_expert_down(d, ep, s));
+  }
+  *x_last = x_prev;
+  return MOE_OK;
+}
+
+int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
+              int32_t* committed, int32_t* counts, const moe_verify_aux* aux, void* stream) {
+  if (!c) return fail(MOE_EINVAL, "ctx is NULL");
+  const moe_verify_config& g = c->cfg;
+  if (!g.has_lm_head) return fail(MOE_EINVAL, "context was created without an LM head");
+  if (B < 1) return fail(MOE_EINVAL, "B must be >= 1");
+  if (K < 0 || K > g.k_max) return fail(MOE_EINVAL, "K must be in [0, k_max]");
+  const int64_t T64 = static_cast<int64_t>(B) * (K + 1);
+  if (T64 > g.max_tokens) return fail(MOE_EINVAL, "B*(K+1) exceeds max_tokens");
+  int r;
+  if ((r = check_ptr(hidden, "hidden", true))) return r;
+  if ((r = check_ptr(drafts, "drafts", K > 0))) return r;
+  if ((r = check_ptr(committed, "committed", true))) return r;
+  if ((r = check_ptr(counts, "counts", true))) return r;
+  if ((r = check_aux(aux))) return r;
+  const int T = static_cast<int>(T64);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const moe::Dims& d = c->d;
+
+  const void* x_last = nullptr;
+  if ((r = run_blocks(c, hidden, T, aux, 0, g.n_layers, s, &x_last))) return r;
+
+  const int64_t H = g.hidden, k = g.top_k;
+  const int li = g.n_layers - 1;
+  moe::NormRouterParams nr{};
+  nr.x_in = x_last;
+  nr.x_out = aux && aux->hidden_out ? aux->hidden_out : c->xres;
+  nr.y = c->y;
+  nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
+  nr.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
+  nr.m_out = aux && aux->moe_out ? aux->moe_out + li * T * H : nullptr;
+  nr.gamma = c->final_gamma;
+  nr.xhat = c->xhat;
+  nr.keys = c->keys;
+  nr.T = T;
+  nr.combine = 1;
+  nr.norm = 1;
+  nr.route = 0;
+  MOE_HIP(moe::launch_norm_router(d, nr, s));
+
+  moe::LmHeadParams lp{};
+  lp.xf = c->xhat;
+  lp.lm = c->lm;
+  lp.T = T;
+  lp.keys = c->keys;
+  lp.done = c->done;
+  lp.drafts = drafts;
+  lp.B = B;
+  lp.K = K;
+  lp.committed = committed;
+  lp.counts = counts;
+  lp.tstar = aux ? aux->tstar : nullptr;
+  MOE_HIP(moe::launch_lmhead(d, lp, s));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* weights, void* hip_stream,
+                    moe_verify_ctx** out) {
+  if (out) *out = nullptr;
+  if (!cfg || !weights || !out) return fail(MOE_EINVAL, "cfg, weights and out must be non-NULL");
+  int r;
+  if ((r = validate_config(*cfg))) return r;
+  if ((r = validate_weights(*cfg, *weights))) return r;
+  moe_verify_ctx* c = new (std::nothrow) moe_verify_ctx();
+  if (!c) return fail(MOE_ENOMEM, "host allocation failed");
+  try {
+    r = create(*cfg, *weights, static_cast<hipStream_t>(hip_stream), c);
+  } catch (...) {
+    r = fail(MOE_ENOMEM, "host exception during init");
+  }
+  if (r != MOE_OK) {
+    const std::string keep = g_last_error;
+    ctx_free(c);
+    g_last_error = keep;
+    return r;
+  }
+  *out = c;
+  g_last_error.clear();
+  return MOE_OK;
+}
+
+int moe_verify_step(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
+                    int32_t* committed, int32_t* counts, void* hip_stream) {
+  return step_impl(ctx, hidden, drafts, B, K, committed, counts, nullptr, hip_stream);
+}
+
+int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
+                       int32_t* committed, int32_t* counts, const moe_verify_aux* aux, void* hip_stream) {
+  return step_impl(ctx, hidden, drafts, B, K, committed, counts, aux, hip_stream);
+}
+
+int moe_block_forward(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, void* y,
+                      const moe_verify_aux* aux, void* hip_stream) {
+  if (!ctx) return fail(MOE_EINVAL, "ctx is NULL");
+  const moe_verify_config& g = ctx->cfg;
+  if (layer < 0 || layer >= g.n_layers) return fail(MOE_EINVAL, "layer out of range");
+  const int cap = g.max_prefill_tokens > 0 ? g.max_prefill_tokens : g.max_tokens;
+  if (T < 1 || T > cap) return fail(MOE_EINVAL, "T must be in [1, max_prefill_tokens]");
+  int r;
+  if ((r = check_ptr(x, "x", true))) return r;
+  if ((r = check_ptr(y, "y", true))) return r;
+  if ((r = check_aux(aux))) return r;
+  const size_t bytes = static_cast<size_t>(T) * g.hidden * ctx->esize;
+  const char* xb = static_cast<const char*>(x);
+  const char* yb = static_cast<const char*>(y);
+  if (xb < yb + bytes && yb < xb + bytes) return fail(MOE_EINVAL, "x and y overlap");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const void* x_last = nullptr;
+  if ((r = run_blocks(ctx, x, T, aux, layer, 1, s, &x_last))) return r;
+  moe::NormRouterParams nr{};
+  nr.x_in = x;
+  nr.x_out = y;
+  nr.y = ctx->y;
+  nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx : ctx->idx[0];
+  nr.prev_w = aux && aux->topk_w ? aux->topk_w : ctx->w[0];
+  nr.m_out = aux ? aux->moe_out : nullptr;
+  nr.T = T;
+  nr.combine = 1;
+  MOE_HIP(moe::launch_norm_router(ctx->d, nr, s));
+  return MOE_OK;
+}
+
+void moe_verify_destroy(moe_verify_ctx* ctx) { ctx_free(ctx); }
+
+const char* moe_verify_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

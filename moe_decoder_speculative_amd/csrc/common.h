@@ -1,0 +1,90 @@
+// Device helpers shared by the gfx950 kernels of the MoE verification step.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+typedef uint16_t bf16_t;                                           // bfloat16 bits
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));       // MFMA operand
+typedef float f32x4_t __attribute__((ext_vector_type(4)));         // 16x16 MFMA acc
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;       // 4 wavefronts
+constexpr int kMaxExperts = 64;   // one router lane per routed expert
+constexpr int kMaxTopK = 8;
+constexpr int kTile = 16;         // MFMA 16x16x32: rows / tokens per tile
+constexpr int kKStep = 32;        // MFMA 16x16x32: reduction per instruction
+constexpr int kFragElems = 512;   // bf16 elements of one 16x32 operand tile
+
+__device__ __forceinline__ float bf16_to_f32(bf16_t v) {
+  return __uint_as_float(static_cast<uint32_t>(v) << 16);
+}
+
+// float32 -> bfloat16, round to nearest, ties to even; NaN -> quiet NaN.
+__device__ __forceinline__ bf16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<bf16_t>(u >> 16);
+}
+
+// Storage-type traits: load one element as float, round a float to storage.
+template <typename ST> struct Storage;
+template <> struct Storage<float> {
+  static __device__ __forceinline__ float load(const float* p, int64_t i) { return p[i]; }
+  static __device__ __forceinline__ float round(float v) { return v; }
+  static __device__ __forceinline__ void store(float* p, int64_t i, float v) { p[i] = v; }
+};
+template <> struct Storage<bf16_t> {
+  static __device__ __forceinline__ float load(const bf16_t* p, int64_t i) { return bf16_to_f32(p[i]); }
+  static __device__ __forceinline__ float round(float v) { return bf16_to_f32(f32_to_bf16(v)); }
+  static __device__ __forceinline__ void store(bf16_t* p, int64_t i, float v) { p[i] = f32_to_bf16(v); }
+};
+
+// 16-byte operand fragment loads (8 bf16).
+__device__ __forceinline__ bf16x8_t load_frag(const bf16_t* p) {
+  uint4 v = *reinterpret_cast<const uint4*>(p);
+  return __builtin_bit_cast(bf16x8_t, v);
+}
+__device__ __forceinline__ bf16x8_t zero_frag() {
+  return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
+}
+
+__device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
+  return v;
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    uint64_t w = __shfl_xor(v, o, kWave);
+    v = w > v ? w : v;
+  }
+  return v;
+}
+
+// Order-preserving map of float32 to uint32 (larger float -> larger key).
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Arg-max key: the larger value wins; on equal values the lower index wins.
+__device__ __forceinline__ uint64_t argmax_key(float v, uint32_t index) {
+  return (static_cast<uint64_t>(orderable(v)) << 32) | static_cast<uint64_t>(0xffffffffu - index);
+}
+__device__ __forceinline__ uint32_t argmax_key_index(uint64_t key) {
+  return 0xffffffffu - static_cast<uint32_t>(key & 0xffffffffu);
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+}  // namespace moe

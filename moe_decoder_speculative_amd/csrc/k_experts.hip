@@ -1,0 +1,265 @@
+// Expert SwiGLU on the decode path (a few to a few hundred token rows).
+//
+// At decode sizes the experts are bound by streaming their weights from HBM:
+// each selected expert's 3 x I x H weights are read once per step, whatever
+// the number of its tokens.  One workgroup owns (expert slot, tile of 16
+// output rows).  Its four wavefronts split the reduction dimension in four and
+// each loads its quarter of the weight tile straight into registers with
+// coalesced 1 KiB reads (weights are pre-tiled in MFMA operand order), keeps it
+// there, and loops over the expert's tokens 16 at a time (tokens gathered from
+// the permutation, padded with zeros), issuing 16x16x32 bf16 MFMAs.  The four
+// partial sums are added through LDS.
+//   up:   a[pair][i] = round(silu(Wg x)[i] * (Wu x)[i])        (pairs of the slot)
+//   down: y[pair][h] = (Wd a)[h]                                 (float32)
+// Shared experts occupy slots 0..S-1 and see every token.  The page "Jina AI
+// releases lightweight OCR model with built-in speculative decoding", section
+// "Lean architecture with a compressed encoder", fixes 64 routed and 2 shared
+// experts with top-6 routing; SwiGLU is this library's reading of the expert.
+#include "kernels.h"
+
+namespace moe {
+
+namespace {
+
+struct SlotInfo {
+  int expert;    // weight index 0..E+S-1 (shared experts after the routed ones)
+  int ntok;
+  int base;      // offset into perm (routed)
+  int shared;    // shared slot index or -1
+};
+
+__device__ __forceinline__ bool slot_info(const Dims& d, const ExpertParams& p, int slot, SlotInfo& si) {
+  const int nact = *p.n_active;
+  if (slot >= d.S + nact) return false;
+  if (slot < d.S) {
+    si.expert = d.E + slot;
+    si.ntok = p.T;
+    si.base = 0;
+    si.shared = slot;
+  } else {
+    const int e = p.active[slot - d.S];
+    si.expert = e;
+    si.ntok = p.cnt[e];
+    si.base = p.off[e];
+    si.shared = -1;
+  }
+  return true;
+}
+
+// pair id of the n-th token of a slot (activation / output row)
+__device__ __forceinline__ int slot_pair(const Dims& d, const ExpertParams& p, const SlotInfo& si, int n) {
+  return si.shared >= 0 ? p.T * d.k + si.shared * p.T + n : p.perm[si.base + n];
+}
+
+// ---------------------------------------------------------------- bf16 ----
+
+template <int KW>  // k-steps per wavefront: H / 32 / 4
+__global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p) {
+  __shared__ float red[4][2][kWave][4];
+  __shared__ int pairs[kTile];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int RT = d.I / kTile, KT = d.H / kKStep;
+  const int slot = blockIdx.x / RT, rt = blockIdx.x % RT;
+  SlotInfo si;
+  if (!slot_info(d, p, slot, si)) return;
+
+  const int kt0 = wave * KW;
+  const int64_t tile = (static_cast<int64_t>(si.expert) * RT + rt) * KT + kt0;
+  const bf16_t* g = reinterpret_cast<const bf16_t*>(p.w_gate) + tile * kFragElems + lane * 8;
+  const bf16_t* u = reinterpret_cast<const bf16_t*>(p.w_up) + tile * kFragElems + lane * 8;
+  bf16x8_t ag[KW], au[KW];
+#pragma unroll
+  for (int i = 0; i < KW; ++i) {
+    ag[i] = load_frag(g + i * kFragElems);
+    au[i] = load_frag(u + i * kFragElems);
+  }
+  const bf16_t* xh = reinterpret_cast<const bf16_t*>(p.xhat);
+  bf16_t* act = reinterpret_cast<bf16_t*>(p.act);
+
+  for (int tile0 = 0; tile0 < si.ntok; tile0 += kTile) {
+    const int n = tile0 + lane % kTile;
+    int pair = -1, tok = 0;
+    if (n < si.ntok) {
+      pair = slot_pair(d, p, si, n);
+      tok = si.shared >= 0 ? n : pair / d.k;
+    }
+    const bf16_t* xr = xh + static_cast<int64_t>(tok) * d.H + kt0 * kKStep + (lane / kTile) * 8;
+    bf16x8_t b[KW];
+#pragma unroll
+    for (int i = 0; i < KW; ++i) b[i] = pair >= 0 ? load_frag(xr + i * kKStep) : zero_frag();
+    f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+      cg = mfma16(ag[i], b[i], cg);
+      cu = mfma16(au[i], b[i], cu);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      red[wave][0][lane][i] = cg[i];
+      red[wave][1][lane][i] = cu[i];
+    }
+    if (wave == 0 && lane < kTile) pairs[lane] = pair;
+    __syncthreads();
+    {
+      const int L = threadIdx.x % kWave, i = threadIdx.x / kWave;
+      const int col = L % kTile, row = 4 * (L / kTile) + i;
+      const int pr = pairs[col];
+      if (pr >= 0) {
+        const float gs = ((red[0][0][L][i] + red[1][0][L][i]) + red[2][0][L][i]) + red[3][0][L][i];
+        const float us = ((red[0][1][L][i] + red[1][1][L][i]) + red[2][1][L][i]) + red[3][1][L][i];
+        act[static_cast<int64_t>(pr) * d.I + rt * kTile + row] = f32_to_bf16(silu_mul(gs, us));
+      }
+    }
+    __syncthreads();
+  }
+}
+
+template <int KW, int RPW>  // KW: k-steps per wavefront (I/32/4); RPW: row tiles per workgroup
+__global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p) {
+  __shared__ float red[4][RPW][kWave][4];
+  __shared__ int pairs[kTile];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int RB = d.H / (kTile * RPW), KT = d.I / kKStep;
+  const int slot = blockIdx.x / RB, rb = blockIdx.x % RB;
+  SlotInfo si;
+  if (!slot_info(d, p, slot, si)) return;
+
+  const int kt0 = wave * KW;
+  bf16x8_t a[RPW][KW];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const int64_t tile = (static_cast<int64_t>(si.expert) * (d.H / kTile) + rb * RPW + r) * KT + kt0;
+    const bf16_t* w = reinterpret_cast<const bf16_t*>(p.w_down) + tile * kFragElems + lane * 8;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) a[r][i] = load_frag(w + i * kFragElems);
+  }
+  const bf16_t* act = reinterpret_cast<const bf16_t*>(p.act);
+
+  for (int tile0 = 0; tile0 < si.ntok; tile0 += kTile) {
+    const int n = tile0 + lane % kTile;
+    const int pair = n < si.ntok ? slot_pair(d, p, si, n) : -1;
+    const bf16_t* ar = act + static_cast<int64_t>(pair < 0 ? 0 : pair) * d.I + kt0 * kKStep + (lane / kTile) * 8;
+    bf16x8_t b[KW];
+#pragma unroll
+    for (int i = 0; i < KW; ++i) b[i] = pair >= 0 ? load_frag(ar + i * kKStep) : zero_frag();
+    f32x4_t c[RPW];
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
+      c[r] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int i = 0; i < KW; ++i) c[r] = mfma16(a[r][i], b[i], c[r]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) red[wave][r][lane][i] = c[r][i];
+    }
+    if (wave == 0 && lane < kTile) pairs[lane] = pair;
+    __syncthreads();
+    for (int q = threadIdx.x; q < RPW * kWave * 4; q += kBlock) {
+      const int r = q / (kWave * 4), L = (q / 4) % kWave, i = q % 4;
+      const int col = L % kTile, row = 4 * (L / kTile) + i;
+      const int pr = pairs[col];
+      if (pr >= 0) {
+        const float v = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
+        p.y[static_cast<int64_t>(pr) * d.H + (rb * RPW + r) * kTile + row] = v;
+      }
+    }
+    __syncthreads();
+  }
+}
+
+// ------------------------------------------------------------- float32 ----
+// Plain FMAs, one thread per output row; used for float32 storage.
+
+__global__ __launch_bounds__(kBlock) void k_up_f32(Dims d, ExpertParams p) {
+  const int RB = (d.I + kBlock - 1) / kBlock;
+  const int slot = blockIdx.x / RB, row = (blockIdx.x % RB) * kBlock + threadIdx.x;
+  SlotInfo si;
+  if (!slot_info(d, p, slot, si) || row >= d.I) return;
+  const float* wg = reinterpret_cast<const float*>(p.w_gate) + (static_cast<int64_t>(si.expert) * d.I + row) * d.H;
+  const float* wu = reinterpret_cast<const float*>(p.w_up) + (static_cast<int64_t>(si.expert) * d.I + row) * d.H;
+  const float* xh = reinterpret_cast<const float*>(p.xhat);
+  float* act = reinterpret_cast<float*>(p.act);
+  for (int n = 0; n < si.ntok; ++n) {
+    const int pair = slot_pair(d, p, si, n);
+    const int tok = si.shared >= 0 ? n : pair / d.k;
+    const float* x = xh + static_cast<int64_t>(tok) * d.H;
+    float g = 0.f, u = 0.f;
+    for (int h = 0; h < d.H; ++h) {
+      g = __fadd_rn(g, __fmul_rn(wg[h], x[h]));
+      u = __fadd_rn(u, __fmul_rn(wu[h], x[h]));
+    }
+    act[static_cast<int64_t>(pair) * d.I + row] = silu_mul(g, u);
+  }
+}
+
+__global__ __launch_bounds__(kBlock) void k_down_f32(Dims d, ExpertParams p) {
+  const int RB = (d.H + kBlock - 1) / kBlock;
+  const int slot = blockIdx.x / RB, row = (blockIdx.x % RB) * kBlock + threadIdx.x;
+  SlotInfo si;
+  if (!slot_info(d, p, slot, si) || row >= d.H) return;
+  const float* wd = reinterpret_cast<const float*>(p.w_down) + (static_cast<int64_t>(si.expert) * d.H + row) * d.I;
+  const float* act = reinterpret_cast<const float*>(p.act);
+  for (int n = 0; n < si.ntok; ++n) {
+    const int pair = slot_pair(d, p, si, n);
+    const float* a = act + static_cast<int64_t>(pair) * d.I;
+    float acc = 0.f;
+    for (int i = 0; i < d.I; ++i) acc = __fadd_rn(acc, __fmul_rn(wd[i], a[i]));
+    p.y[static_cast<int64_t>(pair) * d.H + row] = acc;
+  }
+}
+
+template <int KW>
+hipError_t up_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
+  const int grid = (d.S + d.E) * (d.I / kTile);
+  hipLaunchKernelGGL(k_up_mfma<KW>, dim3(grid), dim3(kBlock), 0, s, d, p);
+  return hipGetLastError();
+}
+
+template <int KW>
+hipError_t down_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
+  constexpr int RPW = 2;
+  if ((d.H / kTile) % RPW == 0) {
+    const int grid = (d.S + d.E) * (d.H / (kTile * RPW));
+    hipLaunchKernelGGL((k_down_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p);
+  } else {
+    const int grid = (d.S + d.E) * (d.H / kTile);
+    hipLaunchKernelGGL((k_down_mfma<KW, 1>), dim3(grid), dim3(kBlock), 0, s, d, p);
+  }
+  return hipGetLastError();
+}
+
+#define MOE_KW_CASES(F)                                                                  \
+  switch (kw) {                                                                         \
+    case 1: return F<1>(d, p, s);   case 2: return F<2>(d, p, s);                       \
+    case 3: return F<3>(d, p, s);   case 4: return F<4>(d, p, s);                       \
+    case 5: return F<5>(d, p, s);   case 6: return F<6>(d, p, s);                       \
+    case 7: return F<7>(d, p, s);   case 8: return F<8>(d, p, s);                       \
+    case 9: return F<9>(d, p, s);   case 10: return F<10>(d, p, s);                     \
+    case 11: return F<11>(d, p, s); case 12: return F<12>(d, p, s);                     \
+    case 13: return F<13>(d, p, s); case 14: return F<14>(d, p, s);                     \
+    case 15: return F<15>(d, p, s); case 16: return F<16>(d, p, s);                     \
+    default: return hipErrorInvalidValue;                                               \
+  }
+
+}  // namespace
+
+hipError_t launch_expert_up(const Dims& d, const ExpertParams& p, hipStream_t s) {
+  if (!d.bf16) {
+    const int grid = (d.S + d.E) * ((d.I + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(k_up_f32, dim3(grid), dim3(kBlock), 0, s, d, p);
+    return hipGetLastError();
+  }
+  const int kw = d.H / (kKStep * 4);
+  MOE_KW_CASES(up_kw)
+}
+
+hipError_t launch_expert_down(const Dims& d, const ExpertParams& p, hipStream_t s) {
+  if (!d.bf16) {
+    const int grid = (d.S + d.E) * ((d.H + kBlock - 1) / kBlock);
+    hipLaunchKernelGGL(k_down_f32, dim3(grid), dim3(kBlock), 0, s, d, p);
+    return hipGetLastError();
+  }
+  const int kw = d.I / (kKStep * 4);
+  MOE_KW_CASES(down_kw)
+}
+
+}  // namespace moe

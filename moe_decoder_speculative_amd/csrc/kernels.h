@@ -1,0 +1,93 @@
+// Launch interface between the C ABI (api.cpp) and the gfx950 kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "common.h"
+
+namespace moe {
+
+// Model dimensions (H hidden, E routed, k top-k, S shared, I SwiGLU width,
+// V vocabulary, Vpad padded vocabulary rows of the tiled LM head).
+struct Dims {
+  int H, E, k, S, I, V, Vpad, L;
+  float eps;
+  int bf16;  // 1: bfloat16 storage and MFMA kernels; 0: float32 storage
+};
+
+// Combine (previous block) + RMSNorm + router/top-k over T token rows.
+struct NormRouterParams {
+  const void* x_in;        // [T][H] storage: residual stream entering the kernel
+  void* x_out;             // [T][H] storage: x_in + m (combine only; may equal x_in)
+  const float* y;          // [T*k + S*T][H] previous block's expert outputs (combine)
+  const int* prev_idx;     // [T][k] previous block's selection (combine)
+  const float* prev_w;     // [T][k] previous block's gate weights (combine)
+  float* m_out;            // [T][H] previous block's MoE output, optional (combine)
+  const void* gamma;       // [H] storage, RMSNorm gain (norm)
+  const void* router;      // bf16: tiled [64/16][H/32][512]; f32: [E][H] (route)
+  void* xhat;              // [T][H] storage out (norm)
+  int* idx_out;            // [T][k] (route)
+  float* w_out;            // [T][k] (route)
+  unsigned long long* keys;  // [T] arg-max keys to clear, optional
+  int T;
+  int combine, norm, route;
+};
+hipError_t launch_norm_router(const Dims& d, const NormRouterParams& p, hipStream_t s);
+
+// Stable counting sort of the T*k (token, slot) pairs by expert.
+struct PermuteParams {
+  const int* idx;  // [P] expert of pair p = t*k + j
+  int P;
+  int* cnt;        // [E]
+  int* off;        // [E+1]
+  int* perm;       // [P]
+  int* active;     // [E] experts with cnt > 0, ascending; entries past n_active unused
+  int* n_active;   // [1]
+};
+hipError_t launch_permute(const Dims& d, const PermuteParams& p, hipStream_t s);
+
+// Expert SwiGLU on the decode path.  Expert slots: 0..S-1 are the shared
+// experts (every token), then the active routed experts in ascending order.
+// Activation / output rows: pair p = t*k + j for routed, T*k + s*T + t for shared.
+struct ExpertParams {
+  const void* xhat;      // [T][H] storage
+  const int* cnt;        // [E]
+  const int* off;        // [E+1]
+  const int* perm;       // [T*k]
+  const int* active;     // [E]
+  const int* n_active;   // [1]
+  const void* w_gate;    // this layer: bf16 tiled [E+S][I/16][H/32][512]; f32 [E+S][I][H]
+  const void* w_up;      // same layout as w_gate
+  const void* w_down;    // bf16 tiled [E+S][H/16][I/32][512]; f32 [E+S][H][I]
+  void* act;             // [T*k + S*T][I] storage
+  float* y;              // [T*k + S*T][H] float32
+  int T;
+};
+hipError_t launch_expert_up(const Dims& d, const ExpertParams& p, hipStream_t s);
+hipError_t launch_expert_down(const Dims& d, const ExpertParams& p, hipStream_t s);
+
+// LM head + greedy arg-max + prefix acceptance.
+struct LmHeadParams {
+  const void* xf;            // [T][H] storage (final-norm activations)
+  const void* lm;            // bf16 tiled [Vpad/16][H/32][512]; f32 [V][H]
+  int T;
+  unsigned long long* keys;  // [T], cleared beforehand
+  unsigned int* done;        // completion counter, 0 on entry, left 0 on exit
+  const int* drafts;         // [B][K]
+  int B, K;
+  int* committed;            // [B][K+1]
+  int* counts;               // [B]
+  int* tstar;                // [T], optional
+};
+hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s);
+
+// Weight repacking.  Tiled layout of an [R][C] bf16 matrix (R padded to Rpad
+// with zero rows): tile (rt, kt) of 16 rows x 32 columns is 512 contiguous
+// elements in which lane l of a wavefront owns the 8 elements of row
+// rt*16 + l%16, columns kt*32 + (l/16)*8 .. +8 -- the operand layout of one
+// 16x16x32 MFMA, so a wavefront loads a tile with one coalesced 1 KiB read.
+hipError_t launch_tile_bf16(const bf16_t* src, int64_t src_mat_stride, bf16_t* dst,
+                            int64_t n_mats, int R, int C, int Rpad, hipStream_t s);
+
+}  // namespace moe

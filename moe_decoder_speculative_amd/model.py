@@ -1,0 +1,116 @@
+"""Device-side setup around the C ABI: upload seeded weights, create a
+context, allocate step buffers.  Torch provides device memory and streams only.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+from . import binding as B_
+from .synth import Workload
+
+
+def _torch():
+    import torch
+    return torch
+
+
+def to_device(a: np.ndarray, device="cuda"):
+    """numpy float32 / uint16 (bfloat16 bits) / int32 array -> device tensor."""
+    torch = _torch()
+    a = np.ascontiguousarray(a)
+    if a.dtype == np.uint16:
+        return torch.from_numpy(a.view(np.int16)).view(torch.bfloat16).to(device)
+    return torch.from_numpy(a).to(device)
+
+
+def _stacked(weights: dict, key: str, device):
+    """Per-layer arrays stacked into one [L, ...] device tensor, one layer at a time."""
+    torch = _torch()
+    layers = weights["layers"]
+    first = layers[0][key]
+    dtype = torch.bfloat16 if first.dtype == np.uint16 else torch.float32
+    out = torch.empty((len(layers),) + first.shape, dtype=dtype, device=device)
+    for l, lw in enumerate(layers):
+        out[l].copy_(to_device(lw[key], device))
+    return out
+
+
+class VerifyModel:
+    """A library context for a workload's shapes and weights.
+
+    Weights are uploaded, handed to moe_verify_init (which repacks them into
+    the context) and released again.
+    """
+
+    def __init__(self, w: Workload, weights: dict, max_tokens: int | None = None,
+                 max_prefill_tokens: int = 0, k_max: int = 7, device="cuda", stream=None):
+        torch = _torch()
+        self.w = w
+        self.device = device
+        self.max_tokens = max_tokens or max(w.T, 1)
+        cfg = B_.MoeVerifyConfig(
+            hidden=w.H, n_routed=w.E, top_k=w.k, n_shared=w.S, inter=w.I, vocab=w.V if w.has_lm_head else 0,
+            n_layers=len(weights["layers"]), max_tokens=self.max_tokens, max_prefill_tokens=max_prefill_tokens,
+            k_max=k_max, rms_eps=w.eps, dtype=B_.MOE_DTYPE_BF16 if w.dtype == "bf16" else B_.MOE_DTYPE_F32,
+            has_lm_head=1 if w.has_lm_head else 0)
+        self.cfg = cfg
+        t = {k: _stacked(weights, k, device) for k in ("router", "gate", "up", "down", "s_gate", "s_up",
+                                                       "s_down", "gamma")}
+        fg = to_device(weights["final_gamma"], device) if w.has_lm_head else None
+        lm = to_device(weights["lm_head"], device) if w.has_lm_head else None
+        wts = B_.MoeVerifyWeights(
+            router=t["router"].data_ptr(), w_gate=t["gate"].data_ptr(), w_up=t["up"].data_ptr(),
+            w_down=t["down"].data_ptr(),
+            s_gate=t["s_gate"].data_ptr() if w.S else None, s_up=t["s_up"].data_ptr() if w.S else None,
+            s_down=t["s_down"].data_ptr() if w.S else None, norm_gamma=t["gamma"].data_ptr(),
+            final_gamma=fg.data_ptr() if fg is not None else None, lm_head=lm.data_ptr() if lm is not None else None)
+        torch.cuda.synchronize()
+        self.ctx = B_.moe_verify_init(cfg, wts, stream)
+        del t, fg, lm
+        torch.cuda.synchronize()
+        self.store_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
+
+    # ------------------------------------------------------------------
+    def alloc_outputs(self, B: int, K: int):
+        torch = _torch()
+        committed = torch.empty((B, K + 1), dtype=torch.int32, device=self.device)
+        counts = torch.empty((B,), dtype=torch.int32, device=self.device)
+        return committed, counts
+
+    def alloc_aux(self, T: int, layers: int | None = None, with_hidden=True):
+        torch = _torch()
+        L = layers or self.cfg.n_layers
+        w = self.w
+        aux = dict(
+            topk_idx=torch.empty((L, T, w.k), dtype=torch.int32, device=self.device),
+            topk_w=torch.empty((L, T, w.k), dtype=torch.float32, device=self.device),
+            expert_count=torch.empty((L, w.E), dtype=torch.int32, device=self.device),
+            expert_offset=torch.empty((L, w.E + 1), dtype=torch.int32, device=self.device),
+            perm=torch.empty((L, T * w.k), dtype=torch.int32, device=self.device),
+            moe_out=torch.empty((L, T, w.H), dtype=torch.float32, device=self.device),
+            tstar=torch.empty((T,), dtype=torch.int32, device=self.device),
+        )
+        if with_hidden:
+            aux["hidden_out"] = torch.empty((T, w.H), dtype=self.store_dtype, device=self.device)
+        return aux
+
+    def step(self, hidden, drafts, B: int, K: int, committed, counts, aux: dict | None = None, stream=None):
+        if aux is None:
+            B_.moe_verify_step(self.ctx, hidden, drafts if K > 0 else None, B, K, committed, counts, stream)
+        else:
+            B_.moe_verify_step_ex(self.ctx, hidden, drafts if K > 0 else None, B, K, committed, counts,
+                                  B_.make_aux(**aux), stream)
+
+    def block_forward(self, layer: int, x, T: int, y, aux: dict | None = None, stream=None):
+        B_.moe_block_forward(self.ctx, layer, x, T, y, B_.make_aux(**aux) if aux else None, stream)
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            B_.moe_verify_destroy(self.ctx)
+            self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

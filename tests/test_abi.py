@@ -1,0 +1,114 @@
+"""The C ABI library loads, exports every function include/moe_verify.h declares,
+and rejects bad arguments before any HIP runtime call (so these run without a
+GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from moe_decoder_speculative_amd import binding as B
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_verify.h")
+
+
+def _declared():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_binding_names():
+    assert _declared() == sorted(B.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol():
+    lib = ctypes.CDLL(B.LIB_PATH)
+    for name in _declared():
+        assert hasattr(lib, name), name
+
+
+def _cfg(**kw):
+    base = dict(hidden=256, n_routed=8, top_k=2, n_shared=1, inter=128, vocab=1024, n_layers=1,
+                max_tokens=64, max_prefill_tokens=0, k_max=3, rms_eps=1e-6, dtype=B.MOE_DTYPE_BF16,
+                has_lm_head=1)
+    base.update(kw)
+    return B.MoeVerifyConfig(**base)
+
+
+FAKE = 0x10000  # aligned, never dereferenced: validation fails first
+
+
+def _weights(**kw):
+    base = {n: FAKE for n, _ in B.MoeVerifyWeights._fields_}
+    base.update(kw)
+    return B.MoeVerifyWeights(**base)
+
+
+def _init_rc(cfg, w):
+    lib = B.load_library()
+    out = ctypes.c_void_p(1234)
+    rc = lib.moe_verify_init(ctypes.byref(cfg) if cfg is not None else None,
+                             ctypes.byref(w) if w is not None else None, None, ctypes.byref(out))
+    return rc, out.value
+
+
+@pytest.mark.parametrize("bad", [
+    dict(hidden=100), dict(hidden=0), dict(hidden=1664), dict(hidden=896, dtype=0), dict(inter=96), dict(n_routed=0),
+    dict(n_routed=65), dict(top_k=0), dict(top_k=9), dict(n_routed=4, top_k=5), dict(n_shared=-1),
+    dict(n_shared=5), dict(n_layers=0), dict(max_tokens=0), dict(max_tokens=70000),
+    dict(max_prefill_tokens=-1), dict(k_max=-1), dict(k_max=8), dict(rms_eps=0.0),
+    dict(rms_eps=float("nan")), dict(dtype=2), dict(has_lm_head=2), dict(vocab=0),
+])
+def test_init_rejects_bad_config(bad):
+    rc, out = _init_rc(_cfg(**bad), _weights())
+    assert rc == B.MOE_EINVAL
+    assert out is None
+    assert B.moe_verify_last_error().startswith("config:")
+
+
+@pytest.mark.parametrize("field", ["router", "w_gate", "w_up", "w_down", "s_gate", "s_up", "s_down",
+                                   "norm_gamma", "final_gamma", "lm_head"])
+def test_init_rejects_null_or_misaligned_weight(field):
+    rc, _ = _init_rc(_cfg(), _weights(**{field: None}))
+    assert rc == B.MOE_EINVAL and field in B.moe_verify_last_error()
+    rc, _ = _init_rc(_cfg(), _weights(**{field: FAKE + 8}))
+    assert rc == B.MOE_EINVAL and "aligned" in B.moe_verify_last_error()
+
+
+def test_optional_weights_may_be_null():
+    # S = 0 and no LM head: shared and head pointers are not required.  The
+    # injected allocation failure stops init right after validation.
+    os.environ["MOE_VERIFY_FAULT"] = "alloc"
+    try:
+        rc, out = _init_rc(_cfg(n_shared=0, has_lm_head=0),
+                           _weights(s_gate=None, s_up=None, s_down=None, final_gamma=None, lm_head=None))
+    finally:
+        del os.environ["MOE_VERIFY_FAULT"]
+    assert rc in (B.MOE_ENOMEM, B.MOE_EHIP) and out is None
+
+
+def test_init_null_arguments():
+    assert _init_rc(None, _weights())[0] == B.MOE_EINVAL
+    assert _init_rc(_cfg(), None)[0] == B.MOE_EINVAL
+
+
+def test_step_and_block_reject_null_context():
+    lib = B.load_library()
+    rc = lib.moe_verify_step(None, FAKE, FAKE, 1, 3, FAKE, FAKE, None)
+    assert rc == B.MOE_EINVAL and "ctx" in B.moe_verify_last_error()
+    rc = lib.moe_verify_step_ex(None, FAKE, FAKE, 1, 3, FAKE, FAKE, None, None)
+    assert rc == B.MOE_EINVAL
+    rc = lib.moe_block_forward(None, 0, FAKE, 4, FAKE, None, None)
+    assert rc == B.MOE_EINVAL
+
+
+def test_destroy_null_is_a_no_op():
+    B.moe_verify_destroy(None)
+
+
+def test_binding_raises_with_message():
+    with pytest.raises(B.MoeVerifyError) as ei:
+        B.moe_verify_init(_cfg(hidden=3), _weights())
+    assert ei.value.code == B.MOE_EINVAL and "hidden" in ei.value.message
