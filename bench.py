@@ -1,0 +1,307 @@
+#!/usr/bin/env python3
+"""Throughput of one MoE speculative verification step on one MI355X.
+
+A step is one call of moe_verify_step: B sequences x (K+1) positions through
+L MoE blocks (RMSNorm, top-6-of-64 router, 6 routed + 2 shared SwiGLU
+experts, combine, residual), the final norm, the LM head with greedy arg-max
+and the longest-prefix acceptance.  The headline is verified tokens per
+second (B*(K+1) tokens per step); the dominant kernel is reported against the
+HBM roofline, and the CPU oracle is timed on a bounded sample beside it.
+
+Inputs are seeded synthetic data shaped like the pages' workloads (random
+N(0, 0.02^2) weights, N(0,1) hidden states); they are resident in HBM before
+the timed region.  Several independent weight copies are rotated so that no
+weight byte of a step is served by the 256 MB last-level cache from an earlier
+step.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import hashlib
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
+METRIC = "verified tokens/s per MoE verify step (B×4 tokens); % HBM or MFMA peak"
+EXPERT_BYTES = None  # filled per workload
+
+
+def log(msg: str):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+# ---------------------------------------------------------------- HIP events
+
+class HipEvents:
+    """hipEvent_t handles through the HIP runtime torch has already loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+
+    def create(self) -> int:
+        e = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return e.value
+
+    def record(self, ev: int, stream: int):
+        rc = self.hip.hipEventRecord(ev, stream)
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+    def elapsed_ms(self, a: int, b: int) -> float:
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b)
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return float(ms.value)
+
+    def destroy(self, ev: int):
+        self.hip.hipEventDestroy(ev)
+
+
+# ---------------------------------------------------------- algorithmic work
+
+def expert_bytes(w) -> int:
+    return 3 * w.I * w.H * 2
+
+
+def step_bytes(w, touched_per_layer) -> int:
+    """Bytes the step must move: touched experts' weights, shared experts,
+    router, activations in/out per block, LM head."""
+    per = []
+    for n in touched_per_layer:
+        per.append(n * expert_bytes(w) + w.S * expert_bytes(w) + w.E * w.H * 2 + 2 * w.T * w.H * 2)
+    lm = w.V * w.H * 2 if w.has_lm_head else 0
+    return int(sum(per) + lm)
+
+
+def step_flops(w) -> int:
+    f = w.L * (w.T * (w.k + w.S) * 6 * w.H * w.I + 2 * w.T * w.E * w.H)
+    if w.has_lm_head:
+        f += 2 * w.T * w.H * w.V
+    return int(f)
+
+
+def lmhead_bytes(w) -> int:
+    # weights once + final-norm activations in + one 8-byte key per token
+    return w.V * w.H * 2 + w.T * w.H * 2 + w.T * 8
+
+
+# ------------------------------------------------------------ counter file
+
+def kernel_source_hash(name: str) -> str:
+    p = os.path.join(ROOT, "moe_decoder_speculative_amd", "csrc", name)
+    h = hashlib.sha256()
+    for f in (p, os.path.join(ROOT, "moe_decoder_speculative_amd", "csrc", "common.h")):
+        with open(f, "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profiles(kernel_file: str, workload: str):
+    """HBM bytes per launch from committed counter summaries, or None when
+    absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    ent = data.get(workload)
+    if not ent or ent.get("source_hash") != kernel_source_hash(kernel_file):
+        return None
+    return ent.get("bytes_per_launch")
+
+
+# ---------------------------------------------------------------- CPU leg
+
+def cpu_baseline(w, weights, hidden_np, drafts_np, seconds: float):
+    """The oracle, as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    import oracle
+    shp = oracle.Shape(H=w.H, E=w.E, k=w.k, S=w.S, I=w.I, V=w.V, L=w.L, eps=w.eps, dtype=w.dtype)
+    # sample: whole steps when small, else one sequence (K+1 tokens) per call
+    if w.has_lm_head:
+        seqs = w.B if w.T <= 8 else 1
+        Bs, K = seqs, w.K
+        h = hidden_np[: Bs * (K + 1)]
+        d = drafts_np[:Bs]
+        what = f"{Bs} sequence(s) x {K + 1} positions per oracle step"
+        tokens_per_call = Bs * (K + 1)
+
+        def call():
+            oracle.verify_step(shp, weights, h, d, Bs, K)
+    else:
+        rows = min(w.T, 256)
+        h = hidden_np[:rows]
+        what = f"{rows} token rows per oracle block call"
+        tokens_per_call = rows
+
+        def call():
+            oracle.moe_block(h, weights["layers"][0], shp)
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        call()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    tok_s = n * tokens_per_call / el
+    return {"value": tok_s, "unit": "verified tokens/s" if w.has_lm_head else "tokens/s",
+            "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} calls of {what} in {el:.1f} s (numpy float32, BLAS threads {threads})"}
+
+
+# ---------------------------------------------------------------- main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="decode_b1",
+                    choices=["decode_b1", "decode_b32_zipf", "stack12_b32_zipf"])
+    ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for 1.5 GB)")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: the verification step runs on a single MI355X "
+              "(data parallelism over sequences needs no exchange; see the design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from moe_decoder_speculative_amd import synth, binding
+    from moe_decoder_speculative_amd.model import VerifyModel, to_device
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    w = synth.WORKLOADS[args.workload]
+    log(f"workload {w.name}: B={w.B} K={w.K} T={w.T} L={w.L} H={w.H} E={w.E} k={w.k} S={w.S} I={w.I} V={w.V}")
+    t = time.time()
+    weights = synth.gen_weights(w)
+    noise = synth.HiddenNoise(w)
+    offset = synth.hidden_offset(w, weights, noise)
+    hidden_np = synth.to_storage(noise.draw(w.T) + offset, w.dtype)
+    log(f"generated weights in {time.time() - t:.1f}s")
+
+    copy_bytes = w.L * (w.E + w.S) * expert_bytes(w) + (w.V * w.H * 2 if w.has_lm_head else 0)
+    copies = args.copies or max(1, math.ceil(1.5e9 / copy_bytes))
+    model = VerifyModel(w, weights, max_tokens=w.T, copies=copies)
+    log(f"{copies} weight copies of {copy_bytes / 1e6:.0f} MB in HBM")
+
+    hidden = to_device(hidden_np)
+    # drafts: each correct with probability p against this step's own greedy picks
+    committed, counts = model.alloc_outputs(w.B, w.K)
+    aux = model.alloc_aux(w.T, with_hidden=False)
+    model.step(hidden, to_device(np.zeros((w.B, w.K), np.int32)), w.B, w.K, committed, counts, aux)
+    torch.cuda.synchronize()
+    tstar = aux["tstar"].cpu().numpy()
+    touched = [len(np.unique(aux["topk_idx"][l].cpu().numpy())) for l in range(w.L)]
+    drafts_np = synth.make_drafts(w, tstar.reshape(w.B, w.K + 1))
+    drafts = to_device(drafts_np)
+    model.step(hidden, drafts, w.B, w.K, committed, counts)
+    torch.cuda.synchronize()
+    committed_per_step = int(counts.sum().item())
+    del aux
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(args.warmup):
+        model.step(hidden, drafts, w.B, w.K, committed, counts, copy=i % copies)
+    torch.cuda.synchronize()
+
+    K = args.steps
+    before = [ev.create() for _ in range(K)]
+    after = [ev.create() for _ in range(K)]
+    g0, g1 = ev.create(), ev.create()
+    stage = binding.MOE_STAGE_LMHEAD if w.L == 1 else binding.MOE_STAGE_EXPERT_UP
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(g0, stream)
+    for i in range(K):
+        c = i % copies
+        binding.moe_verify_set_stage_events(model.ctxs[c], stage, before[i], after[i])
+        model.step(hidden, drafts, w.B, w.K, committed, counts, copy=c)
+    ev.record(g1, stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_step = (t1 - t0) * 1e3 / K
+    gpu_ms_step = ev.elapsed_ms(g0, g1) / K
+    kern_ms = sorted(ev.elapsed_ms(b, a) for b, a in zip(before, after))
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    for e in before + after + [g0, g1]:
+        ev.destroy(e)
+
+    if stage == binding.MOE_STAGE_LMHEAD:
+        kname, kfile, kbytes = "k_lmhead_mfma", "k_lmhead.hip", lmhead_bytes(w)
+    else:
+        kname, kfile = "k_up_mfma", "k_experts.hip"
+        kbytes = (touched[0] + w.S) * 2 * w.I * w.H * 2 + w.T * w.H * 2 + w.T * (w.k + w.S) * w.I * 2
+    achieved = kbytes / (kern_avg_ms * 1e-3) / 1e9
+    traffic = traffic_from_profiles(kfile, w.name)
+    sbytes = step_bytes(w, touched)
+
+    res = {
+        "metric": METRIC,
+        "value": w.T / (ms_step * 1e-3),
+        "unit": "verified tokens/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": ms_step,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": w.name, "B": w.B, "K": w.K, "tokens_per_step": w.T, "layers": w.L,
+                   "hidden": w.H, "routed_experts": w.E, "top_k": w.k, "shared_experts": w.S,
+                   "inter": w.I, "vocab": w.V, "routing": w.routing, "weight_copies": copies},
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": achieved / HBM_PEAK_GBS,
+                     "traffic": traffic, "kernel": kname, "bytes_per_launch": kbytes,
+                     "avg_us": kern_avg_ms * 1e3, "median_us": kern_ms[len(kern_ms) // 2] * 1e3},
+        "step": {"gpu_ms_per_step": gpu_ms_step, "algorithmic_bytes": sbytes,
+                 "hbm_frac": sbytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
+                 "flops": step_flops(w), "experts_touched_per_layer": touched,
+                 "committed_tokens_per_step": committed_per_step,
+                 "committed_tokens_per_s": committed_per_step / (ms_step * 1e-3)},
+    }
+    model.close()
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline(w, weights, hidden_np, drafts_np, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

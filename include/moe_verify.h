@@ -192,6 +192,24 @@ int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* d
 int moe_block_forward(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, void* y,
                       const moe_verify_aux* aux, void* hip_stream);
 
+/* Stages that can be bracketed by timing events. */
+#define MOE_STAGE_LMHEAD 0      /* LM head + arg-max + acceptance kernel of a verify step   */
+#define MOE_STAGE_EXPERT_UP 1   /* expert gate/up kernel of the first block of a call        */
+#define MOE_STAGE_EXPERT_DOWN 2 /* expert down kernel of the first block of a call           */
+#define MOE_STAGE_ALL 3         /* the whole call, first kernel to last                      */
+#define MOE_STAGE_COUNT 4
+
+/*
+ * Timing hook for profiling.  `before` and `after` are hipEvent_t handles
+ * created by the caller (or NULL to clear).  The next moe_verify_step /
+ * moe_verify_step_ex / moe_block_forward call on `ctx` records `before` on
+ * its stream right before it launches stage `stage` and `after` right after,
+ * then forgets the pair (one call only), so a caller times N calls with N
+ * event pairs.  The events add two stream records to that call.
+ * Errors: MOE_EINVAL for a NULL ctx or a stage outside [0, MOE_STAGE_COUNT).
+ */
+int moe_verify_set_stage_events(moe_verify_ctx* ctx, int32_t stage, void* before, void* after);
+
 /* Free everything the context owns.  NULL is accepted.  Synchronises the
  * device work the context may still have in flight. */
 void moe_verify_destroy(moe_verify_ctx* ctx);

@@ -10,5 +10,5 @@ seeded inputs.
 from .binding import (  # noqa: F401
     MOE_DTYPE_BF16, MOE_DTYPE_F32, MoeVerifyAux, MoeVerifyConfig, MoeVerifyError, MoeVerifyWeights,
     load_library, make_aux, moe_block_forward, moe_verify_destroy, moe_verify_init,
-    moe_verify_last_error, moe_verify_step, moe_verify_step_ex,
+    moe_verify_last_error, moe_verify_set_stage_events, moe_verify_step, moe_verify_step_ex,
 )

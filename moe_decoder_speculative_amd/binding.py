@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libmoeverify.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_block_forward",
-            "moe_verify_destroy", "moe_verify_last_error")
+            "moe_verify_set_stage_events", "moe_verify_destroy", "moe_verify_last_error")
+MOE_STAGE_LMHEAD, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_ALL = 0, 1, 2, 3
 
 
 class MoeVerifyError(RuntimeError):
@@ -66,6 +67,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_step_ex.restype = ctypes.c_int
     lib.moe_block_forward.argtypes = [vp, i32, vp, i32, vp, ctypes.POINTER(MoeVerifyAux), vp]
     lib.moe_block_forward.restype = ctypes.c_int
+    lib.moe_verify_set_stage_events.argtypes = [vp, i32, vp, vp]
+    lib.moe_verify_set_stage_events.restype = ctypes.c_int
     lib.moe_verify_destroy.argtypes = [vp]
     lib.moe_verify_destroy.restype = None
     lib.moe_verify_last_error.argtypes = []
@@ -134,6 +137,11 @@ def moe_verify_step_ex(ctx: int, hidden, drafts, B: int, K: int, committed, coun
 def moe_block_forward(ctx: int, layer: int, x, T: int, y, aux: MoeVerifyAux | None = None, stream=None) -> None:
     _check(load_library().moe_block_forward(ctx, layer, _ptr(x), T, _ptr(y),
                                             ctypes.byref(aux) if aux is not None else None, _stream(stream)))
+
+
+def moe_verify_set_stage_events(ctx: int, stage: int, before: int | None, after: int | None) -> None:
+    """Bracket `stage` of the next call on ctx with two hipEvent_t handles."""
+    _check(load_library().moe_verify_set_stage_events(ctx, stage, before, after))
 
 
 def moe_verify_destroy(ctx: int | None) -> None:

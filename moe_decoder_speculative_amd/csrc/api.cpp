@@ -53,6 +53,10 @@ struct moe_verify_ctx {
   float* y = nullptr;       // [tw*(k+S)][H]
   unsigned long long* keys = nullptr;  // [tw]
   unsigned int* done = nullptr;
+
+  // one-call timing hooks (moe_verify_set_stage_events)
+  hipEvent_t ev_before[MOE_STAGE_COUNT] = {};
+  hipEvent_t ev_after[MOE_STAGE_COUNT] = {};
 };
 
 namespace {
@@ -65,6 +69,12 @@ int fail(int code, const std::string& msg) {
 }
 
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
+
+void clear_hooks(moe_verify_ctx* c) {
+  for (int i = 0; i < MOE_STAGE_COUNT; ++i) c->ev_before[i] = c->ev_after[i] = nullptr;
+}
 
 #define MOE_HIP(expr)                                                                        \
   do {                                                                                       \
@@ -321,8 +331,12 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     ep.act = c->act;
     ep.y = c->y;
     ep.T = T;
+    if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_EXPERT_UP], s));
     MOE_HIP(moe::launch_expert_up(d, ep, s));
+    if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_EXPERT_UP], s));
+    if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_EXPERT_DOWN], s));
     MOE_HIP(moe::launch_expert_down(d, ep, s));
+    if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_EXPERT_DOWN], s));
   }
   *x_last = x_prev;
   return MOE_OK;
@@ -348,6 +362,7 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
   const moe::Dims& d = c->d;
 
   const void* x_last = nullptr;
+  MOE_HIP(mark(c->ev_before[MOE_STAGE_ALL], s));
   if ((r = run_blocks(c, hidden, T, aux, 0, g.n_layers, s, &x_last))) return r;
 
   const int64_t H = g.hidden, k = g.top_k;
@@ -380,7 +395,10 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
   lp.committed = committed;
   lp.counts = counts;
   lp.tstar = aux ? aux->tstar : nullptr;
+  MOE_HIP(mark(c->ev_before[MOE_STAGE_LMHEAD], s));
   MOE_HIP(moe::launch_lmhead(d, lp, s));
+  MOE_HIP(mark(c->ev_after[MOE_STAGE_LMHEAD], s));
+  MOE_HIP(mark(c->ev_after[MOE_STAGE_ALL], s));
   return MOE_OK;
 }
 
@@ -415,16 +433,21 @@ int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* weig
 
 int moe_verify_step(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
                     int32_t* committed, int32_t* counts, void* hip_stream) {
-  return step_impl(ctx, hidden, drafts, B, K, committed, counts, nullptr, hip_stream);
+  const int r = step_impl(ctx, hidden, drafts, B, K, committed, counts, nullptr, hip_stream);
+  if (ctx) clear_hooks(ctx);
+  return r;
 }
 
 int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
                        int32_t* committed, int32_t* counts, const moe_verify_aux* aux, void* hip_stream) {
-  return step_impl(ctx, hidden, drafts, B, K, committed, counts, aux, hip_stream);
+  const int r = step_impl(ctx, hidden, drafts, B, K, committed, counts, aux, hip_stream);
+  if (ctx) clear_hooks(ctx);
+  return r;
 }
 
-int moe_block_forward(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, void* y,
-                      const moe_verify_aux* aux, void* hip_stream) {
+namespace {
+int block_impl(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, void* y,
+               const moe_verify_aux* aux, void* hip_stream) {
   if (!ctx) return fail(MOE_EINVAL, "ctx is NULL");
   const moe_verify_config& g = ctx->cfg;
   if (layer < 0 || layer >= g.n_layers) return fail(MOE_EINVAL, "layer out of range");
@@ -440,6 +463,7 @@ int moe_block_forward(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t
   if (xb < yb + bytes && yb < xb + bytes) return fail(MOE_EINVAL, "x and y overlap");
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const void* x_last = nullptr;
+  MOE_HIP(mark(ctx->ev_before[MOE_STAGE_ALL], s));
   if ((r = run_blocks(ctx, x, T, aux, layer, 1, s, &x_last))) return r;
   moe::NormRouterParams nr{};
   nr.x_in = x;
@@ -451,6 +475,23 @@ int moe_block_forward(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t
   nr.T = T;
   nr.combine = 1;
   MOE_HIP(moe::launch_norm_router(ctx->d, nr, s));
+  MOE_HIP(mark(ctx->ev_after[MOE_STAGE_ALL], s));
+  return MOE_OK;
+}
+}  // namespace
+
+int moe_block_forward(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, void* y,
+                      const moe_verify_aux* aux, void* hip_stream) {
+  const int r = block_impl(ctx, layer, x, T, y, aux, hip_stream);
+  if (ctx) clear_hooks(ctx);
+  return r;
+}
+
+int moe_verify_set_stage_events(moe_verify_ctx* ctx, int32_t stage, void* before, void* after) {
+  if (!ctx) return fail(MOE_EINVAL, "ctx is NULL");
+  if (stage < 0 || stage >= MOE_STAGE_COUNT) return fail(MOE_EINVAL, "stage out of range");
+  ctx->ev_before[stage] = static_cast<hipEvent_t>(before);
+  ctx->ev_after[stage] = static_cast<hipEvent_t>(after);
   return MOE_OK;
 }
 

@@ -43,7 +43,7 @@ class VerifyModel:
     """
 
     def __init__(self, w: Workload, weights: dict, max_tokens: int | None = None,
-                 max_prefill_tokens: int = 0, k_max: int = 7, device="cuda", stream=None):
+                 max_prefill_tokens: int = 0, k_max: int = 7, device="cuda", stream=None, copies: int = 1):
         torch = _torch()
         self.w = w
         self.device = device
@@ -65,7 +65,17 @@ class VerifyModel:
             s_down=t["s_down"].data_ptr() if w.S else None, norm_gamma=t["gamma"].data_ptr(),
             final_gamma=fg.data_ptr() if fg is not None else None, lm_head=lm.data_ptr() if lm is not None else None)
         torch.cuda.synchronize()
-        self.ctx = B_.moe_verify_init(cfg, wts, stream)
+        # `copies` independent contexts (separate repacked weights) let a
+        # benchmark rotate among them so no weight byte is served from the
+        # last-level cache of a previous step
+        self.ctxs = []
+        try:
+            for _ in range(copies):
+                self.ctxs.append(B_.moe_verify_init(cfg, wts, stream))
+        except Exception:
+            self.close()
+            raise
+        self.ctx = self.ctxs[0]
         del t, fg, lm
         torch.cuda.synchronize()
         self.store_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
@@ -94,20 +104,23 @@ class VerifyModel:
             aux["hidden_out"] = torch.empty((T, w.H), dtype=self.store_dtype, device=self.device)
         return aux
 
-    def step(self, hidden, drafts, B: int, K: int, committed, counts, aux: dict | None = None, stream=None):
+    def step(self, hidden, drafts, B: int, K: int, committed, counts, aux: dict | None = None, stream=None,
+             copy: int = 0):
+        ctx = self.ctxs[copy]
         if aux is None:
-            B_.moe_verify_step(self.ctx, hidden, drafts if K > 0 else None, B, K, committed, counts, stream)
+            B_.moe_verify_step(ctx, hidden, drafts if K > 0 else None, B, K, committed, counts, stream)
         else:
-            B_.moe_verify_step_ex(self.ctx, hidden, drafts if K > 0 else None, B, K, committed, counts,
+            B_.moe_verify_step_ex(ctx, hidden, drafts if K > 0 else None, B, K, committed, counts,
                                   B_.make_aux(**aux), stream)
 
-    def block_forward(self, layer: int, x, T: int, y, aux: dict | None = None, stream=None):
-        B_.moe_block_forward(self.ctx, layer, x, T, y, B_.make_aux(**aux) if aux else None, stream)
+    def block_forward(self, layer: int, x, T: int, y, aux: dict | None = None, stream=None, copy: int = 0):
+        B_.moe_block_forward(self.ctxs[copy], layer, x, T, y, B_.make_aux(**aux) if aux else None, stream)
 
     def close(self):
-        if getattr(self, "ctx", None):
-            B_.moe_verify_destroy(self.ctx)
-            self.ctx = None
+        for c in getattr(self, "ctxs", []):
+            B_.moe_verify_destroy(c)
+        self.ctxs = []
+        self.ctx = None
 
     def __del__(self):
         try:
