@@ -51,8 +51,8 @@ struct moe_verify_ctx {
   int* n_active = nullptr;  // [1]
   char* act = nullptr;      // [tw*(k+S)][I] storage
   float* y = nullptr;       // [tw*(k+S)][H]
-  unsigned long long* keys = nullptr;  // [tw]
-  unsigned int* done = nullptr;
+  unsigned long long* keys = nullptr;  // [kKeySlots][tw]
+  unsigned int* done = nullptr;        // [1] sort-tail completion counter
 
   // one-call timing hooks (moe_verify_set_stage_events)
   hipEvent_t ev_before[MOE_STAGE_COUNT] = {};
@@ -230,6 +230,11 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   const int mult = moe::lmhead_row_multiple();
   d.Vpad = g.has_lm_head ? (d.bf16 ? (d.V + mult - 1) / mult * mult : d.V) : 0;
   MOE_HIP(hipGetDevice(&c->device));
+  int lds = 0;
+  MOE_HIP(hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device));
+  if (static_cast<size_t>(lds) < moe::norm_router_lds_bytes(d) + 256)
+    return fail(MOE_EUNSUPPORTED, "hidden size needs " + std::to_string(moe::norm_router_lds_bytes(d)) +
+                                      " bytes of LDS per workgroup; the device offers " + std::to_string(lds));
 
   const int64_t L = g.n_layers, E = g.n_routed, S = g.n_shared, H = g.hidden, I = g.inter;
   const size_t es = c->esize;
@@ -264,7 +269,7 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   if ((r = ctx_alloc_t(c, 16, &c->n_active))) return r;
   if ((r = ctx_alloc(c, rows * I * es, &c->act))) return r;
   if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->y))) return r;
-  if ((r = ctx_alloc_t(c, tw * sizeof(unsigned long long), &c->keys))) return r;
+  if ((r = ctx_alloc_t(c, moe::kKeySlots * tw * sizeof(unsigned long long), &c->keys))) return r;
   if ((r = ctx_alloc_t(c, 16, &c->done))) return r;
   MOE_HIP(hipMemsetAsync(c->done, 0, 16, s));
 
@@ -306,8 +311,6 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     nr.T = T;
     nr.norm = 1;
     nr.route = 1;
-    MOE_HIP(moe::launch_norm_router(d, nr, s));
-
     moe::PermuteParams pp{};
     pp.idx = idx;
     pp.P = T * static_cast<int>(k);
@@ -316,7 +319,13 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     pp.perm = aux && aux->perm ? aux->perm + li * T * k : c->perm;
     pp.active = c->active;
     pp.n_active = c->n_active;
-    MOE_HIP(moe::launch_permute(d, pp, s));
+    const bool fused_sort = pp.P <= moe::norm_router_sort_limit();
+    if (fused_sort) {
+      // the last norm/router workgroup sorts the pairs
+      nr.sort = moe::SortParams{idx, pp.cnt, pp.off, pp.perm, pp.active, pp.n_active, c->done + 1};
+    }
+    MOE_HIP(moe::launch_norm_router(d, nr, s));
+    if (!fused_sort) MOE_HIP(moe::launch_permute(d, pp, s));
 
     moe::ExpertParams ep{};
     ep.xhat = c->xhat;
@@ -377,6 +386,8 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
   nr.gamma = c->final_gamma;
   nr.xhat = c->xhat;
   nr.keys = c->keys;
+  nr.key_slots = moe::kKeySlots;
+  nr.key_stride = static_cast<int>(c->tw);
   nr.T = T;
   nr.combine = 1;
   nr.norm = 1;
@@ -388,7 +399,7 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
   lp.lm = c->lm;
   lp.T = T;
   lp.keys = c->keys;
-  lp.done = c->done;
+  lp.key_stride = static_cast<int>(c->tw);
   lp.drafts = drafts;
   lp.B = B;
   lp.K = K;
@@ -398,6 +409,7 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
   MOE_HIP(mark(c->ev_before[MOE_STAGE_LMHEAD], s));
   MOE_HIP(moe::launch_lmhead(d, lp, s));
   MOE_HIP(mark(c->ev_after[MOE_STAGE_LMHEAD], s));
+  MOE_HIP(moe::launch_accept(lp, s));
   MOE_HIP(mark(c->ev_after[MOE_STAGE_ALL], s));
   return MOE_OK;
 }

@@ -1,55 +1,53 @@
 // LM head + greedy arg-max + longest-prefix acceptance.
 //
 // The vocabulary matrix is streamed from HBM exactly once per step; logits are
-// never written.  bfloat16: each workgroup owns 64*R vocabulary rows (R row
-// tiles of 16 per wavefront); the K loop runs over chunks of KC 32-wide
-// k-steps.  Weight tiles go straight to registers (pre-tiled, coalesced 1 KiB
-// per wavefront per tile, one chunk prefetched ahead); the final-norm
-// activations of all tokens for the chunk are staged in LDS in operand order
-// (double-buffered) and shared by the four wavefronts.  16x16x32 MFMAs
-// accumulate [rows x tokens] in registers.  The epilogue reduces each token's
-// best (logit, lowest id) over the workgroup's rows and folds it into a 64-bit
-// key with one atomicMax per token; the last workgroup to finish (completion
-// counter) decodes the keys into the greedy picks and runs the acceptance:
-// the longest prefix of drafts equal to the picks, plus the verifier's next
-// pick (page "Jina AI releases lightweight OCR model with built-in speculative
-// decoding", section "Speculative decoding without accuracy loss").
+// never written.  Two bfloat16 kernels:
+//  * up to 16 tokens (decode): one workgroup per 16*RPW vocabulary rows; its
+//    four wavefronts split the reduction dimension in four, each issues all of
+//    its weight-tile loads at once straight into registers (pre-tiled,
+//    coalesced 1 KiB per tile) together with the matching activation
+//    fragments, runs the 16x16x32 MFMAs and the partial sums meet in LDS;
+//  * more tokens: each workgroup owns 64*R rows; the K loop runs over chunks
+//    whose activation fragments for all tokens are staged in LDS (double
+//    buffered) and shared by the four wavefronts, weights again straight to
+//    registers one chunk ahead.
+// The epilogue reduces each token's best (logit, lowest id) over the
+// workgroup's rows into a 64-bit key and folds it with one atomicMax into one
+// of kKeySlots copies of the token's key (spreading same-address atomics).
+// A one-workgroup kernel then reduces the copies into the greedy picks and
+// runs the acceptance: the longest prefix of drafts equal to the picks, plus
+// the verifier's next pick (page "Jina AI releases lightweight OCR model with
+// built-in speculative decoding", section "Speculative decoding without
+// accuracy loss").
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
 
-__device__ void finish_step(const LmHeadParams& p, unsigned int n_blocks) {
-  __shared__ int is_last;
-  __threadfence();  // this thread's key atomics complete before the count below
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned int prev = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == n_blocks - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
+// Greedy picks from the key copies and the prefix acceptance: one small
+// workgroup after the LM-head kernel (the kernel boundary makes every key
+// atomic visible, so the head kernels need no fences or completion counter).
+__global__ __launch_bounds__(kBlock) void k_accept(LmHeadParams p) {
   const int K1 = p.K + 1;
-  for (int t = threadIdx.x; t < p.T; t += kBlock) {
-    if (p.tstar) {
-      const uint64_t key = __hip_atomic_load(p.keys + t, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      p.tstar[t] = static_cast<int>(argmax_key_index(key));
+  auto pick_of = [&](int t) {
+    uint64_t best = 0ull;
+    for (int q = 0; q < kKeySlots; ++q) {
+      const uint64_t key = p.keys[static_cast<int64_t>(q) * p.key_stride + t];
+      best = key > best ? key : best;
     }
-  }
+    return static_cast<int>(argmax_key_index(best));
+  };
+  if (p.tstar)
+    for (int t = threadIdx.x; t < p.T; t += kBlock) p.tstar[t] = pick_of(t);
   for (int b = threadIdx.x; b < p.B; b += kBlock) {
     int pick[8];
-    for (int j = 0; j < K1; ++j) {
-      const uint64_t key = __hip_atomic_load(p.keys + b * K1 + j, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-      pick[j] = static_cast<int>(argmax_key_index(key));
-    }
+    for (int j = 0; j < K1; ++j) pick[j] = pick_of(b * K1 + j);
     int a = 0;
     while (a < p.K && p.drafts[b * p.K + a] == pick[a]) ++a;
     for (int j = 0; j < K1; ++j) p.committed[b * K1 + j] = j <= a ? pick[j] : -1;
     p.counts[b] = a + 1;
   }
-  __syncthreads();
-  if (threadIdx.x == 0) __hip_atomic_store(p.done, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // ---------------------------------------------------------------- bf16 ----
@@ -163,11 +161,63 @@ __global__ __launch_bounds__(kBlock) void k_lmhead_mfma(Dims d, LmHeadParams p) 
 #pragma unroll
       for (int w = 1; w < 4; ++w) b = wbest[w][threadIdx.x] > b ? wbest[w][threadIdx.x] : b;
       const int tok = tok0 + nt * kTile + threadIdx.x;
-      if (tok < p.T && b != 0ull) atomicMax(p.keys + tok, static_cast<unsigned long long>(b));
+      if (tok < p.T && b != 0ull)
+        atomicMax(p.keys + static_cast<int64_t>(blockIdx.x % kKeySlots) * p.key_stride + tok,
+                  static_cast<unsigned long long>(b));
     }
     __syncthreads();
   }
-  finish_step(p, gridDim.x * gridDim.y);
+}
+
+// K-split kernel for up to 16 tokens.  KQ = H/128 k-steps per wavefront,
+// RPW row tiles of 16 vocabulary rows per workgroup.
+template <int KQ, int RPW>
+__global__ __launch_bounds__(kBlock) void k_lmhead_ksplit(Dims d, LmHeadParams p) {
+  __shared__ float red[4][RPW][kWave][4];
+  __shared__ uint64_t kbest[RPW * 16][kTile];
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int KT = d.H / kKStep, kt0 = wave * KQ;
+  const int rt0 = blockIdx.x * RPW;
+  const bf16_t* lm = reinterpret_cast<const bf16_t*>(p.lm);
+  const bf16_t* xf = reinterpret_cast<const bf16_t*>(p.xf);
+
+  bf16x8_t a[RPW][KQ];
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    const bf16_t* w = lm + (static_cast<int64_t>(rt0 + r) * KT + kt0) * kFragElems + lane * 8;
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) a[r][i] = load_frag(w + i * kFragElems);
+  }
+  const int tok = lane % kTile;
+  bf16x8_t b[KQ];
+  const bf16_t* xr = xf + static_cast<int64_t>(tok) * d.H + kt0 * kKStep + (lane / kTile) * 8;
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) b[i] = tok < p.T ? load_frag(xr + i * kKStep) : zero_frag();
+#pragma unroll
+  for (int r = 0; r < RPW; ++r) {
+    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) c = mfma16(a[r][i], b[i], c);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) red[wave][r][lane][i] = c[i];
+  }
+  __syncthreads();
+  // logits of (row, token): sum the four reduction quarters in a fixed order
+  for (int q = threadIdx.x; q < RPW * kWave * 4; q += kBlock) {
+    const int r = q / (kWave * 4), L = (q / 4) % kWave, i = q % 4;
+    const float v = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
+    const int rl = r * 16 + 4 * (L / kTile) + i;  // row within the workgroup
+    const int row = rt0 * kTile + rl;
+    kbest[rl][L % kTile] = row < d.V ? argmax_key(v, static_cast<uint32_t>(row)) : 0ull;
+  }
+  __syncthreads();
+  if (threadIdx.x < kTile && static_cast<int>(threadIdx.x) < p.T) {
+    uint64_t best = 0ull;
+    for (int rl = 0; rl < RPW * 16; ++rl) best = kbest[rl][threadIdx.x] > best ? kbest[rl][threadIdx.x] : best;
+    if (best != 0ull)
+      atomicMax(p.keys + static_cast<int64_t>(blockIdx.x % kKeySlots) * p.key_stride + threadIdx.x,
+                static_cast<unsigned long long>(best));
+  }
 }
 
 // ------------------------------------------------------------- float32 ----
@@ -194,11 +244,19 @@ __global__ __launch_bounds__(kBlock) void k_lmhead_f32(Dims d, LmHeadParams p) {
     if (threadIdx.x == 0) {
       uint64_t b = wbest[0];
       for (int w = 1; w < 4; ++w) b = wbest[w] > b ? wbest[w] : b;
-      if (b != 0ull) atomicMax(p.keys + t, static_cast<unsigned long long>(b));
+      if (b != 0ull)
+        atomicMax(p.keys + static_cast<int64_t>(blockIdx.x % kKeySlots) * p.key_stride + t,
+                  static_cast<unsigned long long>(b));
     }
     __syncthreads();
   }
-  finish_step(p, gridDim.x);
+}
+
+template <int KQ>
+hipError_t lm_ksplit(const Dims& d, const LmHeadParams& p, hipStream_t s) {
+  constexpr int RPW = 2;
+  hipLaunchKernelGGL((k_lmhead_ksplit<KQ, RPW>), dim3(d.Vpad / (kTile * RPW)), dim3(kBlock), 0, s, d, p);
+  return hipGetLastError();
 }
 
 template <int NT>
@@ -216,6 +274,11 @@ hipError_t lm_nt(const Dims& d, const LmHeadParams& p, hipStream_t s) {
 // Rows of the tiled LM head must be padded to a multiple of this.
 int lmhead_row_multiple() { return 256; }
 
+hipError_t launch_accept(const LmHeadParams& p, hipStream_t s) {
+  hipLaunchKernelGGL(k_accept, dim3(1), dim3(kBlock), 0, s, p);
+  return hipGetLastError();
+}
+
 hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s) {
   if (!d.bf16) {
     hipLaunchKernelGGL(k_lmhead_f32, dim3((d.V + kBlock - 1) / kBlock), dim3(kBlock), 0, s, d, p);
@@ -223,7 +286,17 @@ hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s) {
   }
   if ((d.H / kKStep) % 2 != 0) return hipErrorInvalidValue;
   const int nt = (p.T + kTile - 1) / kTile;
-  if (nt <= 1) return lm_nt<1>(d, p, s);
+  if (nt <= 1) {
+    switch (d.H / 128) {
+      case 1: return lm_ksplit<1>(d, p, s);   case 2: return lm_ksplit<2>(d, p, s);
+      case 3: return lm_ksplit<3>(d, p, s);   case 4: return lm_ksplit<4>(d, p, s);
+      case 5: return lm_ksplit<5>(d, p, s);   case 6: return lm_ksplit<6>(d, p, s);
+      case 7: return lm_ksplit<7>(d, p, s);   case 8: return lm_ksplit<8>(d, p, s);
+      case 9: return lm_ksplit<9>(d, p, s);   case 10: return lm_ksplit<10>(d, p, s);
+      case 11: return lm_ksplit<11>(d, p, s); case 12: return lm_ksplit<12>(d, p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   if (nt <= 2) return lm_nt<2>(d, p, s);
   if (nt <= 4) return lm_nt<4>(d, p, s);
   return lm_nt<8>(d, p, s);

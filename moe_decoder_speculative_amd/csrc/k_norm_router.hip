@@ -1,14 +1,23 @@
-// Combine + RMSNorm + top-k softmax router, one workgroup per 16 token rows.
+// Combine + RMSNorm + top-k softmax router (+ counting sort for small steps),
+// one 1024-thread workgroup (16 wavefronts) per 16 token rows.
 //
-// Phase 1 (one wavefront per token row): optionally finish the previous block
+// Phase 1 (wavefront w owns row w): optionally finish the previous block
 //   (m = shared outputs + gate-weighted routed outputs in ascending expert
 //   order, x' = round(x + m)), then RMSNorm xh = round(x / sqrt(mean(x^2)+eps) * gamma).
-// Phase 2: router logits z = W_r xh for the 16 rows.  bfloat16 storage uses
-//   16x16x32 MFMA (wavefront w owns experts 16w..16w+15, the rows' xh sit in
-//   LDS in operand layout); float32 storage uses plain FMAs.
-// Phase 3 (one wavefront per token row, one lane per expert): k rounds of a
+//   All loads of a row are issued before they are consumed, so the phase costs
+//   a few memory latencies, not one per expert row.
+// Phase 2: router logits z = W_r xh.  bfloat16 storage uses 16x16x32 MFMA:
+//   wavefront w computes expert tile w%4 over reduction quarter w/4 (its
+//   router fragments are loaded at kernel start), the rows' xh sit in LDS in
+//   operand layout, the four quarters are summed in a fixed order.  float32
+//   storage uses plain FMAs.
+// Phase 3 (one wavefront per row, one lane per expert): k rounds of a
 //   wavefront arg-max over (logit, lower expert first), then the softmax over
 //   the k selected logits.
+// Tail (small steps): the last workgroup to finish runs the stable counting
+//   sort of all T*k (token, slot) pairs by expert in LDS (ballot ranks within a
+//   wavefront, per-wavefront counts, prefix over wavefronts), so the expert
+//   kernels that follow know each expert's tokens without another launch.
 // The mixture of 64 routed experts with top-6 routing is the decoder of the
 // page "Jina AI releases lightweight OCR model with built-in speculative
 // decoding", section "Lean architecture with a compressed encoder"; the norm,
@@ -19,8 +28,10 @@ namespace moe {
 
 namespace {
 
+constexpr int kThreads = 1024;   // 16 wavefronts
+constexpr int kWaves = kThreads / kWave;
 constexpr int kRows = 16;        // token rows per workgroup
-constexpr int kMaxChunks = 16;   // H <= 4096: 4-element chunks per lane
+constexpr int kGroup = 2;        // expert rows loaded together in the combine
 
 template <typename ST>
 struct alignas(8) Vec4 { ST v[4]; };
@@ -40,51 +51,101 @@ __device__ __forceinline__ void store4(ST* p, const float in[4]) {
   *reinterpret_cast<Vec4<ST>*>(p) = v;
 }
 
-template <typename ST>
-__global__ __launch_bounds__(kBlock) void k_norm_router(Dims d, NormRouterParams p) {
+// Stable counting sort of P pairs by expert, by one 1024-thread workgroup.
+// scratch: >= kWaves*64 + 2*64 ints of LDS.
+__device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, int* scratch) {
+  int* hist = scratch;                 // [64]
+  int* base = scratch + 64;            // [64]
+  int* wcnt = scratch + 128;           // [kWaves][64]
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int E = d.E;
+  if (tid < 64) hist[tid] = 0;
+  __syncthreads();
+  for (int i = tid; i < P; i += kThreads) atomicAdd(&hist[s.idx[i]], 1);
+  __syncthreads();
+  if (wave == 0) {
+    const int c = lane < E ? hist[lane] : 0;
+    int incl = c;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    const unsigned long long act = __ballot(c > 0);
+    base[lane] = incl - c;
+    if (lane < E) {
+      s.cnt[lane] = c;
+      s.off[lane] = incl - c;
+      if (c > 0) s.active[__popcll(act & ((1ull << lane) - 1ull))] = lane;
+    }
+    if (lane == kWave - 1) {
+      s.off[E] = incl;
+      *s.n_active = static_cast<int>(__popcll(act));
+    }
+  }
+  for (int c0 = 0; c0 < P; c0 += kThreads) {
+    for (int i = tid; i < kWaves * 64; i += kThreads) wcnt[i] = 0;
+    __syncthreads();
+    const int pidx = c0 + tid;
+    const bool valid = pidx < P;
+    const int e = valid ? s.idx[pidx] : -1;
+    // lanes of this wavefront holding the same expert
+    unsigned long long match = __ballot(valid);
+#pragma unroll
+    for (int b = 0; b < 6; ++b) {
+      const unsigned long long bit = __ballot(valid && ((e >> b) & 1));
+      match &= ((e >> b) & 1) ? bit : ~bit;
+    }
+    const int rank = __popcll(match & ((1ull << lane) - 1ull));
+    if (valid && rank == 0) wcnt[wave * 64 + e] = __popcll(match);
+    __syncthreads();
+    if (valid) {
+      int pos = base[e] + rank;
+      for (int w = 0; w < wave; ++w) pos += wcnt[w * 64 + e];
+      s.perm[pos] = pidx;
+    }
+    __syncthreads();
+    if (tid < 64) {
+      int tot = 0;
+      for (int w = 0; w < kWaves; ++w) tot += wcnt[w * 64 + tid];
+      base[tid] += tot;
+    }
+    __syncthreads();
+  }
+}
+
+template <typename ST, int KQ>  // KQ = H / 128: router k-steps per wavefront (bf16)
+__global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterParams p) {
+  // dynamic LDS: [0, 16 KiB) router partials zp[4][16][64] (reused by the sort);
+  // then bf16 xh operand tiles [H/32][64 lanes][8] or f32 xh rows [16][H]
   extern __shared__ __align__(16) unsigned char smem[];
-  // bf16: xh operand tiles [H/32][64 lanes][8]; f32: xh rows [16][H]
-  __shared__ float zl[kRows][kMaxExperts + 1];
+  float* zp = reinterpret_cast<float*>(smem);
+  unsigned char* xs = smem + 4 * kRows * 64 * sizeof(float);
+  __shared__ int is_last;
 
   const int H = d.H, k = d.k, T = p.T;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
   const int t0 = blockIdx.x * kRows;
-  const int nchunks = H / 4;  // 4-element chunks per row
+  const int nchunks = H / 4;
+  constexpr int CPL = (KQ + 1) / 2;  // 4-element chunks per lane: ceil(H / 256)
+
+  const int et = wave % 4, kq = wave / 4;
 
   // ------------------------------------------------------------ phase 1
-  for (int n = wave; n < kRows; n += 4) {
-    const int t = t0 + n;
-    if (t >= T) break;
-    float x[kMaxChunks][4];
+  const int n = wave;
+  const int t = t0 + n;
+  if (n < kRows && t < T) {
+    float x[CPL][4];
     const ST* xin = reinterpret_cast<const ST*>(p.x_in) + static_cast<int64_t>(t) * H;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
+    for (int c = 0; c < CPL; ++c) {
       const int ch = lane + c * kWave;
       if (ch < nchunks) load4<ST>(xin + 4 * ch, x[c]);
     }
     if (p.combine) {
-      float m[kMaxChunks][4];
-#pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c)
-#pragma unroll
-        for (int i = 0; i < 4; ++i) m[c][i] = 0.0f;
-      const int P = T * k;
-      for (int s = 0; s < d.S; ++s) {
-        const float* yr = p.y + static_cast<int64_t>(P + s * T + t) * H;
-#pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c) {
-          const int ch = lane + c * kWave;
-          if (ch < nchunks) {
-            float4 v = *reinterpret_cast<const float4*>(yr + 4 * ch);
-            m[c][0] = __fadd_rn(m[c][0], v.x);
-            m[c][1] = __fadd_rn(m[c][1], v.y);
-            m[c][2] = __fadd_rn(m[c][2], v.z);
-            m[c][3] = __fadd_rn(m[c][3], v.w);
-          }
-        }
-      }
-      // routed experts of this row in ascending expert order
+      // rows to add, in order: shared experts, then routed by ascending expert
+      const int nrows = d.S + k;
       int ids[kMaxTopK];
       float ws[kMaxTopK];
       int js[kMaxTopK];
@@ -94,8 +155,8 @@ __global__ __launch_bounds__(kBlock) void k_norm_router(Dims d, NormRouterParams
         js[j] = j;
       }
       for (int a = 1; a < k; ++a) {  // insertion sort by expert id
-        int ia = ids[a], ja = js[a];
-        float wa = ws[a];
+        const int ia = ids[a], ja = js[a];
+        const float wa = ws[a];
         int b = a - 1;
         while (b >= 0 && ids[b] > ia) {
           ids[b + 1] = ids[b];
@@ -107,25 +168,52 @@ __global__ __launch_bounds__(kBlock) void k_norm_router(Dims d, NormRouterParams
         js[b + 1] = ja;
         ws[b + 1] = wa;
       }
-      for (int a = 0; a < k; ++a) {
-        const float* yr = p.y + static_cast<int64_t>(t * k + js[a]) * H;
-        const float g = ws[a];
+      const int P = T * k;
+      float m[CPL][4];
 #pragma unroll
-        for (int c = 0; c < kMaxChunks; ++c) {
-          const int ch = lane + c * kWave;
-          if (ch < nchunks) {
-            float4 v = *reinterpret_cast<const float4*>(yr + 4 * ch);
-            m[c][0] = __fadd_rn(m[c][0], __fmul_rn(g, v.x));
-            m[c][1] = __fadd_rn(m[c][1], __fmul_rn(g, v.y));
-            m[c][2] = __fadd_rn(m[c][2], __fmul_rn(g, v.z));
-            m[c][3] = __fadd_rn(m[c][3], __fmul_rn(g, v.w));
+      for (int c = 0; c < CPL; ++c)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) m[c][i] = 0.0f;
+      for (int r0 = 0; r0 < nrows; r0 += kGroup) {
+        float4 v[kGroup][CPL];
+        float g[kGroup];
+#pragma unroll
+        for (int q = 0; q < kGroup; ++q) {
+          const int r = r0 + q;
+          if (r < nrows) {
+            int64_t row;
+            if (r < d.S) {
+              row = P + r * T + t;
+              g[q] = 1.0f;  // shared expert: weight 1 (1*y == y exactly)
+            } else {
+              row = static_cast<int64_t>(t) * k + js[r - d.S];
+              g[q] = ws[r - d.S];
+            }
+            const float* yr = p.y + row * H;
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              const int ch = lane + c * kWave;
+              if (ch < nchunks) v[q][c] = *reinterpret_cast<const float4*>(yr + 4 * ch);
+            }
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < kGroup; ++q) {
+          if (r0 + q < nrows) {
+#pragma unroll
+            for (int c = 0; c < CPL; ++c) {
+              m[c][0] = __fadd_rn(m[c][0], __fmul_rn(g[q], v[q][c].x));
+              m[c][1] = __fadd_rn(m[c][1], __fmul_rn(g[q], v[q][c].y));
+              m[c][2] = __fadd_rn(m[c][2], __fmul_rn(g[q], v[q][c].z));
+              m[c][3] = __fadd_rn(m[c][3], __fmul_rn(g[q], v[q][c].w));
+            }
           }
         }
       }
       ST* xout = reinterpret_cast<ST*>(p.x_out) + static_cast<int64_t>(t) * H;
       float* mo = p.m_out ? p.m_out + static_cast<int64_t>(t) * H : nullptr;
 #pragma unroll
-      for (int c = 0; c < kMaxChunks; ++c) {
+      for (int c = 0; c < CPL; ++c) {
         const int ch = lane + c * kWave;
         if (ch < nchunks) {
 #pragma unroll
@@ -135,54 +223,65 @@ __global__ __launch_bounds__(kBlock) void k_norm_router(Dims d, NormRouterParams
         }
       }
     }
-    if (!p.norm) continue;
-    float ss = 0.0f;
+    if (p.norm) {
+      float ss = 0.0f;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int ch = lane + c * kWave;
-      if (ch < nchunks)
+      for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + c * kWave;
+        if (ch < nchunks)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) ss = __fadd_rn(ss, __fmul_rn(x[c][i], x[c][i]));
-    }
-    ss = wave_sum(ss);
-    const float rms = sqrtf(ss / static_cast<float>(H) + d.eps);
-    const ST* gam = reinterpret_cast<const ST*>(p.gamma);
-    ST* xh = reinterpret_cast<ST*>(p.xhat) + static_cast<int64_t>(t) * H;
+          for (int i = 0; i < 4; ++i) ss = __fadd_rn(ss, __fmul_rn(x[c][i], x[c][i]));
+      }
+      ss = wave_sum(ss);
+      const float rms = sqrtf(ss / static_cast<float>(H) + d.eps);
+      const ST* gam = reinterpret_cast<const ST*>(p.gamma);
+      ST* xh = reinterpret_cast<ST*>(p.xhat) + static_cast<int64_t>(t) * H;
 #pragma unroll
-    for (int c = 0; c < kMaxChunks; ++c) {
-      const int ch = lane + c * kWave;
-      if (ch < nchunks) {
-        float g[4], v[4];
-        load4<ST>(gam + 4 * ch, g);
+      for (int c = 0; c < CPL; ++c) {
+        const int ch = lane + c * kWave;
+        if (ch < nchunks) {
+          float gg[4], v[4];
+          load4<ST>(gam + 4 * ch, gg);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = Storage<ST>::round(__fmul_rn(x[c][i] / rms, g[i]));
-        store4<ST>(xh + 4 * ch, v);
-        if (p.route) {
-          const int h = 4 * ch;
-          if constexpr (sizeof(ST) == 2) {
-            // operand tile kt = h/32; lane n + 16*((h%32)/8); element h%8
-            bf16_t* tile = reinterpret_cast<bf16_t*>(smem);
-            const int kt = h / 32, ln = n + 16 * ((h % 32) / 8);
-            store4<bf16_t>(tile + (kt * kWave + ln) * 8 + (h % 8), v);
-          } else {
-            float* rows = reinterpret_cast<float*>(smem);
-            *reinterpret_cast<float4*>(rows + n * H + h) = make_float4(v[0], v[1], v[2], v[3]);
+          for (int i = 0; i < 4; ++i) v[i] = Storage<ST>::round(__fmul_rn(x[c][i] / rms, gg[i]));
+          store4<ST>(xh + 4 * ch, v);
+          if (p.route) {
+            const int h = 4 * ch;
+            if constexpr (sizeof(ST) == 2) {
+              // operand tile kt = h/32; lane n + 16*((h%32)/8); element h%8
+              bf16_t* tile = reinterpret_cast<bf16_t*>(xs);
+              const int kt = h / 32, ln = n + 16 * ((h % 32) / 8);
+              store4<bf16_t>(tile + (kt * kWave + ln) * 8 + (h % 8), v);
+            } else {
+              float* rows = reinterpret_cast<float*>(xs);
+              *reinterpret_cast<float4*>(rows + n * H + h) = make_float4(v[0], v[1], v[2], v[3]);
+            }
           }
         }
       }
     }
-    if (p.keys && lane == 0) p.keys[t] = 0ull;
+    if (p.keys && lane < p.key_slots) p.keys[static_cast<int64_t>(lane) * p.key_stride + t] = 0ull;
   }
   if (!p.route) return;
 
-  // rows of this workgroup that are past T: zero operand lanes (bf16) so the
-  // MFMA reads defined values; their logits are never used.
+  // router fragments of this wavefront (requested before the barrier so the
+  // loads overlap it; not earlier, to keep phase 1 within 128 registers)
+  bf16x8_t ra[KQ];
+  if constexpr (sizeof(ST) == 2) {
+    if (et * 16 < d.E) {
+      const bf16_t* wr = reinterpret_cast<const bf16_t*>(p.router) +
+                         (static_cast<int64_t>(et) * (H / kKStep) + kq * KQ) * kFragElems + lane * 8;
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) ra[i] = load_frag(wr + i * kFragElems);
+    }
+  }
   const int nrows = min(kRows, T - t0);
   if constexpr (sizeof(ST) == 2) {
+    // rows of this workgroup past T: zero operand lanes so MFMA reads defined values
     if (nrows < kRows) {
-      bf16_t* tile = reinterpret_cast<bf16_t*>(smem);
+      bf16_t* tile = reinterpret_cast<bf16_t*>(xs);
       const int nkt = H / kKStep;
-      for (int i = threadIdx.x; i < nkt * kWave; i += kBlock) {
+      for (int i = threadIdx.x; i < nkt * kWave; i += kThreads) {
         const int ln = i % kWave;
         if ((ln % 16) >= nrows) *reinterpret_cast<uint4*>(tile + i * 8) = make_uint4(0, 0, 0, 0);
       }
@@ -191,50 +290,48 @@ __global__ __launch_bounds__(kBlock) void k_norm_router(Dims d, NormRouterParams
   __syncthreads();
 
   // ------------------------------------------------------------ phase 2
+  int nq;
   if constexpr (sizeof(ST) == 2) {
-    if (wave * 16 < d.E) {
-      const bf16_t* tile = reinterpret_cast<const bf16_t*>(smem);
-      const bf16_t* wr = reinterpret_cast<const bf16_t*>(p.router) +
-                         static_cast<int64_t>(wave) * (H / kKStep) * kFragElems;
-      f32x4_t acc0 = {0.f, 0.f, 0.f, 0.f}, acc1 = {0.f, 0.f, 0.f, 0.f};
-      const int nkt = H / kKStep;
-      int kt = 0;
-      for (; kt + 1 < nkt; kt += 2) {
-        acc0 = mfma16(load_frag(wr + kt * kFragElems + lane * 8), load_frag(tile + (kt * kWave + lane) * 8), acc0);
-        acc1 = mfma16(load_frag(wr + (kt + 1) * kFragElems + lane * 8),
-                      load_frag(tile + ((kt + 1) * kWave + lane) * 8), acc1);
-      }
-      if (kt < nkt)
-        acc0 = mfma16(load_frag(wr + kt * kFragElems + lane * 8), load_frag(tile + (kt * kWave + lane) * 8), acc0);
-      // lane holds z[expert 16*wave + 4*(lane/16) + i][row lane%16]
+    nq = 4;
+    if (et * 16 < d.E) {
+      const bf16_t* tile = reinterpret_cast<const bf16_t*>(xs);
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) zl[lane % 16][wave * 16 + 4 * (lane / 16) + i] = acc0[i] + acc1[i];
+      for (int i = 0; i < KQ; ++i) acc = mfma16(ra[i], load_frag(tile + ((kq * KQ + i) * kWave + lane) * 8), acc);
+      // lane holds z[expert 16*et + 4*(lane/16) + i][row lane%16] over quarter kq
+#pragma unroll
+      for (int i = 0; i < 4; ++i) zp[(kq * kRows + lane % 16) * 64 + et * 16 + 4 * (lane / 16) + i] = acc[i];
     }
   } else {
-    const float* rows = reinterpret_cast<const float*>(smem);
+    nq = 1;
+    const float* rows = reinterpret_cast<const float*>(xs);
     const float* wr = reinterpret_cast<const float*>(p.router);
-    for (int i = threadIdx.x; i < nrows * d.E; i += kBlock) {
-      const int n = i / d.E, e = i % d.E;
-      const float* xr = rows + n * H;
+    for (int i = threadIdx.x; i < nrows * d.E; i += kThreads) {
+      const int rn = i / d.E, e = i % d.E;
+      const float* xr = rows + rn * H;
       const float* w = wr + static_cast<int64_t>(e) * H;
       float acc = 0.0f;
       for (int h = 0; h < H; ++h) acc = __fadd_rn(acc, __fmul_rn(xr[h], w[h]));
-      zl[n][e] = acc;
+      zp[rn * 64 + e] = acc;
     }
   }
   __syncthreads();
 
   // ------------------------------------------------------------ phase 3
-  for (int n = wave; n < nrows; n += 4) {
-    const int t = t0 + n;
-    uint64_t key = lane < d.E ? argmax_key(zl[n][lane], static_cast<uint32_t>(lane)) : 0ull;
+  if (n < nrows) {
+    float z = 0.0f;
+    if (lane < d.E) {
+      z = zp[n * 64 + lane];
+      for (int q = 1; q < nq; ++q) z = __fadd_rn(z, zp[(q * kRows + n) * 64 + lane]);
+    }
+    uint64_t key = lane < d.E ? argmax_key(z, static_cast<uint32_t>(lane)) : 0ull;
     int sel_e[kMaxTopK];
     float sel_z[kMaxTopK];
     for (int j = 0; j < k; ++j) {
       const uint64_t best = wave_max_u64(key);
       const int e = static_cast<int>(argmax_key_index(best));
       sel_e[j] = e;
-      sel_z[j] = zl[n][e];
+      sel_z[j] = __shfl(z, e, kWave);
       if (lane == e) key = 0ull;
     }
     float ex[kMaxTopK];
@@ -255,21 +352,61 @@ __global__ __launch_bounds__(kBlock) void k_norm_router(Dims d, NormRouterParams
       p.w_out[t * k + lane] = wj;
     }
   }
+  if (!p.sort.done) return;
+
+  // ------------------------------------------------------------ sort tail
+  __threadfence();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const unsigned int prev = __hip_atomic_fetch_add(p.sort.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    is_last = (prev == gridDim.x - 1);
+  }
+  __syncthreads();
+  if (!is_last) return;
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+  counting_sort_block(d, p.sort, T * k, reinterpret_cast<int*>(smem));
+  if (threadIdx.x == 0) __hip_atomic_store(p.sort.done, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+template <typename ST, int KQ>
+hipError_t launch_kq(const Dims& d, const NormRouterParams& p, hipStream_t s) {
+  const dim3 grid((p.T + kRows - 1) / kRows);
+  const size_t xs = p.route ? (sizeof(ST) == 2 ? static_cast<size_t>(d.H) * 32 : static_cast<size_t>(d.H) * kRows * 4) : 0;
+  const size_t smem = 4 * kRows * 64 * sizeof(float) + xs;
+  hipLaunchKernelGGL((k_norm_router<ST, KQ>), grid, dim3(kThreads), smem, s, d, p);
+  return hipGetLastError();
+}
+
+template <typename ST>
+hipError_t launch_st(const Dims& d, const NormRouterParams& p, hipStream_t s) {
+  switch (d.H / 128) {
+    case 1: return launch_kq<ST, 1>(d, p, s);
+    case 2: return launch_kq<ST, 2>(d, p, s);
+    case 3: return launch_kq<ST, 3>(d, p, s);
+    case 4: return launch_kq<ST, 4>(d, p, s);
+    case 5: return launch_kq<ST, 5>(d, p, s);
+    case 6: return launch_kq<ST, 6>(d, p, s);
+    case 7: return launch_kq<ST, 7>(d, p, s);
+    case 8: return launch_kq<ST, 8>(d, p, s);
+    case 9: return launch_kq<ST, 9>(d, p, s);
+    case 10: return launch_kq<ST, 10>(d, p, s);
+    case 11: return launch_kq<ST, 11>(d, p, s);
+    case 12: return launch_kq<ST, 12>(d, p, s);
+    default: return hipErrorInvalidValue;
+  }
 }
 
 }  // namespace
 
+size_t norm_router_lds_bytes(const Dims& d) {
+  return 4 * kRows * 64 * sizeof(float) + (d.bf16 ? static_cast<size_t>(d.H) * 32 : static_cast<size_t>(d.H) * kRows * 4);
+}
+
+int norm_router_sort_limit() { return 8192; }
+
 hipError_t launch_norm_router(const Dims& d, const NormRouterParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
-  const dim3 grid((p.T + kRows - 1) / kRows);
-  if (d.bf16) {
-    const size_t smem = p.route ? static_cast<size_t>(d.H) * 32 : 0;  // 16 rows x H bf16
-    hipLaunchKernelGGL(k_norm_router<bf16_t>, grid, dim3(kBlock), smem, s, d, p);
-  } else {
-    const size_t smem = p.route ? static_cast<size_t>(d.H) * kRows * sizeof(float) : 0;
-    hipLaunchKernelGGL(k_norm_router<float>, grid, dim3(kBlock), smem, s, d, p);
-  }
-  return hipGetLastError();
+  return d.bf16 ? launch_st<bf16_t>(d, p, s) : launch_st<float>(d, p, s);
 }
 
 }  // namespace moe

@@ -16,6 +16,17 @@ struct Dims {
   int bf16;  // 1: bfloat16 storage and MFMA kernels; 0: float32 storage
 };
 
+// Stable counting sort of the T*k (token, slot) pairs by expert.
+struct SortParams {
+  const int* idx;        // [P] expert of pair p = t*k + j
+  int* cnt;              // [E]
+  int* off;              // [E+1]
+  int* perm;             // [P]
+  int* active;           // [E] experts with cnt > 0, ascending
+  int* n_active;         // [1]
+  unsigned int* done;    // completion counter (fused sort tail); NULL: no tail
+};
+
 // Combine (previous block) + RMSNorm + router/top-k over T token rows.
 struct NormRouterParams {
   const void* x_in;        // [T][H] storage: residual stream entering the kernel
@@ -29,11 +40,15 @@ struct NormRouterParams {
   void* xhat;              // [T][H] storage out (norm)
   int* idx_out;            // [T][k] (route)
   float* w_out;            // [T][k] (route)
-  unsigned long long* keys;  // [T] arg-max keys to clear, optional
+  unsigned long long* keys;  // [key_slots][key_stride] arg-max keys to clear, optional
+  int key_slots, key_stride;
+  SortParams sort;           // fused counting sort by the last workgroup (sort.done != NULL)
   int T;
   int combine, norm, route;
 };
 hipError_t launch_norm_router(const Dims& d, const NormRouterParams& p, hipStream_t s);
+size_t norm_router_lds_bytes(const Dims& d);
+int norm_router_sort_limit();  // largest T*k the fused sort tail handles
 
 // Stable counting sort of the T*k (token, slot) pairs by expert.
 struct PermuteParams {
@@ -68,19 +83,21 @@ hipError_t launch_expert_up(const Dims& d, const ExpertParams& p, hipStream_t s)
 hipError_t launch_expert_down(const Dims& d, const ExpertParams& p, hipStream_t s);
 
 // LM head + greedy arg-max + prefix acceptance.
+constexpr int kKeySlots = 32;  // arg-max keys are spread over this many copies
 struct LmHeadParams {
   const void* xf;            // [T][H] storage (final-norm activations)
   const void* lm;            // bf16 tiled [Vpad/16][H/32][512]; f32 [V][H]
   int T;
-  unsigned long long* keys;  // [T], cleared beforehand
-  unsigned int* done;        // completion counter, 0 on entry, left 0 on exit
+  unsigned long long* keys;  // [kKeySlots][key_stride], cleared beforehand
+  int key_stride;
   const int* drafts;         // [B][K]
   int B, K;
   int* committed;            // [B][K+1]
   int* counts;               // [B]
   int* tstar;                // [T], optional
 };
-hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s);
+hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s);  // keys only
+hipError_t launch_accept(const LmHeadParams& p, hipStream_t s);  // picks + acceptance
 
 // Weight repacking.  Tiled layout of an [R][C] bf16 matrix (R padded to Rpad
 // with zero rows): tile (rt, kt) of 16 rows x 32 columns is 512 contiguous
