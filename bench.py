@@ -182,7 +182,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b1",
-                    choices=["decode_b1", "decode_b32_zipf", "stack12_b32_zipf"])
+                    choices=["decode_b1", "decode_b32_zipf", "stack12_b32_zipf", "prefill_8pages"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for 1.5 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -213,28 +213,46 @@ def main():
 
     copy_bytes = w.L * (w.E + w.S) * expert_bytes(w) + (w.V * w.H * 2 if w.has_lm_head else 0)
     copies = args.copies or max(1, math.ceil(1.5e9 / copy_bytes))
-    model = VerifyModel(w, weights, max_tokens=w.T, copies=copies)
+    prefill = not w.has_lm_head
+    model = VerifyModel(w, weights, max_tokens=16 if prefill else w.T,
+                        max_prefill_tokens=w.T if prefill else 0, copies=copies)
     log(f"{copies} weight copies of {copy_bytes / 1e6:.0f} MB in HBM")
 
     hidden = to_device(hidden_np)
-    # drafts: each correct with probability p against this step's own greedy picks
-    committed, counts = model.alloc_outputs(w.B, w.K)
-    aux = model.alloc_aux(w.T, with_hidden=False)
-    model.step(hidden, to_device(np.zeros((w.B, w.K), np.int32)), w.B, w.K, committed, counts, aux)
-    torch.cuda.synchronize()
-    tstar = aux["tstar"].cpu().numpy()
-    touched = [len(np.unique(aux["topk_idx"][l].cpu().numpy())) for l in range(w.L)]
-    drafts_np = synth.make_drafts(w, tstar.reshape(w.B, w.K + 1))
-    drafts = to_device(drafts_np)
-    model.step(hidden, drafts, w.B, w.K, committed, counts)
-    torch.cuda.synchronize()
-    committed_per_step = int(counts.sum().item())
+    drafts_np = None
+    committed_per_step = None
+    if prefill:
+        y = torch.empty_like(hidden)
+        aux = model.alloc_aux(w.T, layers=1, with_hidden=False)
+        aux.pop("tstar")
+        model.block_forward(0, hidden, w.T, y, aux)
+        torch.cuda.synchronize()
+        touched = [int((aux["expert_count"][0] > 0).sum().item())]
+
+        def run(c):
+            model.block_forward(0, hidden, w.T, y, copy=c)
+    else:
+        # drafts: each correct with probability p against this step's own greedy picks
+        committed, counts = model.alloc_outputs(w.B, w.K)
+        aux = model.alloc_aux(w.T, with_hidden=False)
+        model.step(hidden, to_device(np.zeros((w.B, w.K), np.int32)), w.B, w.K, committed, counts, aux)
+        torch.cuda.synchronize()
+        tstar = aux["tstar"].cpu().numpy()
+        touched = [len(np.unique(aux["topk_idx"][l].cpu().numpy())) for l in range(w.L)]
+        drafts_np = synth.make_drafts(w, tstar.reshape(w.B, w.K + 1))
+        drafts = to_device(drafts_np)
+        model.step(hidden, drafts, w.B, w.K, committed, counts)
+        torch.cuda.synchronize()
+        committed_per_step = int(counts.sum().item())
+
+        def run(c):
+            model.step(hidden, drafts, w.B, w.K, committed, counts, copy=c)
     del aux
 
     ev = HipEvents()
     stream = torch.cuda.current_stream().cuda_stream
     for i in range(args.warmup):
-        model.step(hidden, drafts, w.B, w.K, committed, counts, copy=i % copies)
+        run(i % copies)
     torch.cuda.synchronize()
 
     K = args.steps
@@ -244,7 +262,7 @@ def main():
     before = [ev.create() for _ in sampled]
     after = [ev.create() for _ in sampled]
     g0, g1 = ev.create(), ev.create()
-    stage = binding.MOE_STAGE_LMHEAD if w.L == 1 else binding.MOE_STAGE_EXPERT_UP
+    stage = binding.MOE_STAGE_LMHEAD if (w.L == 1 and not prefill) else binding.MOE_STAGE_EXPERT_UP
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     ev.record(g0, stream)
@@ -252,7 +270,7 @@ def main():
         c = i % copies
         if i % EVERY == 0:
             binding.moe_verify_set_stage_events(model.ctxs[c], stage, before[i // EVERY], after[i // EVERY])
-        model.step(hidden, drafts, w.B, w.K, committed, counts, copy=c)
+        run(c)
     ev.record(g1, stream)
     torch.cuda.synchronize()
     t1 = time.perf_counter()
@@ -263,19 +281,39 @@ def main():
     for e in before + after + [g0, g1]:
         ev.destroy(e)
 
-    if stage == binding.MOE_STAGE_LMHEAD:
-        kname, kfile, kbytes = "k_lmhead_mfma", "k_lmhead.hip", lmhead_bytes(w)
+    if prefill:
+        kname, kfile = "k_grouped_gemm<up>", "k_prefill.hip"
+        kflops = (w.T * w.k + w.S * w.T) * 2 * (2 * w.I * w.H)
+        achieved = kflops / (kern_avg_ms * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": achieved / MFMA_BF16_PEAK_TFLOPS, "traffic": traffic_from_profiles(kfile, w.name),
+                "kernel": kname, "flops_per_launch": kflops}
     else:
-        kname, kfile = "k_up_mfma", "k_experts.hip"
-        kbytes = (touched[0] + w.S) * 2 * w.I * w.H * 2 + w.T * w.H * 2 + w.T * (w.k + w.S) * w.I * 2
-    achieved = kbytes / (kern_avg_ms * 1e-3) / 1e9
-    traffic = traffic_from_profiles(kfile, w.name)
+        if stage == binding.MOE_STAGE_LMHEAD:
+            kname, kfile, kbytes = ("k_lmhead_ksplit" if w.T <= 16 else "k_lmhead_mfma"), "k_lmhead.hip", lmhead_bytes(w)
+        else:
+            kname, kfile = "k_up_mfma", "k_experts.hip"
+            kbytes = (touched[0] + w.S) * 2 * w.I * w.H * 2 + w.T * w.H * 2 + w.T * (w.k + w.S) * w.I * 2
+        achieved = kbytes / (kern_avg_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles(kfile, w.name),
+                "kernel": kname, "bytes_per_launch": kbytes}
+    roof.update({"avg_us": kern_avg_ms * 1e3, "median_us": kern_ms[len(kern_ms) // 2] * 1e3,
+                 "launches_timed": len(kern_ms)})
     sbytes = step_bytes(w, touched)
+    sflops = step_flops(w)
+    step = {"gpu_ms_per_step": gpu_ms_step, "algorithmic_bytes": sbytes,
+            "hbm_frac": sbytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), "flops": sflops,
+            "mfma_frac": sflops / (ms_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+            "experts_touched_per_layer": touched}
+    if committed_per_step is not None:
+        step["committed_tokens_per_step"] = committed_per_step
+        step["committed_tokens_per_s"] = committed_per_step / (ms_step * 1e-3)
 
     res = {
         "metric": METRIC,
         "value": w.T / (ms_step * 1e-3),
-        "unit": "verified tokens/s",
+        "unit": "tokens/s" if prefill else "verified tokens/s",
         "n_gpus": 1,
         "steps": K,
         "warmup": args.warmup,
@@ -287,17 +325,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": w.name, "B": w.B, "K": w.K, "tokens_per_step": w.T, "layers": w.L,
                    "hidden": w.H, "routed_experts": w.E, "top_k": w.k, "shared_experts": w.S,
-                   "inter": w.I, "vocab": w.V, "routing": w.routing, "weight_copies": copies},
-        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": achieved / HBM_PEAK_GBS,
-                     "traffic": traffic, "kernel": kname, "bytes_per_launch": kbytes,
-                     "avg_us": kern_avg_ms * 1e3, "median_us": kern_ms[len(kern_ms) // 2] * 1e3,
-                     "launches_timed": len(kern_ms)},
-        "step": {"gpu_ms_per_step": gpu_ms_step, "algorithmic_bytes": sbytes,
-                 "hbm_frac": sbytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9),
-                 "flops": step_flops(w), "experts_touched_per_layer": touched,
-                 "committed_tokens_per_step": committed_per_step,
-                 "committed_tokens_per_s": committed_per_step / (ms_step * 1e-3)},
+                   "inter": w.I, "vocab": w.V if w.has_lm_head else 0, "routing": w.routing,
+                   "weight_copies": copies},
+        "roofline": roof,
+        "step": step,
     }
     model.close()
     torch.cuda.synchronize()

@@ -53,6 +53,9 @@ struct moe_verify_ctx {
   float* y = nullptr;       // [tw*(k+S)][H]
   unsigned long long* keys = nullptr;  // [kKeySlots][tw]
   unsigned int* done = nullptr;        // [1] sort-tail completion counter
+  int4* tiles = nullptr;               // grouped-GEMM tile table
+  int* n_tiles = nullptr;
+  bool gemm_ok = false;                // LDS allows the prefill grouped GEMM
 
   // one-call timing hooks (moe_verify_set_stage_events)
   hipEvent_t ev_before[MOE_STAGE_COUNT] = {};
@@ -71,6 +74,10 @@ int fail(int code, const std::string& msg) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
+
+// Token rows from which a block's experts run as grouped GEMMs on LDS-staged
+// MFMA tiles instead of the weight-streaming decode kernels.
+constexpr int kGemmMinTokens = 512;
 
 void clear_hooks(moe_verify_ctx* c) {
   for (int i = 0; i < MOE_STAGE_COUNT; ++i) c->ev_before[i] = c->ev_after[i] = nullptr;
@@ -232,6 +239,7 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   MOE_HIP(hipGetDevice(&c->device));
   int lds = 0;
   MOE_HIP(hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device));
+  c->gemm_ok = d.bf16 && d.H % 256 == 0 && static_cast<size_t>(lds) >= moe::gemm_lds_bytes() + 2048;
   if (static_cast<size_t>(lds) < moe::norm_router_lds_bytes(d) + 256)
     return fail(MOE_EUNSUPPORTED, "hidden size needs " + std::to_string(moe::norm_router_lds_bytes(d)) +
                                       " bytes of LDS per workgroup; the device offers " + std::to_string(lds));
@@ -271,6 +279,9 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->y))) return r;
   if ((r = ctx_alloc_t(c, moe::kKeySlots * tw * sizeof(unsigned long long), &c->keys))) return r;
   if ((r = ctx_alloc_t(c, 16, &c->done))) return r;
+  if ((r = ctx_alloc_t(c, static_cast<size_t>(moe::gemm_max_tiles(d, static_cast<int>(tw))) * sizeof(int4), &c->tiles)))
+    return r;
+  if ((r = ctx_alloc_t(c, 16, &c->n_tiles))) return r;
   MOE_HIP(hipMemsetAsync(c->done, 0, 16, s));
 
   if ((r = repack(c, w, s))) return r;
@@ -340,6 +351,29 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     ep.act = c->act;
     ep.y = c->y;
     ep.T = T;
+    if (c->gemm_ok && T >= kGemmMinTokens) {
+      // prefill-sized: grouped GEMM over (slot, feature tile, token tile) items
+      moe::GemmTileParams tp{pp.cnt, pp.off, T, c->tiles, c->n_tiles};
+      MOE_HIP(moe::launch_tile_list(d, tp, s));
+      moe::GemmParams gp{};
+      gp.xhat = c->xhat;
+      gp.w_gate = ep.w_gate;
+      gp.w_up = ep.w_up;
+      gp.w_down = ep.w_down;
+      gp.perm = pp.perm;
+      gp.tiles = c->tiles;
+      gp.n_tiles = c->n_tiles;
+      gp.act = c->act;
+      gp.y = c->y;
+      gp.T = T;
+      if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_EXPERT_UP], s));
+      MOE_HIP(moe::launch_grouped_gemm(d, gp, 1, s));
+      if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_EXPERT_UP], s));
+      if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_EXPERT_DOWN], s));
+      MOE_HIP(moe::launch_grouped_gemm(d, gp, 0, s));
+      if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_EXPERT_DOWN], s));
+      continue;
+    }
     if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_EXPERT_UP], s));
     MOE_HIP(moe::launch_expert_up(d, ep, s));
     if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_EXPERT_UP], s));

@@ -82,6 +82,31 @@ struct ExpertParams {
 hipError_t launch_expert_up(const Dims& d, const ExpertParams& p, hipStream_t s);
 hipError_t launch_expert_down(const Dims& d, const ExpertParams& p, hipStream_t s);
 
+// Grouped GEMM for prefill-sized token counts (MFMA, LDS-staged tiles).
+struct GemmTileParams {
+  const int* cnt;        // [E]
+  const int* off;        // [E+1]
+  int T;
+  int4* tiles;           // [gemm_max_tiles]: (expert, slot or -1-offset, first token, tokens)
+  int* n_tiles;          // [1]
+};
+struct GemmParams {
+  const void* xhat;      // [T][H] bf16
+  const void* w_gate;    // tiled, this layer (see ExpertParams)
+  const void* w_up;
+  const void* w_down;
+  const int* perm;       // [T*k]
+  const int4* tiles;
+  const int* n_tiles;
+  void* act;             // [T*k + S*T][I] bf16
+  float* y;              // [T*k + S*T][H] float32
+  int T;
+};
+int gemm_max_tiles(const Dims& d, int T);
+size_t gemm_lds_bytes();
+hipError_t launch_tile_list(const Dims& d, const GemmTileParams& p, hipStream_t s);
+hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipStream_t s);
+
 // LM head + greedy arg-max + prefix acceptance.
 constexpr int kKeySlots = 32;  // arg-max keys are spread over this many copies
 struct LmHeadParams {

@@ -1,10 +1,17 @@
 """Comparison of the HIP path's outputs with the oracle's (GPU tests only).
 
 Bar: bit-exact for expert sets, permutation groups, greedy picks, committed
-tokens and counts; gate weights within 1e-5; float outputs (the MoE output m
-before the residual, the residual stream) within a per-row relative error
-max|gpu - oracle| / max|oracle| of 2e-2 for bfloat16 storage and 1e-4 for
-float32 storage.
+tokens and counts; float outputs (the MoE output m before the residual, the
+residual stream) within a per-row relative error max|gpu - oracle| /
+max|oracle| of 2e-2 for bfloat16 storage and 1e-4 for float32 storage.
+
+Gate weights: within 1e-3 absolute.  Both sides compute the normalised
+activations in fp32 and round them to bf16, but the sum of squares is
+accumulated in a different order, so an activation whose fp32 value lies
+within an ulp of a bf16 rounding boundary can round the other way.  One such
+flip moves a router logit by |W_r| * 2^-8 * |xh| (about 1.3e-3 at 4 sigma of
+both) and a softmax weight by at most a quarter of that.  Without such a flip
+the weights agree to about 1e-6 (fp32 summation order).
 """
 from __future__ import annotations
 
@@ -15,7 +22,7 @@ import numpy as np
 from moe_decoder_speculative_amd.model import VerifyModel, to_device
 
 REL_TOL = {"bf16": 2e-2, "f32": 1e-4}
-W_TOL = 1e-5
+W_TOL = 1e-3
 
 
 def rowwise_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
@@ -92,3 +99,49 @@ def check_step(out: dict, case, B: int, K: int, tag=""):
     assert np.array_equal(out["counts"], ref.counts), f"{tag}: counts differ"
     assert np.array_equal(out["committed"], ref.committed), f"{tag}: committed tokens differ"
     return max(errs), float(herr)
+
+
+def check_stack_teacher_forced(out: dict, case, margin: float = 1e-3, slack: float = 2e-3):
+    """Layer-by-layer check of a multi-block step on the GPU's own residual
+    stream (see test_stack12_b32_zipf_full_shape)."""
+    import oracle
+    from oracle import moe_oracle as O
+    w, shp = case.w, case.shp
+    store = O.storage_round(shp.dtype)
+    x = O.as_f32(case.hidden)
+    undecided = 0
+    exact_traj_rows = 0
+    worst_m = 0.0
+    for l in range(shp.L):
+        ref = O.moe_block(x, case.weights["layers"][l], shp)
+        idx = out["topk_idx"][l]
+        mg = O.topk_margin(ref.z, shp.k)
+        same = np.all(np.sort(idx, 1) == np.sort(ref.idx, 1), axis=1)
+        decided = mg >= margin
+        assert np.all(same[decided]), f"layer {l}: expert sets differ on rows {np.where(decided & ~same)[0]}"
+        for t in np.where(~decided)[0]:   # valid top-k within slack
+            sel = np.zeros(shp.E, bool)
+            sel[idx[t]] = True
+            assert ref.z[t, sel].min() >= ref.z[t, ~sel].max() - slack, f"layer {l} row {t}: invalid top-k"
+        undecided += int((~decided).sum())
+        err = rowwise_rel_err(out["moe_out"][l], ref.m)
+        assert err.max() <= REL_TOL[shp.dtype], f"layer {l}: moe_out rel err {err.max():.3e}"
+        worst_m = max(worst_m, float(err.max()))
+        # the GPU's residual after this block, rebuilt exactly
+        x = store((x + out["moe_out"][l]).astype(np.float32))
+    assert np.array_equal(x, out["hidden_out"]), "rebuilt residual differs from the GPU's hidden_out"
+    lg = O.lm_head_logits(x, case.weights["final_gamma"], case.weights["lm_head"], shp.eps, store)
+    ts = out["tstar"]
+    ref_t = O.greedy_pick(lg)
+    am = O.argmax_margin(lg)
+    decided = am >= margin
+    assert np.array_equal(ts[decided], ref_t[decided]), "greedy picks differ"
+    rows = np.arange(len(ts))
+    assert np.all(lg[rows, ts] >= lg.max(1) - slack), "a greedy pick is not within slack of the maximum"
+    committed, counts = O.accept_prefix(ts.reshape(w.B, w.K + 1), case.drafts)
+    assert np.array_equal(out["counts"], counts) and np.array_equal(out["committed"], committed)
+    exact_traj_rows = int(np.sum(np.all(out["hidden_out"] == case.ref.hidden_out, axis=1)))
+    same_tokens = int(np.sum(ts == case.ref.tstar))
+    return (f"moe_out rel err {worst_m:.2e}; undecided top-k rows {undecided}, undecided picks "
+            f"{int((~decided).sum())}; rows on the oracle's exact trajectory {exact_traj_rows}/{len(ts)}; "
+            f"picks equal to the oracle's own step {same_tokens}/{len(ts)}; committed {int(counts.sum())}")

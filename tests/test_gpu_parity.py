@@ -157,7 +157,58 @@ def test_block_forward_small(T):
 
 @pytest.mark.slow
 def test_stack12_b32_zipf_full_shape():
+    """Twelve blocks.  Along twelve residual additions the bf16 rounding points
+    can resolve differently on the two sides (fp32 sums in another order), so
+    a few rows drift by up to ~1e-2 in router logits by the last layers and
+    the oracle's trajectory no longer decides them.  Each layer is therefore
+    checked teacher-forced on the GPU's own residual stream, rebuilt exactly
+    from its per-layer MoE outputs: the oracle recomputes the layer from that
+    input and the discrete outputs must match bit for bit wherever the
+    oracle's margin there is >= 1e-3 (and be a valid top-k / arg-max within
+    2e-3 elsewhere)."""
+    _torch()
     case = workloads.cached_case("stack12_b32_zipf")
-    model, out = _run_case(case, "stack12_b32_zipf")
-    model.close()
-    parity.say(f"[stack12] committed tokens this step: {int(out['counts'].sum())} over {case.w.B} sequences")
+    w = case.w
+    parity.say(f"[stack12] workload={w.name} L={w.L} B={w.B} K={w.K} T={w.T} entry=moe_verify_step_ex")
+    model = VerifyModel(w, case.weights, max_tokens=w.T)
+    try:
+        out = parity.run_step(model, case, w.B, w.K)
+    finally:
+        model.close()
+    stats = parity.check_stack_teacher_forced(out, case)
+    parity.say(f"[stack12] ok: {stats}")
+
+
+def _prefill_case_check(case, tag):
+    torch = _torch()
+    w = case.w
+    parity.say(f"[{tag}] T={w.T} H={w.H} E={w.E} k={w.k} S={w.S} I={w.I} entry=moe_block_forward "
+               f"(grouped GEMM path from 512 rows)")
+    model = VerifyModel(w, case.weights, max_tokens=16, max_prefill_tokens=w.T)
+    try:
+        x = to_device(case.hidden)
+        y = torch.empty_like(x)
+        aux = model.alloc_aux(w.T, layers=1, with_hidden=False)
+        aux.pop("tstar")
+        model.block_forward(0, x, w.T, y, aux)
+        torch.cuda.synchronize()
+        out = {k: v.cpu().numpy() for k, v in aux.items()}
+        m_err = parity.check_block(out, 0, case.ref.blocks[0], w.k, w.E, w.dtype, w.T, tag)
+        err = parity.rowwise_rel_err(parity.storage_to_f32(y), case.ref.blocks[0].x_out).max()
+        assert err <= parity.REL_TOL[w.dtype], f"{tag}: block output rel err {err:.3e}"
+        parity.say(f"[{tag}] ok: moe_out rel err {m_err:.2e}, output rel err {err:.2e}")
+    finally:
+        model.close()
+
+
+@pytest.mark.parametrize("T", [512, 1000, 2048])
+def test_block_forward_grouped_gemm_small(T):
+    """Grouped-GEMM path (T >= 512) on a small block: several token tiles per
+    expert, ragged last tiles."""
+    w = workloads.small_bf16(B=T, K=0, L=1, seed_id=70 + T).with_(has_lm_head=False, drafts="none")
+    _prefill_case_check(workloads.build_case(w), f"gemm small T{T}")
+
+
+def test_prefill_8pages_full_shape():
+    case = workloads.cached_case("prefill_8pages")
+    _prefill_case_check(case, "prefill_8pages")
