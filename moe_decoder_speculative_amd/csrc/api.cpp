@@ -239,7 +239,7 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   MOE_HIP(hipGetDevice(&c->device));
   int lds = 0;
   MOE_HIP(hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device));
-  c->gemm_ok = d.bf16 && d.H % 256 == 0 && static_cast<size_t>(lds) >= moe::gemm_lds_bytes() + 2048;
+  c->gemm_ok = d.bf16 && d.H % 256 == 0 && static_cast<size_t>(lds) >= moe::gemm_lds_bytes();
   if (static_cast<size_t>(lds) < moe::norm_router_lds_bytes(d) + 256)
     return fail(MOE_EUNSUPPORTED, "hidden size needs " + std::to_string(moe::norm_router_lds_bytes(d)) +
                                       " bytes of LDS per workgroup; the device offers " + std::to_string(lds));
@@ -265,7 +265,10 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   c->tw = tw;
   const int64_t rows = tw * (g.top_k + S);
   if ((r = ctx_alloc(c, tw * H * es, &c->xres))) return r;
-  if ((r = ctx_alloc(c, tw * H * es, &c->xhat))) return r;
+  // one extra all-zero row past the end of xhat and act: padding lanes of the
+  // grouped GEMM read it instead of branching
+  if ((r = ctx_alloc(c, (tw + 1) * H * es, &c->xhat))) return r;
+  MOE_HIP(hipMemsetAsync(c->xhat + tw * H * es, 0, H * es, s));
   for (int i = 0; i < 2; ++i) {
     if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->idx[i]))) return r;
     if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(float), &c->w[i]))) return r;
@@ -275,7 +278,8 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->perm))) return r;
   if ((r = ctx_alloc_t(c, E * sizeof(int), &c->active))) return r;
   if ((r = ctx_alloc_t(c, 16, &c->n_active))) return r;
-  if ((r = ctx_alloc(c, rows * I * es, &c->act))) return r;
+  if ((r = ctx_alloc(c, (rows + 1) * I * es, &c->act))) return r;
+  MOE_HIP(hipMemsetAsync(c->act + rows * I * es, 0, I * es, s));
   if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->y))) return r;
   if ((r = ctx_alloc_t(c, moe::kKeySlots * tw * sizeof(unsigned long long), &c->keys))) return r;
   if ((r = ctx_alloc_t(c, 16, &c->done))) return r;
@@ -366,6 +370,8 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
       gp.act = c->act;
       gp.y = c->y;
       gp.T = T;
+      gp.xhat_zero_row = static_cast<int>(c->tw);
+      gp.act_zero_row = static_cast<int>(c->tw * (g.top_k + g.n_shared));
       if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_EXPERT_UP], s));
       MOE_HIP(moe::launch_grouped_gemm(d, gp, 1, s));
       if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_EXPERT_UP], s));

@@ -3,12 +3,14 @@
 // At prefill sizes (about 915 tokens per routed expert, every token for each
 // shared expert) the experts are bound by MFMA throughput, not HBM.  Work item
 // = (expert slot, tile of 128 output features, tile of 256 of the slot's
-// tokens).  A 256-thread workgroup computes one item: its operands for a
-// 64-wide slice of the reduction dimension -- 16 weight row tiles (already in
+// tokens).  A 256-thread workgroup computes one item: its operands for each
+// 32-wide step of the reduction dimension -- 16 weight row tiles (already in
 // MFMA operand order in HBM) and 16 token tiles gathered through the
-// permutation -- are staged in LDS (double buffered, 128 KiB), and each of
-// the four wavefronts accumulates a 128 x 128 (rows x tokens) tile with
-// 16x16x32 bf16 MFMAs (256 accumulators per lane).
+// permutation (padding lanes read an all-zero row) -- go straight from global
+// memory into a 4-stage LDS ring with gfx950's direct-to-LDS 16-byte loads
+// (no registers, three steps in flight), and each of the four wavefronts
+// accumulates a 128 x 128 (rows x tokens) tile with 16x16x32 bf16 MFMAs
+// (256 accumulators per lane, in AGPRs).
 //   up:   rows are 8 gate + 8 up tiles of the same 128 features; epilogue
 //         a = round(silu(g) * u) written per pair (bf16)
 //   down: rows are 16 tiles of 16 hidden features; epilogue y (fp32) per pair
@@ -29,10 +31,8 @@ namespace {
 constexpr int kBT = 256;          // tokens per item
 constexpr int kRowTiles = 16;     // MFMA row tiles per item
 constexpr int kTokTiles = kBT / kTile;
-constexpr int kSlabK = 2;         // k-steps (of 32) per LDS slab
-constexpr int kFragsPerSlab = (kRowTiles + kTokTiles) * kSlabK;     // 64
-constexpr int kPiecesPerThread = kFragsPerSlab * kWave / kBlock;    // 16
-constexpr int kSlabElems = kFragsPerSlab * kFragElems;              // bf16 per slab
+constexpr int kStages = 4;        // LDS ring depth (one 32-wide k-step per stage), 128 KiB
+constexpr int kStageBytes = (kRowTiles + kTokTiles) * kFragElems * 2;   // 32 KiB
 constexpr int kXcds = 8;
 
 // Tile table: one entry per (slot, token tile), shared slots first, then the
@@ -62,11 +62,17 @@ __global__ __launch_bounds__(64) void k_tile_list(Dims d, GemmTileParams p) {
   if (lane == kWave - 1) *p.n_tiles = n_shared + incl;
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]); only the vector-memory count is waited on.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+
 template <bool UP>
 __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
+  // LDS ring of kStages stages; a stage holds one 32-wide k-step: 16 weight
+  // fragments then 16 token fragments, 1 KiB each, in MFMA operand order.
   extern __shared__ __align__(16) unsigned char smem[];
-  bf16_t* lds = reinterpret_cast<bf16_t*>(smem);  // [2][kFragsPerSlab][64][8]
-  __shared__ int pairs[kBT];
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int wr = wave / 2, wt = wave % 2;         // wavefront's row half / token half
@@ -83,69 +89,52 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
   const bool shared = tile.y >= 0;
   const int base = shared ? 0 : -1 - tile.y;
 
-  // pair ids of this item's tokens
-  for (int i = threadIdx.x; i < kBT; i += kBlock) {
-    int pr = -1;
-    if (i < ntok) pr = shared ? p.T * d.k + tile.y * p.T + m0 + i : p.perm[base + m0 + i];
-    pairs[i] = pr;
-  }
-  __syncthreads();
+  // pair id of the item's i-th token (-1: padding); its result row.  Read from
+  // the permutation when needed (the LDS is all ring).
+  auto pair_of = [&](int i) -> int {
+    if (i >= ntok) return -1;
+    return shared ? p.T * d.k + tile.y * p.T + m0 + i : p.perm[base + m0 + i];
+  };
 
   const int Kd = UP ? d.H : d.I;                   // reduction length
   const int KT = Kd / kKStep;
-  const int nslab = KT / kSlabK;
   const bf16_t* wa = reinterpret_cast<const bf16_t*>(UP ? p.w_gate : p.w_down);
   const bf16_t* wu = reinterpret_cast<const bf16_t*>(p.w_up);
   const bf16_t* src = reinterpret_cast<const bf16_t*>(UP ? p.xhat : p.act);
+  const int zero_row = UP ? p.xhat_zero_row : p.act_zero_row;
   const int rows_per_expert_tiles = UP ? d.I / kTile : d.H / kTile;
 
-  // per-thread staging pieces: q = threadIdx.x + kBlock * j; frag q/64, lane q%64.
-  // Pieces j < 8 are weight fragments (frag = r*kSlabK + kk, r < 16), j >= 8
-  // token fragments; their addresses advance by a fixed stride per slab.
-  const bf16_t* pbase[kPiecesPerThread];
+  // this wavefront fills weight fragments 4w..4w+3 and token fragments
+  // 4w..4w+3 of every stage; lane offsets (elements, 32-bit) advance by one
+  // k-step per stage
+  int woff[4], toff[4];
+  const bf16_t* wmat[4];
 #pragma unroll
-  for (int j = 0; j < kPiecesPerThread; ++j) {
-    const int q = threadIdx.x + kBlock * j;
-    const int f = q / kWave, ln = q % kWave;
-    const int kk = f % kSlabK, r = f / kSlabK;
-    if (r < kRowTiles) {
-      const bf16_t* mat;
-      int row_tile;
-      if (UP) {
-        const int half = r / 8, qq = r % 8;
-        mat = (qq / 4) ? wu : wa;
-        row_tile = ft * 8 + half * 4 + qq % 4;
-      } else {
-        mat = wa;
-        row_tile = ft * 16 + r;
-      }
-      pbase[j] = mat + ((static_cast<int64_t>(expert) * rows_per_expert_tiles + row_tile) * KT + kk) * kFragElems + ln * 8;
+  for (int q = 0; q < 4; ++q) {
+    const int r = wave * 4 + q;  // weight row tile of the item
+    int row_tile;
+    if (UP) {
+      const int half = r / 8, qq = r % 8;
+      wmat[q] = (qq / 4) ? wu : wa;
+      row_tile = ft * 8 + half * 4 + qq % 4;
     } else {
-      const int tt = r - kRowTiles;
-      const int pr = pairs[tt * kTile + ln % kTile];
-      if (pr < 0) {
-        pbase[j] = nullptr;
-      } else {
-        const int64_t row = UP ? static_cast<int64_t>(shared ? pr - p.T * d.k - tile.y * p.T : pr / d.k) : pr;
-        pbase[j] = src + row * Kd + kk * kKStep + (ln / kTile) * 8;
-      }
+      wmat[q] = wa;
+      row_tile = ft * 16 + r;
     }
+    woff[q] = ((expert * rows_per_expert_tiles + row_tile) * KT) * kFragElems + lane * 8;
+    const int pr = pair_of(r * kTile + lane % kTile);  // token tile r of the item
+    int row = zero_row;
+    if (pr >= 0) row = UP ? (shared ? pr - p.T * d.k - tile.y * p.T : pr / d.k) : pr;
+    toff[q] = row * Kd + (lane / kTile) * 8;
   }
-  static_assert(kRowTiles * kSlabK * kWave == 8 * kBlock, "weight pieces are j < 8");
-
-  bf16x8_t st[kPiecesPerThread];
-  auto load_slab = [&](int slab) {
+  auto issue = [&](int kt) {
+    unsigned char* st = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int j = 0; j < kPiecesPerThread; ++j) {
-      const int64_t step = j < 8 ? static_cast<int64_t>(kSlabK) * kFragElems : kSlabK * kKStep;
-      st[j] = pbase[j] ? load_frag(pbase[j] + slab * step) : zero_frag();
-    }
-  };
-  auto store_slab = [&](int buf) {
-#pragma unroll
-    for (int j = 0; j < kPiecesPerThread; ++j) {
-      const int q = threadIdx.x + kBlock * j;
-      *reinterpret_cast<bf16x8_t*>(lds + buf * kSlabElems + q * 8) = st[j];
+    for (int q = 0; q < 4; ++q) {
+      __builtin_amdgcn_global_load_lds((void*)(wmat[q] + woff[q] + kt * kFragElems),
+                                       (lds_ptr_t)(st + (wave * 4 + q) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((void*)(src + toff[q] + kt * kKStep),
+                                       (lds_ptr_t)(st + (kRowTiles + wave * 4 + q) * 1024), 16, 0, 0);
     }
   };
 
@@ -155,31 +144,78 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
 #pragma unroll
     for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  load_slab(0);
-  store_slab(0);
-  __syncthreads();
-  for (int s = 0; s < nslab; ++s) {
-    const bool more = s + 1 < nslab;
-    if (more) load_slab(s + 1);
-    const bf16_t* buf = lds + (s & 1) * kSlabElems;
-#pragma unroll
-    for (int kk = 0; kk < kSlabK; ++kk) {
-      bf16x8_t a[8], bt[8];
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        a[i] = *reinterpret_cast<const bf16x8_t*>(buf + (((wr * 8 + i) * kSlabK + kk) * kWave + lane) * 8);
-#pragma unroll
-      for (int j = 0; j < 8; ++j)
-        bt[j] = *reinterpret_cast<const bf16x8_t*>(
-            buf + (((kRowTiles + wt * 8 + j) * kSlabK + kk) * kWave + lane) * 8);
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-#pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(a[i], bt[j], acc[i][j]);
-    }
-    if (more) store_slab((s + 1) & 1);
-    __syncthreads();
+  // Fragment registers, double buffered: step k+1 is read from LDS while the
+  // 64 MFMAs of step k run.  KT is even (H and I are multiples of 128), so the
+  // loop runs in pairs with the two register sets in fixed roles.
+  //
+  // The barriers are bare: a fenced barrier would wait for every load in
+  // flight, later steps included, and drain the ring.  LDS-DMA writes are
+  // complete once vmcnt says so; each wavefront waits for its own loads of a
+  // step before the barrier, so after it every wavefront's share has landed.
+  bf16x8_t a0[8], b0[8], a1[8], b1[8];
+#define MOE_READ_STEP(K, A, B)                                                                     \
+  {                                                                                                \
+    const unsigned char* st_ = smem + ((K) % kStages) * kStageBytes;                               \
+    _Pragma("unroll") for (int j = 0; j < 8; ++j) B[j] =                                           \
+        *reinterpret_cast<const bf16x8_t*>(st_ + (kRowTiles + wt * 8 + j) * 1024 + lane * 16);     \
+    _Pragma("unroll") for (int i = 0; i < 8; ++i) A[i] =                                           \
+        *reinterpret_cast<const bf16x8_t*>(st_ + (wr * 8 + i) * 1024 + lane * 16);                 \
   }
+#define MOE_MMA_STEP(A, B)                                                                         \
+  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                    \
+  _Pragma("unroll") for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(A[i], B[j], acc[i][j]);
+  // wait for this wavefront's loads of step k+1 at iteration k: the steps
+  // issued after it (up to two) may stay in flight, 8 loads each
+#define MOE_WAIT_NEXT(K)                                                                           \
+  {                                                                                                \
+    const int later_ = min(KT, (K) + kStages) - (K) - 2;                                           \
+    if (later_ >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(24));                                   \
+    else if (later_ == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));                              \
+    else if (later_ == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));                               \
+    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                                \
+  }
+// One step: make step K+1 available (wait for this wavefront's loads, bare
+// barrier, refill the ring), then run step K's 64 MFMAs with step K+1's 16
+// fragment reads interleaved, one read after every 4 MFMAs.  Interleaving
+// matters: with all reads ahead of the MFMAs, the first MFMA waits for all of
+// them (the LDS counter cannot express "16 newer reads may stay in flight").
+// At the last step the reads fetch a stale stage that is never used.
+#define MOE_STEP(K, CA, CB, NA, NB)                                                                \
+  {                                                                                                \
+    if ((K) + 1 < KT) {                                                                            \
+      MOE_WAIT_NEXT(K)                                                                             \
+      __builtin_amdgcn_s_barrier(); /* step K+1 landed; everyone has read step K */                \
+      if ((K) + kStages < KT) issue((K) + kStages); /* into step K's buffer */                     \
+    }                                                                                              \
+    MOE_MMA_STEP(CA, CB)                                                                           \
+    MOE_READ_STEP((K) + 1, NA, NB)                                                                 \
+    _Pragma("unroll") for (int g_ = 0; g_ < 16; ++g_) {                                            \
+      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0); /* 4 MFMA */                              \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* 1 LDS read */                          \
+    }                                                                                              \
+  }
+
+#pragma unroll
+  for (int s = 0; s < kStages; ++s)
+    if (s < KT) issue(s);
+  // step 0 landed once the other issued steps (up to kStages - 1) remain
+  switch (min(KT, kStages) - 1) {
+    case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(32)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(24)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(16)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(8)); break;
+    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
+  }
+  __builtin_amdgcn_s_barrier();
+  MOE_READ_STEP(0, a0, b0)
+  for (int k = 0; k < KT; k += 2) {
+    MOE_STEP(k, a0, b0, a1, b1)
+    MOE_STEP(k + 1, a1, b1, a0, b0)
+  }
+#undef MOE_STEP
+#undef MOE_WAIT_NEXT
+#undef MOE_MMA_STEP
+#undef MOE_READ_STEP
 
   // epilogue: lane holds rows 4*(lane/16)+i of each row tile, token lane%16
   if (UP) {
@@ -189,7 +225,7 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
       const int feat = (ft * 8 + wr * 4 + f) * kTile + 4 * (lane / kTile);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int pr = pairs[(wt * 8 + j) * kTile + lane % kTile];
+        const int pr = pair_of((wt * 8 + j) * kTile + lane % kTile);
         if (pr < 0) continue;
         ushort4 v;
         v.x = f32_to_bf16(silu_mul(acc[f][j][0], acc[f + 4][j][0]));
@@ -205,7 +241,7 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
       const int feat = (ft * 16 + wr * 8 + i) * kTile + 4 * (lane / kTile);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int pr = pairs[(wt * 8 + j) * kTile + lane % kTile];
+        const int pr = pair_of((wt * 8 + j) * kTile + lane % kTile);
         if (pr < 0) continue;
         *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(pr) * d.H + feat) =
             make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
@@ -221,7 +257,7 @@ int gemm_max_tiles(const Dims& d, int T) {
   return d.S * ((T + kBT - 1) / kBT) + (T * d.k) / kBT + d.E;
 }
 
-size_t gemm_lds_bytes() { return 2ull * kSlabElems * sizeof(bf16_t); }
+size_t gemm_lds_bytes() { return static_cast<size_t>(kStages) * kStageBytes; }
 
 hipError_t launch_tile_list(const Dims& d, const GemmTileParams& p, hipStream_t s) {
   hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(64), 0, s, d, p);
@@ -229,8 +265,8 @@ hipError_t launch_tile_list(const Dims& d, const GemmTileParams& p, hipStream_t 
 }
 
 hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipStream_t s) {
-  if (d.I % 128 != 0 || d.H % 256 != 0 || (d.H / kKStep) % kSlabK != 0 || (d.I / kKStep) % kSlabK != 0)
-    return hipErrorInvalidValue;
+  // the step loop runs in pairs (H and I are multiples of 128)
+  if (d.I % 128 != 0 || d.H % 256 != 0) return hipErrorInvalidValue;
   const int n_ft = up ? d.I / 128 : d.H / 256;
   const int64_t items = static_cast<int64_t>(gemm_max_tiles(d, p.T)) * n_ft;
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;

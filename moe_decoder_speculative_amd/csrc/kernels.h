@@ -101,6 +101,8 @@ struct GemmParams {
   void* act;             // [T*k + S*T][I] bf16
   float* y;              // [T*k + S*T][H] float32
   int T;
+  int xhat_zero_row;     // an all-zero row of xhat (padding tokens read it)
+  int act_zero_row;      // an all-zero row of act
 };
 int gemm_max_tiles(const Dims& d, int T);
 size_t gemm_lds_bytes();
