@@ -52,8 +52,9 @@ __device__ __forceinline__ void store4(ST* p, const float in[4]) {
 }
 
 // Stable counting sort of P pairs by expert, by one 1024-thread workgroup.
-// scratch: >= kWaves*64 + 2*64 ints of LDS.
-__device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, int* scratch) {
+// scratch: >= kWaves*64 + 2*64 ints of LDS.  The expert ids are read from
+// `ids` (LDS) when given, else from s.idx.
+__device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, int* scratch, const int* ids) {
   int* hist = scratch;                 // [64]
   int* base = scratch + 64;            // [64]
   int* wcnt = scratch + 128;           // [kWaves][64]
@@ -61,7 +62,7 @@ __device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, i
   const int E = d.E;
   if (tid < 64) hist[tid] = 0;
   __syncthreads();
-  for (int i = tid; i < P; i += kThreads) atomicAdd(&hist[s.idx[i]], 1);
+  for (int i = tid; i < P; i += kThreads) atomicAdd(&hist[ids ? ids[i] : s.idx[i]], 1);
   __syncthreads();
   if (wave == 0) {
     const int c = lane < E ? hist[lane] : 0;
@@ -88,7 +89,7 @@ __device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, i
     __syncthreads();
     const int pidx = c0 + tid;
     const bool valid = pidx < P;
-    const int e = valid ? s.idx[pidx] : -1;
+    const int e = valid ? (ids ? ids[pidx] : s.idx[pidx]) : -1;
     // lanes of this wavefront holding the same expert
     unsigned long long match = __ballot(valid);
 #pragma unroll
@@ -122,6 +123,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   float* zp = reinterpret_cast<float*>(smem);
   unsigned char* xs = smem + 4 * kRows * 64 * sizeof(float);
   __shared__ int is_last;
+  __shared__ int sel[kRows * kMaxTopK];  // this workgroup's selections (single-workgroup sort)
 
   const int H = d.H, k = d.k, T = p.T;
   const int lane = threadIdx.x % kWave;
@@ -350,11 +352,18 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
         }
       p.idx_out[t * k + lane] = ej;
       p.w_out[t * k + lane] = wj;
+      sel[n * k + lane] = ej;
     }
   }
   if (!p.sort.done) return;
 
   // ------------------------------------------------------------ sort tail
+  if (gridDim.x == 1) {
+    // one workgroup holds every selection: sort from LDS, no cross-CU sync
+    __syncthreads();
+    counting_sort_block(d, p.sort, T * k, reinterpret_cast<int*>(smem), sel);
+    return;
+  }
   __threadfence();
   __syncthreads();
   if (threadIdx.x == 0) {
@@ -364,7 +373,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   __syncthreads();
   if (!is_last) return;
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  counting_sort_block(d, p.sort, T * k, reinterpret_cast<int*>(smem));
+  counting_sort_block(d, p.sort, T * k, reinterpret_cast<int*>(smem), nullptr);
   if (threadIdx.x == 0) __hip_atomic_store(p.sort.done, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
 }
 

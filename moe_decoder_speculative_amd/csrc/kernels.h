@@ -122,9 +122,26 @@ struct LmHeadParams {
   int* committed;            // [B][K+1]
   int* counts;               // [B]
   int* tstar;                // [T], optional
+  // Fused final combine + RMSNorm and acceptance (launch_lmhead_fused):
+  const void* x_in;          // [T][H] storage: residual entering the last block
+  const float* y;            // last block's expert outputs (see NormRouterParams)
+  const int* prev_idx;       // [T][k]
+  const float* prev_w;       // [T][k]
+  const void* gamma;         // [H] final RMSNorm gain
+  void* x_out;               // [T][H] storage: final residual, optional
+  float* m_out;              // [T][H] last block's MoE output, optional
+  void* xf_out;              // [T][H] bf16 scratch for the normalised rows
+  unsigned int* norm_count;  // rows produced (monotonic; wait until norm_target)
+  unsigned int norm_target;
+  unsigned int* done;        // workgroups finished (monotonic from done_base)
+  unsigned int done_base;
+  int* err;                  // set to 1 if a bounded wait timed out
 };
 hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s);  // keys only
 hipError_t launch_accept(const LmHeadParams& p, hipStream_t s);  // picks + acceptance
+// Up to 16 bf16 tokens: final combine + norm, LM head, picks and acceptance in
+// one launch.  Returns the number of workgroups launched in *blocks.
+hipError_t launch_lmhead_fused(const Dims& d, const LmHeadParams& p, hipStream_t s, unsigned int* blocks);
 
 // Weight repacking.  Tiled layout of an [R][C] bf16 matrix (R padded to Rpad
 // with zero rows): tile (rt, kt) of 16 rows x 32 columns is 512 contiguous
