@@ -290,7 +290,8 @@ def main():
                 "kernel": kname, "flops_per_launch": kflops}
     else:
         if stage == binding.MOE_STAGE_LMHEAD:
-            kname, kfile, kbytes = ("k_lmhead_ksplit" if w.T <= 16 else "k_lmhead_mfma"), "k_lmhead.hip", lmhead_bytes(w)
+            kname = "k_lmhead_fused" if w.T <= 16 else ("k_lmhead_wide" if w.T <= 128 else "k_lmhead_mfma")
+            kfile, kbytes = "k_lmhead.hip", lmhead_bytes(w)
         else:
             kname, kfile = "k_up_mfma", "k_experts.hip"
             kbytes = (touched[0] + w.S) * 2 * w.I * w.H * 2 + w.T * w.H * 2 + w.T * (w.k + w.S) * w.I * 2

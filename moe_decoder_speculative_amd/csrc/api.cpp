@@ -53,9 +53,7 @@ struct moe_verify_ctx {
   float* y = nullptr;       // [tw*(k+S)][H]
   unsigned long long* keys = nullptr;  // [kKeySlots][tw]
   unsigned int* done = nullptr;        // [1] sort-tail completion, [2] rows produced, [3] head workgroups done
-  int* err = nullptr;                  // set by a kernel whose bounded wait timed out
-  unsigned int norm_epoch = 0;         // running totals behind done[2] and done[3]
-  unsigned int head_epoch = 0;
+
   int4* tiles = nullptr;               // grouped-GEMM tile table
   int* n_tiles = nullptr;
   bool gemm_ok = false;                // LDS allows the prefill grouped GEMM
@@ -242,6 +240,8 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   MOE_HIP(hipGetDevice(&c->device));
   int lds = 0;
   MOE_HIP(hipDeviceGetAttribute(&lds, hipDeviceAttributeMaxSharedMemoryPerBlock, c->device));
+  MOE_HIP(hipDeviceGetAttribute(&d.n_cu, hipDeviceAttributeMultiprocessorCount, c->device));
+  if (d.n_cu < 1) d.n_cu = 1;
   c->gemm_ok = d.bf16 && d.H % 256 == 0 && static_cast<size_t>(lds) >= moe::gemm_lds_bytes();
   if (static_cast<size_t>(lds) < moe::norm_router_lds_bytes(d) + 256)
     return fail(MOE_EUNSUPPORTED, "hidden size needs " + std::to_string(moe::norm_router_lds_bytes(d)) +
@@ -290,8 +290,7 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
     return r;
   if ((r = ctx_alloc_t(c, 16, &c->n_tiles))) return r;
   MOE_HIP(hipMemsetAsync(c->done, 0, 16, s));
-  if ((r = ctx_alloc_t(c, 16, &c->err))) return r;
-  MOE_HIP(hipMemsetAsync(c->err, 0, 16, s));
+
   // arg-max keys are zero between steps (the acceptance clears them after use)
   MOE_HIP(hipMemsetAsync(c->keys, 0, moe::kKeySlots * tw * sizeof(unsigned long long), s));
 
@@ -423,59 +422,6 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
 
   const int64_t H = g.hidden, k = g.top_k;
   const int li = g.n_layers - 1;
-  if (d.bf16 && T <= 16) {
-    // final combine + norm, LM head, picks and acceptance in one launch
-    moe::LmHeadParams lp{};
-    lp.lm = c->lm;
-    lp.T = T;
-    lp.keys = c->keys;
-    lp.key_stride = static_cast<int>(c->tw);
-    lp.drafts = drafts;
-    lp.B = B;
-    lp.K = K;
-    lp.committed = committed;
-    lp.counts = counts;
-    lp.tstar = aux ? aux->tstar : nullptr;
-    lp.x_in = x_last;
-    lp.y = c->y;
-    lp.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
-    lp.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
-    lp.gamma = c->final_gamma;
-    lp.x_out = aux ? aux->hidden_out : nullptr;
-    lp.m_out = aux && aux->moe_out ? aux->moe_out + li * T * H : nullptr;
-    lp.xf_out = c->xhat;
-    lp.norm_count = c->done + 2;
-    lp.norm_target = c->norm_epoch + static_cast<unsigned>(T);
-    lp.done = c->done + 3;
-    lp.done_base = c->head_epoch;
-    lp.err = c->err;
-    unsigned int blocks = 0;
-    MOE_HIP(mark(c->ev_before[MOE_STAGE_LMHEAD], s));
-    MOE_HIP(moe::launch_lmhead_fused(d, lp, s, &blocks));
-    MOE_HIP(mark(c->ev_after[MOE_STAGE_LMHEAD], s));
-    MOE_HIP(mark(c->ev_after[MOE_STAGE_ALL], s));
-    c->norm_epoch += static_cast<unsigned>(T);
-    c->head_epoch += blocks;
-    return MOE_OK;
-  }
-  moe::NormRouterParams nr{};
-  nr.x_in = x_last;
-  nr.x_out = aux && aux->hidden_out ? aux->hidden_out : c->xres;
-  nr.y = c->y;
-  nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
-  nr.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
-  nr.m_out = aux && aux->moe_out ? aux->moe_out + li * T * H : nullptr;
-  nr.gamma = c->final_gamma;
-  nr.xhat = c->xhat;
-  nr.keys = c->keys;
-  nr.key_slots = moe::kKeySlots;
-  nr.key_stride = static_cast<int>(c->tw);
-  nr.T = T;
-  nr.combine = 1;
-  nr.norm = 1;
-  nr.route = 0;
-  MOE_HIP(moe::launch_norm_router(d, nr, s));
-
   moe::LmHeadParams lp{};
   lp.xf = c->xhat;
   lp.lm = c->lm;
@@ -488,6 +434,36 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
   lp.committed = committed;
   lp.counts = counts;
   lp.tstar = aux ? aux->tstar : nullptr;
+  if (d.bf16) {
+    // final combine + norm: one workgroup per row
+    lp.x_in = x_last;
+    lp.y = c->y;
+    lp.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
+    lp.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
+    lp.gamma = c->final_gamma;
+    lp.x_out = aux ? aux->hidden_out : nullptr;
+    lp.m_out = aux && aux->moe_out ? aux->moe_out + li * T * H : nullptr;
+    lp.xf_out = c->xhat;
+    MOE_HIP(moe::launch_final_norm(d, lp, s));
+  } else {
+    moe::NormRouterParams nr{};
+    nr.x_in = x_last;
+    nr.x_out = aux && aux->hidden_out ? aux->hidden_out : c->xres;
+    nr.y = c->y;
+    nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
+    nr.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
+    nr.m_out = aux && aux->moe_out ? aux->moe_out + li * T * H : nullptr;
+    nr.gamma = c->final_gamma;
+    nr.xhat = c->xhat;
+    nr.keys = c->keys;
+    nr.key_slots = moe::kKeySlots;
+    nr.key_stride = static_cast<int>(c->tw);
+    nr.T = T;
+    nr.combine = 1;
+    nr.norm = 1;
+    nr.route = 0;
+    MOE_HIP(moe::launch_norm_router(d, nr, s));
+  }
   MOE_HIP(mark(c->ev_before[MOE_STAGE_LMHEAD], s));
   MOE_HIP(moe::launch_lmhead(d, lp, s));
   MOE_HIP(mark(c->ev_after[MOE_STAGE_LMHEAD], s));

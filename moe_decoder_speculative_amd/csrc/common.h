@@ -52,6 +52,25 @@ __device__ __forceinline__ bf16x8_t zero_frag() {
   return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));
 }
 
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
+// [6:4], lgkmcnt [11:8]).  waitcnt_vm(n): at most n vector-memory operations
+// of this wavefront outstanding; waitcnt_lgkm0: all LDS / scalar operations done.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int waitcnt_lgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Workgroup barrier for LDS hand-offs only.  __syncthreads() also waits for
+// every outstanding global load, which would drain a prefetch pipeline; this
+// one waits for this wavefront's LDS operations and keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 __device__ __forceinline__ f32x4_t mfma16(bf16x8_t a, bf16x8_t b, f32x4_t c) {
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
@@ -73,8 +92,9 @@ __device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
 
 // Order-preserving map of float32 to uint32 (larger float -> larger key).
 __device__ __forceinline__ uint32_t orderable(float f) {
-  uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: all bits flipped; otherwise the sign bit set (branch-free)
+  const uint32_t u = __float_as_uint(f);
+  return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
 }
 
 // Arg-max key: the larger value wins; on equal values the lower index wins.

@@ -1,57 +1,75 @@
-// LM head + greedy arg-max + longest-prefix acceptance.
+// Final norm, LM head + greedy arg-max, longest-prefix acceptance.
 //
-// The vocabulary matrix is streamed from HBM exactly once per step; logits are
-// never written.  Two bfloat16 kernels:
-//  * up to 16 tokens (decode): one workgroup per 16*RPW vocabulary rows; its
-//    four wavefronts split the reduction dimension in four, each issues all of
-//    its weight-tile loads at once straight into registers (pre-tiled,
-//    coalesced 1 KiB per tile) together with the matching activation
-//    fragments, runs the 16x16x32 MFMAs and the partial sums meet in LDS;
-//  * more tokens: each workgroup owns 64*R rows; the K loop runs over chunks
-//    whose activation fragments for all tokens are staged in LDS (double
-//    buffered) and shared by the four wavefronts, weights again straight to
-//    registers one chunk ahead.
-// The epilogue reduces each token's best (logit, lowest id) over the
-// workgroup's rows into a 64-bit key and folds it with one atomicMax into one
-// of kKeySlots copies of the token's key (spreading same-address atomics).
-// A one-workgroup kernel then reduces the copies into the greedy picks and
-// runs the acceptance: the longest prefix of drafts equal to the picks, plus
-// the verifier's next pick (page "Jina AI releases lightweight OCR model with
-// built-in speculative decoding", section "Speculative decoding without
-// accuracy loss").
+// Three launches, back to back on the step's stream:
+//  1. k_final_norm: one workgroup per token row finishes the last block
+//     (shared + gate-weighted routed expert outputs in a fixed order, the
+//     residual add and its rounding) and applies the final RMSNorm;
+//  2. an LM-head kernel streams the vocabulary matrix from HBM exactly once
+//     and folds each token's best (logit, lowest id) into one of kKeySlots
+//     64-bit keys with an atomicMax (logits are never written):
+//       * up to 16 tokens: k_lmhead_stream, persistent, two 256-thread
+//         workgroups per CU; the four wavefronts split the reduction and the
+//         next unit's weight tiles are loaded while the current one is reduced;
+//       * 17..128 tokens: k_lmhead_wide, persistent, one 512-thread workgroup
+//         per CU with register rings of weight and activation fragments;
+//       * more: k_lmhead_mfma, activation fragments staged in LDS;
+//  3. k_accept reduces the key copies into the greedy picks, leaves them at
+//     zero for the next step and runs the acceptance: the longest prefix of
+//     drafts equal to the picks, plus the verifier's next pick (page "Jina AI
+//     releases lightweight OCR model with built-in speculative decoding",
+//     section "Speculative decoding without accuracy loss").
+// Separate launches beat in-kernel hand-offs here: a cross-workgroup signal
+// through memory costs a store and a poll round trip (several microseconds
+// across XCDs), while consecutive launches on one queue start within about a
+// microsecond and the kernel boundary orders the memory.
 #include "kernels.h"
 
 namespace moe {
 
 namespace {
 
-// Greedy picks from the key copies and the prefix acceptance: one small
-// workgroup after the LM-head kernel (the kernel boundary makes every key
-// atomic visible, so the head kernels need no fences or completion counter).
+// ------------------------------------------------------------ acceptance ----
+// One workgroup per kAcceptSeqs sequences: every key copy of its tokens is
+// read once (all loads in flight together) and cleared, the copies are folded
+// per token in LDS, then one thread per sequence runs the acceptance.
+constexpr int kAcceptSeqs = 32;
+constexpr int kAcceptTok = kAcceptSeqs * 8;  // K + 1 <= 8 tokens per sequence
+
 __global__ __launch_bounds__(kBlock) void k_accept(LmHeadParams p) {
+  __shared__ unsigned long long best[kAcceptTok];
   const int K1 = p.K + 1;
-  auto pick_of = [&](int t) {
-    uint64_t best = 0ull;
-    for (int q = 0; q < kKeySlots; ++q) {
-      const uint64_t key = p.keys[static_cast<int64_t>(q) * p.key_stride + t];
-      best = key > best ? key : best;
+  const int b0 = blockIdx.x * kAcceptSeqs;
+  const int nb = min(kAcceptSeqs, p.B - b0);
+  const int t0 = b0 * K1, nt = nb * K1;
+  for (int t = threadIdx.x; t < nt; t += kBlock) best[t] = 0ull;
+  __syncthreads();
+  constexpr int kPer = kKeySlots * kAcceptTok / kBlock;
+  unsigned long long kv[kPer];
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = threadIdx.x + q * kBlock;  // copy i / nt of token i % nt
+    kv[q] = i < kKeySlots * nt ? p.keys[static_cast<int64_t>(i / nt) * p.key_stride + t0 + i % nt] : 0ull;
+  }
+#pragma unroll
+  for (int q = 0; q < kPer; ++q) {
+    const int i = threadIdx.x + q * kBlock;
+    if (i < kKeySlots * nt) {
+      p.keys[static_cast<int64_t>(i / nt) * p.key_stride + t0 + i % nt] = 0ull;
+      atomicMax(best + i % nt, kv[q]);
     }
-    return static_cast<int>(argmax_key_index(best));
-  };
-  if (p.tstar)
-    for (int t = threadIdx.x; t < p.T; t += kBlock) p.tstar[t] = pick_of(t);
-  for (int b = threadIdx.x; b < p.B; b += kBlock) {
-    int pick[8];
-    for (int j = 0; j < K1; ++j) pick[j] = pick_of(b * K1 + j);
-    int a = 0;
-    while (a < p.K && p.drafts[b * p.K + a] == pick[a]) ++a;
-    for (int j = 0; j < K1; ++j) p.committed[b * K1 + j] = j <= a ? pick[j] : -1;
-    p.counts[b] = a + 1;
   }
   __syncthreads();
-  // leave every key copy at zero for the next step
-  for (int i = threadIdx.x; i < kKeySlots * p.T; i += kBlock)
-    p.keys[static_cast<int64_t>(i / p.T) * p.key_stride + i % p.T] = 0ull;
+  if (p.tstar)
+    for (int t = threadIdx.x; t < nt; t += kBlock) p.tstar[t0 + t] = static_cast<int>(argmax_key_index(best[t]));
+  if (static_cast<int>(threadIdx.x) < nb) {
+    const int b = b0 + threadIdx.x;
+    const unsigned long long* pk = best + threadIdx.x * K1;
+    int a = 0;
+    while (a < p.K && p.drafts[b * p.K + a] == static_cast<int>(argmax_key_index(pk[a]))) ++a;
+    for (int j = 0; j < K1; ++j)
+      p.committed[b * K1 + j] = j <= a ? static_cast<int>(argmax_key_index(pk[j])) : -1;
+    p.counts[b] = a + 1;
+  }
 }
 
 // ---------------------------------------------------------------- bf16 ----
@@ -173,58 +191,7 @@ __global__ __launch_bounds__(kBlock) void k_lmhead_mfma(Dims d, LmHeadParams p) 
   }
 }
 
-// K-split kernel for up to 16 tokens.  KQ = H/128 k-steps per wavefront,
-// RPW row tiles of 16 vocabulary rows per workgroup.
-template <int KQ, int RPW>
-__global__ __launch_bounds__(kBlock) void k_lmhead_ksplit(Dims d, LmHeadParams p) {
-  __shared__ float red[4][RPW][kWave][4];
-  __shared__ uint64_t kbest[RPW * 16][kTile];
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int KT = d.H / kKStep, kt0 = wave * KQ;
-  const int rt0 = blockIdx.x * RPW;
-  const bf16_t* lm = reinterpret_cast<const bf16_t*>(p.lm);
-  const bf16_t* xf = reinterpret_cast<const bf16_t*>(p.xf);
 
-  bf16x8_t a[RPW][KQ];
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    const bf16_t* w = lm + (static_cast<int64_t>(rt0 + r) * KT + kt0) * kFragElems + lane * 8;
-#pragma unroll
-    for (int i = 0; i < KQ; ++i) a[r][i] = load_frag(w + i * kFragElems);
-  }
-  const int tok = lane % kTile;
-  bf16x8_t b[KQ];
-  const bf16_t* xr = xf + static_cast<int64_t>(tok) * d.H + kt0 * kKStep + (lane / kTile) * 8;
-#pragma unroll
-  for (int i = 0; i < KQ; ++i) b[i] = tok < p.T ? load_frag(xr + i * kKStep) : zero_frag();
-#pragma unroll
-  for (int r = 0; r < RPW; ++r) {
-    f32x4_t c = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int i = 0; i < KQ; ++i) c = mfma16(a[r][i], b[i], c);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) red[wave][r][lane][i] = c[i];
-  }
-  __syncthreads();
-  // logits of (row, token): sum the four reduction quarters in a fixed order
-  for (int q = threadIdx.x; q < RPW * kWave * 4; q += kBlock) {
-    const int r = q / (kWave * 4), L = (q / 4) % kWave, i = q % 4;
-    const float v = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
-    const int rl = r * 16 + 4 * (L / kTile) + i;  // row within the workgroup
-    const int row = rt0 * kTile + rl;
-    kbest[rl][L % kTile] = row < d.V ? argmax_key(v, static_cast<uint32_t>(row)) : 0ull;
-  }
-  __syncthreads();
-  if (threadIdx.x < kTile && static_cast<int>(threadIdx.x) < p.T) {
-    uint64_t best = 0ull;
-    for (int rl = 0; rl < RPW * 16; ++rl) best = kbest[rl][threadIdx.x] > best ? kbest[rl][threadIdx.x] : best;
-    if (best != 0ull)
-      atomicMax(p.keys + static_cast<int64_t>(blockIdx.x % kKeySlots) * p.key_stride + threadIdx.x,
-                static_cast<unsigned long long>(best));
-  }
-}
-
-// ------------------------------------------------------------- float32 ----
 // One thread per vocabulary row, loop over tokens; float32 storage only.
 
 __global__ __launch_bounds__(kBlock) void k_lmhead_f32(Dims d, LmHeadParams p) {
@@ -257,108 +224,124 @@ __global__ __launch_bounds__(kBlock) void k_lmhead_f32(Dims d, LmHeadParams p) {
 }
 
 
-// ------------------------------------------------- fused decode head ----
-// Up to 16 tokens.  Workgroups 0..T-1 first produce one normalised row each
-// (finish the last block: m = shared + gate-weighted routed outputs in
-// ascending expert order, x = round(x + m), RMSNorm with the final gain), and
-// publish it with agent-scope stores and a counter; every workgroup issues
-// its weight loads before waiting for the T rows, so the final norm overlaps
-// the head's weight stream.  The workgroup that finishes last (counter) turns
-// the key copies into the greedy picks and runs the acceptance.  Counters are
-// monotonic across steps (the host passes the epoch), waits are bounded (on a
-// timeout *err is set and the step's outputs are invalid).
-constexpr unsigned kSpinLimit = 1u << 22;
 
-__device__ __forceinline__ void store_u64_agent(void* p, uint64_t v) {
-  __hip_atomic_store(reinterpret_cast<uint64_t*>(p), v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ uint64_t load_u64_agent(const void* p) {
-  return __hip_atomic_load(reinterpret_cast<const uint64_t*>(p), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-template <int CPB>  // 4-element chunks per thread: ceil(H / 1024)
-__device__ void produce_final_row(const Dims& d, const LmHeadParams& p, int t, float* red) {
-  const int H = d.H, k = d.k, T = p.T, tid = threadIdx.x;
+// One normalised row t, computed by a whole workgroup of NTHR threads: finish
+// the last block (m = shared + gate-weighted routed outputs, x = round(x + m))
+// and apply the final RMSNorm.  red holds NTHR / 64 floats, stage
+// kMaxTopK * NTHR * CPB float4 of LDS.  Every
+// load (the row, the gain, the row's expert ids and gate weights, all shared-
+// and routed-expert output rows in slot order) is issued before any is used,
+// so the row costs about one memory latency.  The combine order -- shared
+// experts, then routed experts by ascending id -- is applied through LDS: the
+// product w_j * y_j of routed slot j is stored at the slot's rank among the
+// row's ids and the products are added back in rank order (the same rounded
+// operations in the same order as adding w * y expert by expert).
+template <int NTHR, int CPB>  // CPB 4-element chunks per thread: ceil(H / (4 * NTHR))
+__device__ __forceinline__ void produce_final_row(const Dims& d, const LmHeadParams& p, int t, float* red,
+                                                  float4* stage) {
+  const int H = d.H, k = d.k, S = d.S, T = p.T, tid = threadIdx.x;
   const int nchunks = H / 4;
   const bf16_t* xin = reinterpret_cast<const bf16_t*>(p.x_in) + static_cast<int64_t>(t) * H;
-  float x[CPB][4];
+  const bf16_t* gam = reinterpret_cast<const bf16_t*>(p.gamma);
+  int idv[kMaxTopK];
+  float wv[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {  // indices clamped to the row's k entries
+    idv[j] = p.prev_idx[t * k + min(j, k - 1)];
+    wv[j] = p.prev_w[t * k + min(j, k - 1)];
+  }
+  uint2 xv[CPB], gv[CPB];
+  float4 vs[4][CPB], vr[kMaxTopK][CPB];  // shared-expert rows; routed rows by slot
 #pragma unroll
   for (int c = 0; c < CPB; ++c) {
-    const int ch = tid + c * kBlock;
+    const int ch = tid + c * NTHR;
     if (ch < nchunks) {
-      const uint2 v = *reinterpret_cast<const uint2*>(xin + 4 * ch);
-      x[c][0] = __uint_as_float(v.x << 16);
-      x[c][1] = __uint_as_float(v.x & 0xffff0000u);
-      x[c][2] = __uint_as_float(v.y << 16);
-      x[c][3] = __uint_as_float(v.y & 0xffff0000u);
+      xv[c] = *reinterpret_cast<const uint2*>(xin + 4 * ch);
+      gv[c] = *reinterpret_cast<const uint2*>(gam + 4 * ch);
     }
   }
-  // rows in the combine order: shared experts, then routed by ascending expert
-  int ids[kMaxTopK], js[kMaxTopK];
-  float ws[kMaxTopK];
-  for (int j = 0; j < k; ++j) {
-    ids[j] = p.prev_idx[t * k + j];
-    ws[j] = p.prev_w[t * k + j];
-    js[j] = j;
-  }
-  for (int a = 1; a < k; ++a) {
-    const int ia = ids[a], ja = js[a];
-    const float wa = ws[a];
-    int b = a - 1;
-    while (b >= 0 && ids[b] > ia) {
-      ids[b + 1] = ids[b];
-      js[b + 1] = js[b];
-      ws[b + 1] = ws[b];
-      --b;
-    }
-    ids[b + 1] = ia;
-    js[b + 1] = ja;
-    ws[b + 1] = wa;
-  }
-  const int nrows = d.S + k;
-  constexpr int kRowsMax = 4 + kMaxTopK;
-  float4 v[kRowsMax][CPB];
-  float g[kRowsMax];
 #pragma unroll
-  for (int r = 0; r < kRowsMax; ++r) {
-    if (r < nrows) {
-      int64_t row;
-      if (r < d.S) {
-        row = static_cast<int64_t>(T) * k + r * T + t;
-        g[r] = 1.0f;  // shared expert: weight 1 (1*y == y exactly)
-      } else {
-        row = static_cast<int64_t>(t) * k + js[r - d.S];
-        g[r] = ws[r - d.S];
-      }
-      const float* yr = p.y + row * H;
+  for (int r = 0; r < 4; ++r) {  // shared expert r: row T*k + r*T + t
+    const float* yr = p.y + (static_cast<int64_t>(T) * k + r * T + t) * H;
+#pragma unroll
+    for (int c = 0; c < CPB; ++c) {
+      const int ch = tid + c * NTHR;
+      if (r < S && ch < nchunks) vs[r][c] = *reinterpret_cast<const float4*>(yr + 4 * ch);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {  // routed slot j: row t*k + j
+    const float* yr = p.y + (static_cast<int64_t>(t) * k + j) * H;
+#pragma unroll
+    for (int c = 0; c < CPB; ++c) {
+      const int ch = tid + c * NTHR;
+      if (j < k && ch < nchunks) vr[j][c] = *reinterpret_cast<const float4*>(yr + 4 * ch);
+    }
+  }
+  // rank of each slot among the row's (distinct) ids: uniform scalars
+  int ids[kMaxTopK];
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) ids[j] = __builtin_amdgcn_readfirstlane(idv[j]);
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      int rank = 0;
+#pragma unroll
+      for (int q = 0; q < kMaxTopK; ++q) rank += (q < k && ids[q] < ids[j]) ? 1 : 0;
 #pragma unroll
       for (int c = 0; c < CPB; ++c) {
-        const int ch = tid + c * kBlock;
-        if (ch < nchunks) v[r][c] = *reinterpret_cast<const float4*>(yr + 4 * ch);
+        const int ch = tid + c * NTHR;
+        if (ch < nchunks)
+          stage[(rank * CPB + c) * NTHR + tid] =
+              make_float4(__fmul_rn(wv[j], vr[j][c].x), __fmul_rn(wv[j], vr[j][c].y),
+                          __fmul_rn(wv[j], vr[j][c].z), __fmul_rn(wv[j], vr[j][c].w));
       }
     }
   }
-  float m[CPB][4];
+  float x[CPB][4], m[CPB][4];
 #pragma unroll
-  for (int c = 0; c < CPB; ++c)
+  for (int c = 0; c < CPB; ++c) {
+    x[c][0] = __uint_as_float(xv[c].x << 16);
+    x[c][1] = __uint_as_float(xv[c].x & 0xffff0000u);
+    x[c][2] = __uint_as_float(xv[c].y << 16);
+    x[c][3] = __uint_as_float(xv[c].y & 0xffff0000u);
 #pragma unroll
     for (int i = 0; i < 4; ++i) m[c][i] = 0.0f;
+  }
+  // shared experts: weight 1 (1 * y == y exactly)
 #pragma unroll
-  for (int r = 0; r < kRowsMax; ++r) {
-    if (r < nrows) {
+  for (int r = 0; r < 4; ++r) {
+    if (r < S) {
 #pragma unroll
       for (int c = 0; c < CPB; ++c) {
-        m[c][0] = __fadd_rn(m[c][0], __fmul_rn(g[r], v[r][c].x));
-        m[c][1] = __fadd_rn(m[c][1], __fmul_rn(g[r], v[r][c].y));
-        m[c][2] = __fadd_rn(m[c][2], __fmul_rn(g[r], v[r][c].z));
-        m[c][3] = __fadd_rn(m[c][3], __fmul_rn(g[r], v[r][c].w));
+        m[c][0] = __fadd_rn(m[c][0], vs[r][c].x);
+        m[c][1] = __fadd_rn(m[c][1], vs[r][c].y);
+        m[c][2] = __fadd_rn(m[c][2], vs[r][c].z);
+        m[c][3] = __fadd_rn(m[c][3], vs[r][c].w);
+      }
+    }
+  }
+  // routed experts by ascending id (this thread's own LDS slots: no barrier)
+#pragma unroll
+  for (int q = 0; q < kMaxTopK; ++q) {
+    if (q < k) {
+#pragma unroll
+      for (int c = 0; c < CPB; ++c) {
+        const int ch = tid + c * NTHR;
+        if (ch < nchunks) {
+          const float4 y = stage[(q * CPB + c) * NTHR + tid];
+          m[c][0] = __fadd_rn(m[c][0], y.x);
+          m[c][1] = __fadd_rn(m[c][1], y.y);
+          m[c][2] = __fadd_rn(m[c][2], y.z);
+          m[c][3] = __fadd_rn(m[c][3], y.w);
+        }
       }
     }
   }
   float ss = 0.0f;
 #pragma unroll
   for (int c = 0; c < CPB; ++c) {
-    const int ch = tid + c * kBlock;
+    const int ch = tid + c * NTHR;
     if (ch < nchunks) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -381,33 +364,45 @@ __device__ void produce_final_row(const Dims& d, const LmHeadParams& p, int t, f
   ss = wave_sum(ss);
   if (tid % kWave == 0) red[tid / kWave] = ss;
   __syncthreads();
-  ss = ((red[0] + red[1]) + red[2]) + red[3];
+  ss = red[0];
+#pragma unroll
+  for (int w = 1; w < NTHR / kWave; ++w) ss += red[w];
   const float rms = sqrtf(ss / static_cast<float>(H) + d.eps);
-  const bf16_t* gam = reinterpret_cast<const bf16_t*>(p.gamma);
   bf16_t* xf = reinterpret_cast<bf16_t*>(p.xf_out) + static_cast<int64_t>(t) * H;
 #pragma unroll
   for (int c = 0; c < CPB; ++c) {
-    const int ch = tid + c * kBlock;
+    const int ch = tid + c * NTHR;
     if (ch < nchunks) {
-      const uint2 gv = *reinterpret_cast<const uint2*>(gam + 4 * ch);
-      const float gg[4] = {__uint_as_float(gv.x << 16), __uint_as_float(gv.x & 0xffff0000u),
-                           __uint_as_float(gv.y << 16), __uint_as_float(gv.y & 0xffff0000u)};
+      const float gg[4] = {__uint_as_float(gv[c].x << 16), __uint_as_float(gv[c].x & 0xffff0000u),
+                           __uint_as_float(gv[c].y << 16), __uint_as_float(gv[c].y & 0xffff0000u)};
       uint64_t packed = 0;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
         packed |= static_cast<uint64_t>(f32_to_bf16(__fmul_rn(x[c][i] / rms, gg[i]))) << (16 * i);
-      store_u64_agent(xf + 4 * ch, packed);
+      *reinterpret_cast<uint64_t*>(xf + 4 * ch) = packed;
     }
   }
 }
 
-template <int KQ, int RPW, int CPB>
-__global__ __launch_bounds__(kBlock, 2) void k_lmhead_fused(Dims d, LmHeadParams p) {
+
+template <int CPB>
+__global__ __launch_bounds__(kBlock) void k_final_norm(Dims d, LmHeadParams p) {
+  __shared__ float sred[kBlock / kWave];
+  __shared__ float4 ystage[kMaxTopK * kBlock * CPB];
+  produce_final_row<kBlock, CPB>(d, p, blockIdx.x, sred, ystage);
+}
+
+// --------------------------------------------------- up to 16 tokens ----
+// Persistent (two 256-thread workgroups per CU) over units of RPW row tiles.
+// The four wavefronts split the reduction (KQ = H/128 k-steps each), hold
+// their activation fragments in registers for the whole kernel, and load the
+// next unit's weight tiles (RPW * KQ fragments, coalesced 1 KiB each) while
+// the current unit's partial sums meet in LDS.
+template <int KQ, int RPW>
+__global__ __launch_bounds__(kBlock, 2) void k_lmhead_stream(Dims d, LmHeadParams p) {
   __shared__ float red[4][RPW][kWave][4];
   __shared__ uint64_t kbest[RPW * 16][kTile];
   __shared__ uint64_t run_best[kTile];
-  __shared__ float sred[4];
-  __shared__ int is_last;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int KT = d.H / kKStep, kt0 = wave * KQ;
   const int n_units = d.Vpad / (kTile * RPW);   // units of RPW row tiles
@@ -421,54 +416,19 @@ __global__ __launch_bounds__(kBlock, 2) void k_lmhead_fused(Dims d, LmHeadParams
     }
   };
 
-  // 1. the first unit's weight tiles, in flight before anything else
-  bf16x8_t a0[RPW][KQ], a1[RPW][KQ];
-  int u = blockIdx.x;
-  if (u < n_units) load_unit(u, a0);
   if (threadIdx.x < kTile) run_best[threadIdx.x] = 0ull;
-  // 2. workgroups 0..T-1 produce the normalised rows
-  if (static_cast<int>(blockIdx.x) < p.T) {
-    produce_final_row<CPB>(d, p, blockIdx.x, sred);
-    __builtin_amdgcn_s_waitcnt(0);  // this thread's row stores are done
-    __syncthreads();
-    if (threadIdx.x == 0)
-      __hip_atomic_fetch_add(p.norm_count, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
-  // 3. wait for all T rows (bounded)
-  if (threadIdx.x == 0) {
-    unsigned spins = 0;
-    while (static_cast<int>(__hip_atomic_load(p.norm_count, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) -
-                            p.norm_target) < 0) {
-      if (++spins > kSpinLimit) {
-        *p.err = 1;
-        break;
-      }
-      __builtin_amdgcn_s_sleep(2);
-    }
-  }
-  __syncthreads();
-  // 4. activation fragments, read once and kept in registers; read coherently
-  //    (the rows were just written on other CUs; this CU's L2 may hold an
-  //    older copy of those lines)
-  const int tok = lane % kTile;
+  // activation fragments (token lane % 16; rows past T repeat row T - 1, their
+  // results are never used), read once and kept in registers, issued first
+  const int tok = min(lane % kTile, p.T - 1);
   bf16x8_t b[KQ];
-  const bf16_t* xr = reinterpret_cast<const bf16_t*>(p.xf_out) + static_cast<int64_t>(tok) * d.H + kt0 * kKStep +
+  const bf16_t* xr = reinterpret_cast<const bf16_t*>(p.xf) + static_cast<int64_t>(tok) * d.H + kt0 * kKStep +
                      (lane / kTile) * 8;
 #pragma unroll
-  for (int i = 0; i < KQ; ++i) {
-    if (tok < p.T) {
-      uint4 w;
-      const uint64_t lo = load_u64_agent(xr + i * kKStep), hi = load_u64_agent(xr + i * kKStep + 4);
-      w.x = static_cast<uint32_t>(lo);
-      w.y = static_cast<uint32_t>(lo >> 32);
-      w.z = static_cast<uint32_t>(hi);
-      w.w = static_cast<uint32_t>(hi >> 32);
-      b[i] = __builtin_bit_cast(bf16x8_t, w);
-    } else {
-      b[i] = zero_frag();
-    }
-  }
-  // 5. stream this workgroup's units, the next unit's tiles one unit ahead
+  for (int i = 0; i < KQ; ++i) b[i] = load_frag(xr + i * kKStep);
+  bf16x8_t a0[RPW][KQ], a1[RPW][KQ];
+  int u = blockIdx.x;  // < n_units (grid <= units)
+  load_unit(u, a0);
+
   auto do_unit = [&](int uu, const bf16x8_t (&a)[RPW][KQ]) {
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
@@ -479,6 +439,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_lmhead_fused(Dims d, LmHeadParams
       for (int i = 0; i < 4; ++i) red[wave][r][lane][i] = c[i];
     }
     __syncthreads();
+    // logits of (row, token): the four reduction quarters summed in a fixed order
     for (int q = threadIdx.x; q < RPW * kWave * 4; q += kBlock) {
       const int r = q / (kWave * 4), L = (q / 4) % kWave, i = q % 4;
       const float v = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
@@ -493,77 +454,238 @@ __global__ __launch_bounds__(kBlock, 2) void k_lmhead_fused(Dims d, LmHeadParams
       run_best[threadIdx.x] = best;
     }
   };
-  while (u < n_units) {
-    const int un = u + gridDim.x;
-    if (un < n_units) load_unit(un, a1);
+  // steady state: both units of a pair exist, every load is unconditional
+  // (the compiler's wait before a unit's MFMAs then leaves the next unit's
+  // loads in flight)
+  const int g = gridDim.x;
+  for (; u + 2 * g < n_units; u += 2 * g) {
+    load_unit(u + g, a1);
     do_unit(u, a0);
-    u = un;
-    if (u >= n_units) break;
-    const int un2 = u + gridDim.x;
-    if (un2 < n_units) load_unit(un2, a0);
-    do_unit(u, a1);
-    u = un2;
+    load_unit(u + 2 * g, a0);
+    do_unit(u + g, a1);
+  }
+  if (u + g < n_units) {
+    load_unit(u + g, a1);
+    do_unit(u, a0);
+    do_unit(u + g, a1);
+  } else {
+    do_unit(u, a0);
   }
   __syncthreads();
   if (threadIdx.x < kTile && static_cast<int>(threadIdx.x) < p.T && run_best[threadIdx.x] != 0ull)
+    atomicMax(p.keys + static_cast<int64_t>(blockIdx.x % kKeySlots) * p.key_stride + threadIdx.x,
+              static_cast<unsigned long long>(run_best[threadIdx.x]));
+}
+
+// ------------------------------------------------- 17..128 tokens ----
+// One 512-thread workgroup per CU, persistent over units of 8R row tiles
+// (R = 4 up to 4 token tiles, 2 for 8, which keeps the accumulators plus the
+// load rings within the 256 registers of two wavefronts per SIMD); wavefront
+// w owns the unit's row tiles Rw..Rw+R-1 over the whole reduction, so its
+// accumulators (R row tiles x NT token tiles) never leave registers.  Per
+// 32-wide k-step g:
+//  * weight fragments go straight to registers from a ring of P steps in
+//    flight per wavefront (PR KiB: 16 KiB with P = 4, R = 4 and P = 8,
+//    R = 2), which keeps HBM busy through the barriers;
+//  * the activation fragments of all NT token tiles (NT KiB, shared by the 8
+//    wavefronts) come from a double-buffered LDS stage; wavefront w loads
+//    token tile w % NT of step g into a ring of P registers P steps ahead and
+//    writes it to the LDS stage during step g - 1.  One barrier per step.
+// All loads are ordinary register loads, so the compiler's own wait counts
+// are exact.
+constexpr int kWideThreads = 512;
+constexpr int kWideWaves = kWideThreads / kWave;
+constexpr int kWideStageBytes = kWideWaves * 1024;  // one fragment slot per wavefront
+
+template <int NT, int R, int P>
+__global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadParams p) {
+  static_assert(NT >= 1 && NT <= kWideWaves, "one activation fragment per wavefront and step");
+  static_assert(P == 4 || P == 8, "weight ring of one or two groups of four steps");
+  constexpr int kUnitTiles = kWideWaves * R;
+  __shared__ __align__(16) unsigned char bring[2 * kWideStageBytes];
+  __shared__ uint64_t wbest[kWideWaves][NT * kTile];
+  __shared__ uint64_t run_best[NT * kTile];
+  // the wavefront index as a scalar: addresses and branches that depend only
+  // on it stay scalar
+  const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int H = d.H, KT = H / kKStep;
+  const int n_tiles = d.Vpad / kTile;
+  const int n_units = (n_tiles + kUnitTiles - 1) / kUnitTiles;
+  const int total = ((n_units - 1 - static_cast<int>(blockIdx.x)) / static_cast<int>(gridDim.x) + 1) * KT;
+  const bf16_t* lm = reinterpret_cast<const bf16_t*>(p.lm);
+
+  // Weight fragments of this workgroup's steps in order (step g: its
+  // (g / KT)-th unit, k-step g % KT), through a scalar cursor.  Row tiles past
+  // the matrix are clamped to its last tile (results discarded).
+  int a_u = blockIdx.x, a_kt = 0;
+  auto load_a_next = [&](bf16x8_t (&a)[R]) {
+#pragma unroll
+    for (int r = 0; r < R; ++r) {
+      const int vt = min(a_u * kUnitTiles + wave * R + r, n_tiles - 1);
+      a[r] = load_frag(lm + (static_cast<int64_t>(vt) * KT + a_kt) * kFragElems + lane * 8);
+    }
+    if (++a_kt == KT) {
+      a_kt = 0;
+      a_u += gridDim.x;
+    }
+  };
+  // activation fragment (token tile w % NT) of step g for wavefront w, into
+  // slot w of a stage (slots >= NT are never read: every wavefront runs the
+  // same code, which keeps the loads free of branches and the compiler's wait
+  // counts exact).  Rows past T repeat row T - 1 (results discarded).
+  const int btok = min((wave % NT) * kTile + lane % kTile, p.T - 1);
+  const bf16_t* bsrc = reinterpret_cast<const bf16_t*>(p.xf) + static_cast<int64_t>(btok) * H + (lane / kTile) * 8;
+  int b_kt = 0;  // k-step of the next activation fragment to load
+  auto load_b_next = [&]() -> bf16x8_t {
+    const bf16x8_t v = load_frag(bsrc + b_kt * kKStep);
+    if (++b_kt == KT) b_kt = 0;
+    return v;
+  };
+  auto put_b = [&](int g, const bf16x8_t& v) {
+    *reinterpret_cast<bf16x8_t*>(bring + (g & 1) * kWideStageBytes + wave * 1024 + lane * 16) = v;
+  };
+
+  f32x4_t acc[R][NT];
+#pragma unroll
+  for (int r = 0; r < R; ++r)
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) acc[r][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // End of a unit: per-token best (logit, lowest row) over the unit's rows.
+  // Branch-free: rows past V get key 0, and after the two butterflies the
+  // four lanes l, l+16, l+32, l+48 hold the same value and all store it.
+  int cur_u = blockIdx.x;  // unit being accumulated
+  auto unit_end = [&]() {
+    const int u = cur_u;
+    cur_u += gridDim.x;
+#pragma unroll
+    for (int nt = 0; nt < NT; ++nt) {
+      uint64_t best = 0ull;
+#pragma unroll
+      for (int r = 0; r < R; ++r)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int row = (u * kUnitTiles + wave * R + r) * kTile + 4 * (lane / kTile) + i;
+          const uint64_t valid = 0ull - static_cast<uint64_t>(row < d.V);
+          const uint64_t key = argmax_key(acc[r][nt][i], static_cast<uint32_t>(row)) & valid;
+          best = key > best ? key : best;
+          acc[r][nt][i] = 0.f;
+        }
+      uint64_t o = __shfl_xor(best, 16, kWave);
+      best = o > best ? o : best;
+      o = __shfl_xor(best, 32, kWave);
+      best = o > best ? o : best;
+      wbest[wave][nt * kTile + lane % kTile] = best;
+    }
+    lds_barrier();
+    if (wave < (NT * kTile + kWave - 1) / kWave) {
+      const int t = wave * kWave + lane;
+      uint64_t b = run_best[t % (NT * kTile)];
+#pragma unroll
+      for (int w = 0; w < kWideWaves; ++w) {
+        const uint64_t v = wbest[w][t % (NT * kTile)];
+        b = v > b ? v : b;
+      }
+      if (t < NT * kTile) run_best[t] = b;
+    }
+  };
+
+  if (threadIdx.x < NT * kTile) run_best[threadIdx.x] = 0ull;
+  // weight ring primed (total >= KT >= 4)
+  bf16x8_t a[P][R];
+#pragma unroll
+  for (int j = 0; j < P; ++j)
+    if (j < total) load_a_next(a[j]);
+  // activation ring: slot j holds the fragment of a step g = j mod P
+  //    (loaded for every g < total + P: rows repeat, so reads stay in bounds)
+  bf16x8_t pb[P];
+#pragma unroll
+  for (int j = 0; j < P; ++j) pb[j] = load_b_next();
+  put_b(0, pb[0]);
+  pb[0] = load_b_next();
+  lds_barrier();
+
+  // Step G on ring slot J = G mod P: stage G is in LDS.  Write step G+1's
+  // fragment (slot J+1) to the other stage and refill that slot with step
+  // G+1+P; MFMAs on stage G with weight slot J, refilled with step G+P;
+  // barrier.  The two rings have the same depth: loads complete in order, so
+  // waiting for step G+1's fragment (issued P-1 steps earlier) leaves the
+  // weight loads of the P-1 steps after it in flight.  In a steady group (ST
+  // = true, a literal) the step and every refill exist; otherwise each is
+  // tested at run time.  Activation loads past the last step read valid rows
+  // and are never used.
+#define MOE_WIDE_STEP(G, J, ST)                                                                    \
+  if ((ST) || (G) < total) {                                                                       \
+    if ((ST) || (G) + 1 < total) put_b((G) + 1, pb[((J) + 1) % P]);                                \
+    pb[((J) + 1) % P] = load_b_next();                                                             \
+    const unsigned char* st_ = bring + ((G) & 1) * kWideStageBytes + lane * 16;                    \
+    _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                            \
+      const bf16x8_t b_ = *reinterpret_cast<const bf16x8_t*>(st_ + nt * 1024);                     \
+      _Pragma("unroll") for (int r = 0; r < R; ++r)                                                \
+        acc[r][nt] = mfma16(a[J][r], b_, acc[r][nt]);                                              \
+    }                                                                                              \
+    if ((ST) || (G) + P < total) load_a_next(a[J]);                                                \
+    lds_barrier();                                                                                 \
+  }
+  // Four steps on ring slots J..J+3 (KT is a multiple of 4, so a unit can
+  // only end after a fourth step).
+#define MOE_WIDE_QUAD(G, J, ST)                                                                    \
+  {                                                                                                \
+    MOE_WIDE_STEP(G, J, ST)                                                                        \
+    MOE_WIDE_STEP((G) + 1, (J) + 1, ST)                                                            \
+    MOE_WIDE_STEP((G) + 2, (J) + 2, ST)                                                            \
+    MOE_WIDE_STEP((G) + 3, (J) + 3, ST)                                                            \
+    if (((ST) || (G) + 4 <= total) && ((G) + 4) % KT == 0) unit_end();                             \
+  }
+  // A group: P steps, one pass over the ring slots.
+#define MOE_WIDE_GROUP(G, ST)                                                                      \
+  {                                                                                                \
+    MOE_WIDE_QUAD(G, 0, ST)                                                                        \
+    if (P == 8) MOE_WIDE_QUAD((G) + 4, 4 % P, ST)                                                  \
+  }
+  // The first steady group is peeled so that the loop is only entered in the
+  // state it leaves (the compiler's wait counts at the loop head hold for
+  // every path into it).
+  int g = 0;
+  if (total >= 2 * P) {
+    MOE_WIDE_GROUP(0, true)
+    for (g = P; g + 2 * P <= total; g += P) MOE_WIDE_GROUP(g, true)
+  }
+  for (; g < total; g += P) MOE_WIDE_GROUP(g, false)
+#undef MOE_WIDE_GROUP
+#undef MOE_WIDE_QUAD
+#undef MOE_WIDE_STEP
+
+  if (static_cast<int>(threadIdx.x) < NT * kTile && static_cast<int>(threadIdx.x) < p.T &&
+      run_best[threadIdx.x] != 0ull)
     __hip_atomic_fetch_max(p.keys + static_cast<int64_t>(blockIdx.x % kKeySlots) * p.key_stride + threadIdx.x,
                            static_cast<unsigned long long>(run_best[threadIdx.x]), __ATOMIC_RELAXED,
                            __HIP_MEMORY_SCOPE_AGENT);
-  // 6. the last workgroup to finish runs the acceptance
-  __builtin_amdgcn_s_waitcnt(0);  // this thread's key atomic is performed
-  __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned old = __hip_atomic_fetch_add(p.done, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (old - p.done_base) == gridDim.x - 1;
-  }
-  __syncthreads();
-  if (!is_last) return;
-  const int K1 = p.K + 1;
-  auto pick_of = [&](int t) {
-    uint64_t best = 0ull;
-    for (int q = 0; q < kKeySlots; ++q) {
-      const uint64_t key = load_u64_agent(p.keys + static_cast<int64_t>(q) * p.key_stride + t);
-      best = key > best ? key : best;
-    }
-    return static_cast<int>(argmax_key_index(best));
-  };
-  if (p.tstar)
-    for (int t = threadIdx.x; t < p.T; t += kBlock) p.tstar[t] = pick_of(t);
-  for (int bq = threadIdx.x; bq < p.B; bq += kBlock) {
-    int pick[8];
-    for (int j = 0; j < K1; ++j) pick[j] = pick_of(bq * K1 + j);
-    int acc = 0;
-    while (acc < p.K && p.drafts[bq * p.K + acc] == pick[acc]) ++acc;
-    for (int j = 0; j < K1; ++j) p.committed[bq * K1 + j] = j <= acc ? pick[j] : -1;
-    p.counts[bq] = acc + 1;
-  }
-  __syncthreads();
-  for (int i = threadIdx.x; i < kKeySlots * p.T; i += kBlock)
-    store_u64_agent(p.keys + static_cast<int64_t>(i / p.T) * p.key_stride + i % p.T, 0ull);
+}
+
+template <int NT, int R, int P>
+hipError_t lm_wide_nt(const Dims& d, const LmHeadParams& p, hipStream_t s) {
+  // persistent: one workgroup per CU
+  constexpr int kUnitTiles = kWideWaves * R;
+  const unsigned units = (d.Vpad / kTile + kUnitTiles - 1) / kUnitTiles;
+  const unsigned grid = units < static_cast<unsigned>(d.n_cu) ? units : static_cast<unsigned>(d.n_cu);
+  hipLaunchKernelGGL((k_lmhead_wide<NT, R, P>), dim3(grid), dim3(kWideThreads), 0, s, d, p);
+  return hipGetLastError();
 }
 
 template <int KQ>
-hipError_t lm_fused_kq(const Dims& d, const LmHeadParams& p, hipStream_t s, unsigned int* blocks) {
+hipError_t lm_stream_kq(const Dims& d, const LmHeadParams& p, hipStream_t s) {
   constexpr int RPW = 2;
-  constexpr int CPB = (KQ * 32 + kBlock - 1) / kBlock;  // ceil((H/4) / 256)
   // persistent: two workgroups per CU stream the vocabulary units in turn
   const unsigned units = d.Vpad / (kTile * RPW);
-  const unsigned grid = units < 512u ? units : 512u;
-  *blocks = grid;
-  hipLaunchKernelGGL((k_lmhead_fused<KQ, RPW, CPB>), dim3(grid), dim3(kBlock), 0, s, d, p);
+  const unsigned cap = 2u * static_cast<unsigned>(d.n_cu);
+  const unsigned grid = units < cap ? units : cap;
+  hipLaunchKernelGGL((k_lmhead_stream<KQ, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p);
   return hipGetLastError();
 }
 
-template <int KQ>
-hipError_t lm_ksplit(const Dims& d, const LmHeadParams& p, hipStream_t s) {
-  constexpr int RPW = 2;
-  hipLaunchKernelGGL((k_lmhead_ksplit<KQ, RPW>), dim3(d.Vpad / (kTile * RPW)), dim3(kBlock), 0, s, d, p);
-  return hipGetLastError();
-}
-
-template <int NT>
+template <int NT, int R, int KC>
 hipError_t lm_nt(const Dims& d, const LmHeadParams& p, hipStream_t s) {
-  constexpr int R = 4, KC = 2;
   const int groups = (p.T + NT * kTile - 1) / (NT * kTile);
   const dim3 grid(d.Vpad / (64 * R), groups);
   const size_t smem = 2ull * NT * KC * kWave * 16;
@@ -576,21 +698,22 @@ hipError_t lm_nt(const Dims& d, const LmHeadParams& p, hipStream_t s) {
 // Rows of the tiled LM head must be padded to a multiple of this.
 int lmhead_row_multiple() { return 256; }
 
-hipError_t launch_lmhead_fused(const Dims& d, const LmHeadParams& p, hipStream_t s, unsigned int* blocks) {
-  if (!d.bf16 || p.T > kTile || p.T < 1) return hipErrorInvalidValue;
-  switch (d.H / 128) {
-    case 1: return lm_fused_kq<1>(d, p, s, blocks);   case 2: return lm_fused_kq<2>(d, p, s, blocks);
-    case 3: return lm_fused_kq<3>(d, p, s, blocks);   case 4: return lm_fused_kq<4>(d, p, s, blocks);
-    case 5: return lm_fused_kq<5>(d, p, s, blocks);   case 6: return lm_fused_kq<6>(d, p, s, blocks);
-    case 7: return lm_fused_kq<7>(d, p, s, blocks);   case 8: return lm_fused_kq<8>(d, p, s, blocks);
-    case 9: return lm_fused_kq<9>(d, p, s, blocks);   case 10: return lm_fused_kq<10>(d, p, s, blocks);
-    case 11: return lm_fused_kq<11>(d, p, s, blocks); case 12: return lm_fused_kq<12>(d, p, s, blocks);
-    default: return hipErrorInvalidValue;
+hipError_t launch_final_norm(const Dims& d, const LmHeadParams& p, hipStream_t s) {
+  if (!d.bf16 || p.T < 1) return hipErrorInvalidValue;
+  const int chunks = d.H / 4;  // 4-element chunks per row
+  if (chunks <= kBlock) {
+    hipLaunchKernelGGL((k_final_norm<1>), dim3(p.T), dim3(kBlock), 0, s, d, p);
+  } else if (chunks <= 2 * kBlock) {
+    hipLaunchKernelGGL((k_final_norm<2>), dim3(p.T), dim3(kBlock), 0, s, d, p);
+  } else {
+    return hipErrorInvalidValue;
   }
+  return hipGetLastError();
 }
 
 hipError_t launch_accept(const LmHeadParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_accept, dim3(1), dim3(kBlock), 0, s, p);
+  if (p.K + 1 > 8) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_accept, dim3((p.B + kAcceptSeqs - 1) / kAcceptSeqs), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 
@@ -599,22 +722,23 @@ hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s) {
     hipLaunchKernelGGL(k_lmhead_f32, dim3((d.V + kBlock - 1) / kBlock), dim3(kBlock), 0, s, d, p);
     return hipGetLastError();
   }
-  if ((d.H / kKStep) % 2 != 0) return hipErrorInvalidValue;
-  const int nt = (p.T + kTile - 1) / kTile;
-  if (nt <= 1) {
+  if (d.H % 128 != 0) return hipErrorInvalidValue;
+  if (p.T <= kTile) {
     switch (d.H / 128) {
-      case 1: return lm_ksplit<1>(d, p, s);   case 2: return lm_ksplit<2>(d, p, s);
-      case 3: return lm_ksplit<3>(d, p, s);   case 4: return lm_ksplit<4>(d, p, s);
-      case 5: return lm_ksplit<5>(d, p, s);   case 6: return lm_ksplit<6>(d, p, s);
-      case 7: return lm_ksplit<7>(d, p, s);   case 8: return lm_ksplit<8>(d, p, s);
-      case 9: return lm_ksplit<9>(d, p, s);   case 10: return lm_ksplit<10>(d, p, s);
-      case 11: return lm_ksplit<11>(d, p, s); case 12: return lm_ksplit<12>(d, p, s);
+      case 1: return lm_stream_kq<1>(d, p, s);   case 2: return lm_stream_kq<2>(d, p, s);
+      case 3: return lm_stream_kq<3>(d, p, s);   case 4: return lm_stream_kq<4>(d, p, s);
+      case 5: return lm_stream_kq<5>(d, p, s);   case 6: return lm_stream_kq<6>(d, p, s);
+      case 7: return lm_stream_kq<7>(d, p, s);   case 8: return lm_stream_kq<8>(d, p, s);
+      case 9: return lm_stream_kq<9>(d, p, s);   case 10: return lm_stream_kq<10>(d, p, s);
+      case 11: return lm_stream_kq<11>(d, p, s); case 12: return lm_stream_kq<12>(d, p, s);
       default: return hipErrorInvalidValue;
     }
   }
-  if (nt <= 2) return lm_nt<2>(d, p, s);
-  if (nt <= 4) return lm_nt<4>(d, p, s);
-  return lm_nt<8>(d, p, s);
+  const int nt = (p.T + kTile - 1) / kTile;
+  if (nt <= 2) return lm_wide_nt<2, 4, 4>(d, p, s);
+  if (nt <= 4) return lm_wide_nt<4, 4, 4>(d, p, s);
+  if (nt <= 8) return lm_wide_nt<8, 2, 8>(d, p, s);
+  return lm_nt<8, 4, 2>(d, p, s);
 }
 
 }  // namespace moe

@@ -62,12 +62,6 @@ __global__ __launch_bounds__(64) void k_tile_list(Dims d, GemmTileParams p) {
   if (lane == kWave - 1) *p.n_tiles = n_shared + incl;
 }
 
-typedef __attribute__((address_space(3))) void* lds_ptr_t;
-
-// s_waitcnt immediates (gfx9 encoding: vmcnt bits [3:0] and [15:14], expcnt
-// [6:4], lgkmcnt [11:8]); only the vector-memory count is waited on.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-
 template <bool UP>
 __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
   // LDS ring of kStages stages; a stage holds one 32-wide k-step: 16 weight

@@ -14,6 +14,7 @@ struct Dims {
   int H, E, k, S, I, V, Vpad, L;
   float eps;
   int bf16;  // 1: bfloat16 storage and MFMA kernels; 0: float32 storage
+  int n_cu;  // compute units of the device (sizes persistent grids)
 };
 
 // Stable counting sort of the T*k (token, slot) pairs by expert.
@@ -115,14 +116,14 @@ struct LmHeadParams {
   const void* xf;            // [T][H] storage (final-norm activations)
   const void* lm;            // bf16 tiled [Vpad/16][H/32][512]; f32 [V][H]
   int T;
-  unsigned long long* keys;  // [kKeySlots][key_stride], cleared beforehand
+  unsigned long long* keys;  // [kKeySlots][key_stride], zero between steps
   int key_stride;
   const int* drafts;         // [B][K]
   int B, K;
   int* committed;            // [B][K+1]
   int* counts;               // [B]
   int* tstar;                // [T], optional
-  // Fused final combine + RMSNorm and acceptance (launch_lmhead_fused):
+  // Final combine + RMSNorm (launch_final_norm), writing xf_out:
   const void* x_in;          // [T][H] storage: residual entering the last block
   const float* y;            // last block's expert outputs (see NormRouterParams)
   const int* prev_idx;       // [T][k]
@@ -130,18 +131,12 @@ struct LmHeadParams {
   const void* gamma;         // [H] final RMSNorm gain
   void* x_out;               // [T][H] storage: final residual, optional
   float* m_out;              // [T][H] last block's MoE output, optional
-  void* xf_out;              // [T][H] bf16 scratch for the normalised rows
-  unsigned int* norm_count;  // rows produced (monotonic; wait until norm_target)
-  unsigned int norm_target;
-  unsigned int* done;        // workgroups finished (monotonic from done_base)
-  unsigned int done_base;
-  int* err;                  // set to 1 if a bounded wait timed out
+  void* xf_out;              // [T][H] bf16 normalised rows
 };
+// bf16: one workgroup per row finishes the last block and normalises it.
+hipError_t launch_final_norm(const Dims& d, const LmHeadParams& p, hipStream_t s);
 hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s);  // keys only
-hipError_t launch_accept(const LmHeadParams& p, hipStream_t s);  // picks + acceptance
-// Up to 16 bf16 tokens: final combine + norm, LM head, picks and acceptance in
-// one launch.  Returns the number of workgroups launched in *blocks.
-hipError_t launch_lmhead_fused(const Dims& d, const LmHeadParams& p, hipStream_t s, unsigned int* blocks);
+hipError_t launch_accept(const LmHeadParams& p, hipStream_t s);  // picks + acceptance, keys cleared
 
 // Weight repacking.  Tiled layout of an [R][C] bf16 matrix (R padded to Rpad
 // with zero rows): tile (rt, kt) of 16 rows x 32 columns is 512 contiguous

@@ -47,7 +47,7 @@ def test_tiny_fp32_step():
     assert out["counts"].tolist() == [2, 2]
 
 
-@pytest.mark.parametrize("B,K,L", [(5, 3, 2), (1, 3, 1), (3, 2, 1), (7, 0, 1), (9, 7, 3)])
+@pytest.mark.parametrize("B,K,L", [(5, 3, 2), (1, 3, 1), (3, 2, 1), (7, 0, 1), (9, 7, 3), (12, 3, 1), (40, 3, 1)])
 def test_small_bf16_step(B, K, L):
     w = workloads.small_bf16(B=B, K=K, L=L, seed_id=20 + B + 10 * K + 100 * L)
     case = workloads.build_case(w)
