@@ -52,7 +52,6 @@ struct moe_verify_ctx {
   char* act = nullptr;      // [tw*(k+S)][I] storage
   float* y = nullptr;       // [tw*(k+S)][H]
   unsigned long long* keys = nullptr;  // [kKeySlots][tw]
-  unsigned int* done = nullptr;        // [1] sort-tail completion, [2] rows produced, [3] head workgroups done
 
   int4* tiles = nullptr;               // grouped-GEMM tile table
   int* n_tiles = nullptr;
@@ -285,11 +284,9 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   MOE_HIP(hipMemsetAsync(c->act + rows * I * es, 0, I * es, s));
   if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->y))) return r;
   if ((r = ctx_alloc_t(c, moe::kKeySlots * tw * sizeof(unsigned long long), &c->keys))) return r;
-  if ((r = ctx_alloc_t(c, 16, &c->done))) return r;
   if ((r = ctx_alloc_t(c, static_cast<size_t>(moe::gemm_max_tiles(d, static_cast<int>(tw))) * sizeof(int4), &c->tiles)))
     return r;
   if ((r = ctx_alloc_t(c, 16, &c->n_tiles))) return r;
-  MOE_HIP(hipMemsetAsync(c->done, 0, 16, s));
 
   // arg-max keys are zero between steps (the acceptance clears them after use)
   MOE_HIP(hipMemsetAsync(c->keys, 0, moe::kKeySlots * tw * sizeof(unsigned long long), s));
@@ -340,10 +337,10 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     pp.perm = aux && aux->perm ? aux->perm + li * T * k : c->perm;
     pp.active = c->active;
     pp.n_active = c->n_active;
-    const bool fused_sort = pp.P <= moe::norm_router_sort_limit();
+    const bool fused_sort = T <= moe::norm_router_sort_limit();
     if (fused_sort) {
-      // the last norm/router workgroup sorts the pairs
-      nr.sort = moe::SortParams{idx, pp.cnt, pp.off, pp.perm, pp.active, pp.n_active, c->done + 1};
+      // the (single) norm/router workgroup sorts the pairs
+      nr.sort = moe::SortParams{idx, pp.cnt, pp.off, pp.perm, pp.active, pp.n_active, 1};
     }
     MOE_HIP(moe::launch_norm_router(d, nr, s));
     if (!fused_sort) MOE_HIP(moe::launch_permute(d, pp, s));
@@ -455,9 +452,6 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
     nr.m_out = aux && aux->moe_out ? aux->moe_out + li * T * H : nullptr;
     nr.gamma = c->final_gamma;
     nr.xhat = c->xhat;
-    nr.keys = c->keys;
-    nr.key_slots = moe::kKeySlots;
-    nr.key_stride = static_cast<int>(c->tw);
     nr.T = T;
     nr.combine = 1;
     nr.norm = 1;

@@ -11,13 +11,15 @@
 //   router fragments are loaded at kernel start), the rows' xh sit in LDS in
 //   operand layout, the four quarters are summed in a fixed order.  float32
 //   storage uses plain FMAs.
-// Phase 3 (one wavefront per row, one lane per expert): k rounds of a
-//   wavefront arg-max over (logit, lower expert first), then the softmax over
-//   the k selected logits.
-// Tail (small steps): the last workgroup to finish runs the stable counting
-//   sort of all T*k (token, slot) pairs by expert in LDS (ballot ranks within a
+// Phase 3 (one wavefront per row, one lane per expert): each expert's rank by
+//   (logit desc, lower expert first) from all-pairs comparisons of broadcast
+//   keys; the k best, in rank order, get the softmax over the selected logits.
+// Tail (steps of at most 16 tokens, one workgroup): the stable counting sort
+//   of all T*k (token, slot) pairs by expert in LDS (ballot ranks within a
 //   wavefront, per-wavefront counts, prefix over wavefronts), so the expert
 //   kernels that follow know each expert's tokens without another launch.
+//   Larger steps sort in a separate launch: a cross-workgroup hand-off inside
+//   the kernel (release fence, counter, acquire fence) costs more here.
 // The mixture of 64 routed experts with top-6 routing is the decoder of the
 // page "Jina AI releases lightweight OCR model with built-in speculative
 // decoding", section "Lean architecture with a compressed encoder"; the norm,
@@ -122,7 +124,6 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   extern __shared__ __align__(16) unsigned char smem[];
   float* zp = reinterpret_cast<float*>(smem);
   unsigned char* xs = smem + 4 * kRows * 64 * sizeof(float);
-  __shared__ int is_last;
   __shared__ int sel[kRows * kMaxTopK];  // this workgroup's selections (single-workgroup sort)
 
   const int H = d.H, k = d.k, T = p.T;
@@ -134,16 +135,36 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
 
   const int et = wave % 4, kq = wave / 4;
 
-  // ------------------------------------------------------------ phase 1
+  // router fragments of this wavefront, requested after phase 1 (to keep
+  // phase 1 within 128 registers)
+  bf16x8_t ra[KQ];
   const int n = wave;
   const int t = t0 + n;
-  if (n < kRows && t < T) {
+  const bool has_row = n < kRows && t < T;
+  auto load_router = [&]() {
+    if constexpr (sizeof(ST) == 2) {
+      if (p.route && et * 16 < d.E) {
+        const bf16_t* wr = reinterpret_cast<const bf16_t*>(p.router) +
+                           (static_cast<int64_t>(et) * (H / kKStep) + kq * KQ) * kFragElems + lane * 8;
+#pragma unroll
+        for (int i = 0; i < KQ; ++i) ra[i] = load_frag(wr + i * kFragElems);
+      }
+    }
+  };
+
+  // ------------------------------------------------------------ phase 1
+  if (has_row) {
     float x[CPL][4];
+    Vec4<ST> gg[CPL];  // the gain, loaded with the row, converted when used
     const ST* xin = reinterpret_cast<const ST*>(p.x_in) + static_cast<int64_t>(t) * H;
+    const ST* gam = reinterpret_cast<const ST*>(p.gamma);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int ch = lane + c * kWave;
-      if (ch < nchunks) load4<ST>(xin + 4 * ch, x[c]);
+      if (ch < nchunks) {
+        load4<ST>(xin + 4 * ch, x[c]);
+        if (p.norm) gg[c] = *reinterpret_cast<const Vec4<ST>*>(gam + 4 * ch);
+      }
     }
     if (p.combine) {
       // rows to add, in order: shared experts, then routed by ascending expert
@@ -236,16 +257,14 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
       }
       ss = wave_sum(ss);
       const float rms = sqrtf(ss / static_cast<float>(H) + d.eps);
-      const ST* gam = reinterpret_cast<const ST*>(p.gamma);
       ST* xh = reinterpret_cast<ST*>(p.xhat) + static_cast<int64_t>(t) * H;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int ch = lane + c * kWave;
         if (ch < nchunks) {
-          float gg[4], v[4];
-          load4<ST>(gam + 4 * ch, gg);
+          float v[4];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = Storage<ST>::round(__fmul_rn(x[c][i] / rms, gg[i]));
+          for (int i = 0; i < 4; ++i) v[i] = Storage<ST>::round(__fmul_rn(x[c][i] / rms, Storage<ST>::load(gg[c].v, i)));
           store4<ST>(xh + 4 * ch, v);
           if (p.route) {
             const int h = 4 * ch;
@@ -262,21 +281,9 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
         }
       }
     }
-    if (p.keys && lane < p.key_slots) p.keys[static_cast<int64_t>(lane) * p.key_stride + t] = 0ull;
   }
   if (!p.route) return;
-
-  // router fragments of this wavefront (requested before the barrier so the
-  // loads overlap it; not earlier, to keep phase 1 within 128 registers)
-  bf16x8_t ra[KQ];
-  if constexpr (sizeof(ST) == 2) {
-    if (et * 16 < d.E) {
-      const bf16_t* wr = reinterpret_cast<const bf16_t*>(p.router) +
-                         (static_cast<int64_t>(et) * (H / kKStep) + kq * KQ) * kFragElems + lane * 8;
-#pragma unroll
-      for (int i = 0; i < KQ; ++i) ra[i] = load_frag(wr + i * kFragElems);
-    }
-  }
+  load_router();
   const int nrows = min(kRows, T - t0);
   if constexpr (sizeof(ST) == 2) {
     // rows of this workgroup past T: zero operand lanes so MFMA reads defined values
@@ -326,55 +333,45 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
       z = zp[n * 64 + lane];
       for (int q = 1; q < nq; ++q) z = __fadd_rn(z, zp[(q * kRows + n) * 64 + lane]);
     }
-    uint64_t key = lane < d.E ? argmax_key(z, static_cast<uint32_t>(lane)) : 0ull;
-    int sel_e[kMaxTopK];
-    float sel_z[kMaxTopK];
-    for (int j = 0; j < k; ++j) {
-      const uint64_t best = wave_max_u64(key);
-      const int e = static_cast<int>(argmax_key_index(best));
-      sel_e[j] = e;
-      sel_z[j] = __shfl(z, e, kWave);
-      if (lane == e) key = 0ull;
+    // rank of each expert (lane) among the row's logits, by (logit desc,
+    // expert asc): the number of experts with a larger key.  Every key is
+    // broadcast from its lane (scalar reads, no dependent shuffle chain).
+    const uint64_t key = lane < d.E ? argmax_key(z, static_cast<uint32_t>(lane)) : 0ull;
+    const uint32_t klo = static_cast<uint32_t>(key), khi = static_cast<uint32_t>(key >> 32);
+    int rank = 0;
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) {
+      // (readlane returns int: go through uint32_t, never sign-extend)
+      const uint64_t ke = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(khi, e))) << 32) |
+                          static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(klo, e)));
+      rank += ke > key ? 1 : 0;
     }
-    float ex[kMaxTopK];
+    const bool chosen = lane < d.E && rank < k;
+    // softmax over the selection, max-subtracted, denominator summed in
+    // selection order (rank 0, 1, ...)
+    const unsigned long long first = __ballot(chosen && rank == 0);
+    const float z0 = __shfl(z, __ffsll(static_cast<long long>(first)) - 1, kWave);
+    const float ex = chosen ? expf(z - z0) : 0.0f;
     float den = 0.0f;
-    for (int j = 0; j < k; ++j) {
-      ex[j] = expf(sel_z[j] - sel_z[0]);
-      den = __fadd_rn(den, ex[j]);
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        const unsigned long long m = __ballot(chosen && rank == j);
+        den = __fadd_rn(den, __shfl(ex, __ffsll(static_cast<long long>(m)) - 1, kWave));
+      }
     }
-    if (lane < k) {
-      float wj = 0.0f;
-      int ej = 0;
-      for (int j = 0; j < k; ++j)
-        if (j == lane) {
-          wj = ex[j] / den;
-          ej = sel_e[j];
-        }
-      p.idx_out[t * k + lane] = ej;
-      p.w_out[t * k + lane] = wj;
-      sel[n * k + lane] = ej;
+    if (chosen) {
+      p.idx_out[t * k + rank] = lane;
+      p.w_out[t * k + rank] = ex / den;
+      sel[n * k + rank] = lane;
     }
   }
-  if (!p.sort.done) return;
+  if (!p.sort.fused) return;
 
   // ------------------------------------------------------------ sort tail
-  if (gridDim.x == 1) {
-    // one workgroup holds every selection: sort from LDS, no cross-CU sync
-    __syncthreads();
-    counting_sort_block(d, p.sort, T * k, reinterpret_cast<int*>(smem), sel);
-    return;
-  }
-  __threadfence();
+  // one workgroup holds every selection: sort from LDS, no cross-CU sync
   __syncthreads();
-  if (threadIdx.x == 0) {
-    const unsigned int prev = __hip_atomic_fetch_add(p.sort.done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    is_last = (prev == gridDim.x - 1);
-  }
-  __syncthreads();
-  if (!is_last) return;
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
-  counting_sort_block(d, p.sort, T * k, reinterpret_cast<int*>(smem), nullptr);
-  if (threadIdx.x == 0) __hip_atomic_store(p.sort.done, 0u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+  counting_sort_block(d, p.sort, T * k, reinterpret_cast<int*>(smem), sel);
 }
 
 template <typename ST, int KQ>
@@ -411,7 +408,7 @@ size_t norm_router_lds_bytes(const Dims& d) {
   return 4 * kRows * 64 * sizeof(float) + (d.bf16 ? static_cast<size_t>(d.H) * 32 : static_cast<size_t>(d.H) * kRows * 4);
 }
 
-int norm_router_sort_limit() { return 8192; }
+int norm_router_sort_limit() { return kRows; }
 
 hipError_t launch_norm_router(const Dims& d, const NormRouterParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;

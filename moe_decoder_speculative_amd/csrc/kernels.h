@@ -25,7 +25,7 @@ struct SortParams {
   int* perm;             // [P]
   int* active;           // [E] experts with cnt > 0, ascending
   int* n_active;         // [1]
-  unsigned int* done;    // completion counter (fused sort tail); NULL: no tail
+  int fused;             // 1: the (single) norm/router workgroup sorts in LDS
 };
 
 // Combine (previous block) + RMSNorm + router/top-k over T token rows.
@@ -41,15 +41,13 @@ struct NormRouterParams {
   void* xhat;              // [T][H] storage out (norm)
   int* idx_out;            // [T][k] (route)
   float* w_out;            // [T][k] (route)
-  unsigned long long* keys;  // [key_slots][key_stride] arg-max keys to clear, optional
-  int key_slots, key_stride;
-  SortParams sort;           // fused counting sort by the last workgroup (sort.done != NULL)
+  SortParams sort;           // fused counting sort (sort.fused: single-workgroup steps only)
   int T;
   int combine, norm, route;
 };
 hipError_t launch_norm_router(const Dims& d, const NormRouterParams& p, hipStream_t s);
 size_t norm_router_lds_bytes(const Dims& d);
-int norm_router_sort_limit();  // largest T*k the fused sort tail handles
+int norm_router_sort_limit();  // largest T the fused single-workgroup sort handles
 
 // Stable counting sort of the T*k (token, slot) pairs by expert.
 struct PermuteParams {
