@@ -186,6 +186,8 @@ def main():
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for 1.5 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -202,6 +204,17 @@ def main():
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
+    if args.copy_calibration:
+        # a copy kernel of known size: FETCH_SIZE and WRITE_SIZE of one
+        # dispatch against 1 GiB give the counters' scale
+        n = 1 << 30
+        src = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "dispatches": 5}))
+        return
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w.name}: B={w.B} K={w.K} T={w.T} L={w.L} H={w.H} E={w.E} k={w.k} S={w.S} I={w.I} V={w.V}")
     t = time.time()
@@ -290,7 +303,7 @@ def main():
                 "kernel": kname, "flops_per_launch": kflops}
     else:
         if stage == binding.MOE_STAGE_LMHEAD:
-            kname = "k_lmhead_fused" if w.T <= 16 else ("k_lmhead_wide" if w.T <= 128 else "k_lmhead_mfma")
+            kname = "k_lmhead_stream" if w.T <= 16 else ("k_lmhead_wide" if w.T <= 128 else "k_lmhead_mfma")
             kfile, kbytes = "k_lmhead.hip", lmhead_bytes(w)
         else:
             kname, kfile = "k_up_mfma", "k_experts.hip"
