@@ -7,8 +7,13 @@
 // each loads its quarter of the weight tile straight into registers with
 // coalesced 1 KiB reads (weights are pre-tiled in MFMA operand order), keeps it
 // there, and loops over the expert's tokens 16 at a time (tokens gathered from
-// the permutation, padded with zeros), issuing 16x16x32 bf16 MFMAs.  The four
-// partial sums are added through LDS.
+// the permutation; columns past the expert's tokens repeat its last token and
+// are never stored), issuing 16x16x32 bf16 MFMAs; with several token tiles the
+// next tile's activation fragments are requested before the current tile's
+// MFMAs.  The four partial sums are added through LDS.  For steps sorted by
+// the permutation kernel the slots are launched busiest first (the active
+// list is ordered by token count), so the longest workgroups do not trail
+// the kernel.
 //   up:   a[pair][i] = round(silu(Wg x)[i] * (Wu x)[i])        (pairs of the slot)
 //   down: y[pair][h] = (Wd a)[h]                                 (float32)
 // Shared experts occupy slots 0..S-1 and see every token.  The page "Jina AI
@@ -76,17 +81,18 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p) {
   const bf16_t* xh = reinterpret_cast<const bf16_t*>(p.xhat);
   bf16_t* act = reinterpret_cast<bf16_t*>(p.act);
 
-  for (int tile0 = 0; tile0 < si.ntok; tile0 += kTile) {
-    const int n = tile0 + lane % kTile;
-    int pair = -1, tok = 0;
-    if (n < si.ntok) {
-      pair = slot_pair(d, p, si, n);
-      tok = si.shared >= 0 ? n : pair / d.k;
-    }
+  // activation fragments of the token tile at tile0 (column lane % 16); rows
+  // past the slot's tokens repeat its last token and are never stored
+  auto load_tile = [&](int tile0, int& pair, bf16x8_t (&b)[KW]) {
+    const int n = tile0 + lane % kTile, nc = min(n, si.ntok - 1);
+    const int pr = slot_pair(d, p, si, nc);
+    pair = n < si.ntok ? pr : -1;
+    const int tok = si.shared >= 0 ? nc : pr / d.k;
     const bf16_t* xr = xh + static_cast<int64_t>(tok) * d.H + kt0 * kKStep + (lane / kTile) * 8;
-    bf16x8_t b[KW];
 #pragma unroll
-    for (int i = 0; i < KW; ++i) b[i] = pair >= 0 ? load_frag(xr + i * kKStep) : zero_frag();
+    for (int i = 0; i < KW; ++i) b[i] = load_frag(xr + i * kKStep);
+  };
+  auto do_tile = [&](int pair, const bf16x8_t (&b)[KW]) {
     f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < KW; ++i) {
@@ -111,6 +117,25 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p) {
       }
     }
     __syncthreads();
+  };
+
+  int pair;
+  bf16x8_t b[KW];
+  load_tile(0, pair, b);
+  if (si.ntok <= kTile) {
+    do_tile(pair, b);
+    return;
+  }
+  // several token tiles: the next tile's fragments are requested before this
+  // tile's MFMAs (unconditionally; past the last tile they are never used)
+  for (int tile0 = 0; tile0 < si.ntok; tile0 += kTile) {
+    int pair_n;
+    bf16x8_t bn[KW];
+    load_tile(tile0 + kTile, pair_n, bn);
+    do_tile(pair, b);
+    pair = pair_n;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) b[i] = bn[i];
   }
 }
 
@@ -135,13 +160,17 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p) {
   }
   const bf16_t* act = reinterpret_cast<const bf16_t*>(p.act);
 
-  for (int tile0 = 0; tile0 < si.ntok; tile0 += kTile) {
+  // activation fragments of the token tile at tile0 (column lane % 16); rows
+  // past the slot's tokens repeat its last pair and are never stored
+  auto load_tile = [&](int tile0, int& pair, bf16x8_t (&b)[KW]) {
     const int n = tile0 + lane % kTile;
-    const int pair = n < si.ntok ? slot_pair(d, p, si, n) : -1;
-    const bf16_t* ar = act + static_cast<int64_t>(pair < 0 ? 0 : pair) * d.I + kt0 * kKStep + (lane / kTile) * 8;
-    bf16x8_t b[KW];
+    const int pr = slot_pair(d, p, si, min(n, si.ntok - 1));
+    pair = n < si.ntok ? pr : -1;
+    const bf16_t* ar = act + static_cast<int64_t>(pr) * d.I + kt0 * kKStep + (lane / kTile) * 8;
 #pragma unroll
-    for (int i = 0; i < KW; ++i) b[i] = pair >= 0 ? load_frag(ar + i * kKStep) : zero_frag();
+    for (int i = 0; i < KW; ++i) b[i] = load_frag(ar + i * kKStep);
+  };
+  auto do_tile = [&](int pair, const bf16x8_t (&b)[KW]) {
     f32x4_t c[RPW];
 #pragma unroll
     for (int r = 0; r < RPW; ++r) {
@@ -163,6 +192,25 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p) {
       }
     }
     __syncthreads();
+  };
+
+  int pair;
+  bf16x8_t b[KW];
+  load_tile(0, pair, b);
+  if (si.ntok <= kTile) {
+    do_tile(pair, b);
+    return;
+  }
+  // several token tiles: the next tile's fragments are requested before this
+  // tile's MFMAs (unconditionally; past the last tile they are never used)
+  for (int tile0 = 0; tile0 < si.ntok; tile0 += kTile) {
+    int pair_n;
+    bf16x8_t bn[KW];
+    load_tile(tile0 + kTile, pair_n, bn);
+    do_tile(pair, b);
+    pair = pair_n;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) b[i] = bn[i];
   }
 }
 

@@ -1,5 +1,6 @@
 // Combine + RMSNorm + top-k softmax router (+ counting sort for small steps),
-// one 1024-thread workgroup (16 wavefronts) per 16 token rows.
+// one 1024-thread workgroup (16 wavefronts) per 16 token rows (4 for steps of
+// 17..256 rows, to spread the combine reads over more CUs).
 //
 // Phase 1 (wavefront w owns row w): optionally finish the previous block
 //   (m = shared outputs + gate-weighted routed outputs in ascending expert
@@ -32,7 +33,7 @@ namespace {
 
 constexpr int kThreads = 1024;   // 16 wavefronts
 constexpr int kWaves = kThreads / kWave;
-constexpr int kRows = 16;        // token rows per workgroup
+constexpr int kRows = 16;        // token rows a workgroup can hold (MFMA tile columns)
 constexpr int kGroup = 2;        // expert rows loaded together in the combine
 
 template <typename ST>
@@ -76,6 +77,8 @@ __device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, i
     }
     const unsigned long long act = __ballot(c > 0);
     base[lane] = incl - c;
+    // active experts in ascending order (at most 16 tokens: every expert has
+    // about the same load, so no busiest-first ordering)
     if (lane < E) {
       s.cnt[lane] = c;
       s.off[lane] = incl - c;
@@ -118,7 +121,7 @@ __device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, i
 }
 
 template <typename ST, int KQ>  // KQ = H / 128: router k-steps per wavefront (bf16)
-__global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterParams p) {
+__global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterParams p, int rows) {
   // dynamic LDS: [0, 16 KiB) router partials zp[4][16][64] (reused by the sort);
   // then bf16 xh operand tiles [H/32][64 lanes][8] or f32 xh rows [16][H]
   extern __shared__ __align__(16) unsigned char smem[];
@@ -129,7 +132,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   const int H = d.H, k = d.k, T = p.T;
   const int lane = threadIdx.x % kWave;
   const int wave = threadIdx.x / kWave;
-  const int t0 = blockIdx.x * kRows;
+  const int t0 = blockIdx.x * rows;  // rows <= kRows token rows per workgroup
   const int nchunks = H / 4;
   constexpr int CPL = (KQ + 1) / 2;  // 4-element chunks per lane: ceil(H / 256)
 
@@ -140,7 +143,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   bf16x8_t ra[KQ];
   const int n = wave;
   const int t = t0 + n;
-  const bool has_row = n < kRows && t < T;
+  const bool has_row = n < rows && t < T;
   auto load_router = [&]() {
     if constexpr (sizeof(ST) == 2) {
       if (p.route && et * 16 < d.E) {
@@ -284,7 +287,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   }
   if (!p.route) return;
   load_router();
-  const int nrows = min(kRows, T - t0);
+  const int nrows = min(rows, T - t0);
   if constexpr (sizeof(ST) == 2) {
     // rows of this workgroup past T: zero operand lanes so MFMA reads defined values
     if (nrows < kRows) {
@@ -376,10 +379,14 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
 
 template <typename ST, int KQ>
 hipError_t launch_kq(const Dims& d, const NormRouterParams& p, hipStream_t s) {
-  const dim3 grid((p.T + kRows - 1) / kRows);
+  // 16 rows per workgroup when one workgroup takes the whole step (fused sort)
+  // or the step is prefill-sized; 4 otherwise, so that a verify step of a few
+  // hundred rows spreads its combine reads over more CUs
+  const int rows = (p.T <= kRows || p.T > 256) ? kRows : 4;
+  const dim3 grid((p.T + rows - 1) / rows);
   const size_t xs = p.route ? (sizeof(ST) == 2 ? static_cast<size_t>(d.H) * 32 : static_cast<size_t>(d.H) * kRows * 4) : 0;
   const size_t smem = 4 * kRows * 64 * sizeof(float) + xs;
-  hipLaunchKernelGGL((k_norm_router<ST, KQ>), grid, dim3(kThreads), smem, s, d, p);
+  hipLaunchKernelGGL((k_norm_router<ST, KQ>), grid, dim3(kThreads), smem, s, d, p, rows);
   return hipGetLastError();
 }
 

@@ -7,8 +7,9 @@
 // offset and its rank among the active experts), then gathers the pairs routed
 // to e in increasing pair order: each thread scans a contiguous run of pairs,
 // a block-wide exclusive scan of the per-thread match counts gives every
-// thread its output position, and the thread writes its matches in order.  Outputs cnt[e], off[e] (and off[E] = P), perm[off[e] ..] and the
-// ascending list of active experts.  Grouping tokens by expert is what lets a
+// thread its output position, and the thread writes its matches in order.
+// Outputs cnt[e], off[e] (and off[E] = P), perm[off[e] ..] and the list of
+// active experts, busiest first.  Grouping tokens by expert is what lets a
 // top-k mixture of experts touch each selected expert's weights once per step
 // (page "Jina AI lance jina-ocr-v1 ...", section "Architecture MoE et
 // economies de parametres": only a fraction of the parameters is active per
@@ -60,12 +61,20 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(int E, PermuteParams p
       if (lane >= o) incl += v;
     }
     const unsigned long long act = __ballot(c > 0);
+    // active experts, busiest first (ties: lower id first): the expert kernels
+    // start the longest slots first
+    int rank = 0;
+#pragma unroll
+    for (int q = 0; q < kWave; ++q) {
+      const int cq = __builtin_amdgcn_readlane(c, q);
+      rank += (cq > c || (cq == c && q < lane)) ? 1 : 0;
+    }
     if (lane == e) {
       base_e = incl - c;
       cnt_e = c;
       p.cnt[e] = c;
       p.off[e] = incl - c;
-      if (c > 0) p.active[__popcll(act & ((1ull << lane) - 1ull))] = e;
+      if (c > 0) p.active[rank] = e;
     }
     if (e == E - 1 && lane == E - 1) {
       p.off[E] = incl;

@@ -56,13 +56,14 @@ struct PermuteParams {
   int* cnt;        // [E]
   int* off;        // [E+1]
   int* perm;       // [P]
-  int* active;     // [E] experts with cnt > 0, ascending; entries past n_active unused
+  int* active;     // [E] experts with cnt > 0, busiest first; entries past n_active unused
   int* n_active;   // [1]
 };
 hipError_t launch_permute(const Dims& d, const PermuteParams& p, hipStream_t s);
 
 // Expert SwiGLU on the decode path.  Expert slots: 0..S-1 are the shared
-// experts (every token), then the active routed experts in ascending order.
+// experts (every token), then the active routed experts in the order of the
+// active list (busiest first when the permutation kernel built it).
 // Activation / output rows: pair p = t*k + j for routed, T*k + s*T + t for shared.
 struct ExpertParams {
   const void* xhat;      // [T][H] storage
