@@ -3,14 +3,15 @@
 // At prefill sizes (about 915 tokens per routed expert, every token for each
 // shared expert) the experts are bound by MFMA throughput, not HBM.  Work item
 // = (expert slot, tile of 128 output features, tile of 256 of the slot's
-// tokens).  A 256-thread workgroup computes one item: its operands for each
+// tokens).  A 512-thread workgroup computes one item: its operands for each
 // 32-wide step of the reduction dimension -- 16 weight row tiles (already in
 // MFMA operand order in HBM) and 16 token tiles gathered through the
 // permutation (padding lanes read an all-zero row) -- go straight from global
 // memory into a 4-stage LDS ring with gfx950's direct-to-LDS 16-byte loads
-// (no registers, three steps in flight), and each of the four wavefronts
-// accumulates a 128 x 128 (rows x tokens) tile with 16x16x32 bf16 MFMAs
-// (256 accumulators per lane, in AGPRs).
+// (no registers, three steps in flight), and each of the eight wavefronts
+// (two per SIMD, so one's MFMAs cover the other's waits) accumulates a
+// 128 x 64 (rows x tokens) tile with 16x16x32 bf16 MFMAs (128 accumulators
+// per lane).
 //   up:   rows are 8 gate + 8 up tiles of the same 128 features; epilogue
 //         a = round(silu(g) * u) written per pair (bf16)
 //   down: rows are 16 tiles of 16 hidden features; epilogue y (fp32) per pair
@@ -34,6 +35,7 @@ constexpr int kTokTiles = kBT / kTile;
 constexpr int kStages = 4;        // LDS ring depth (one 32-wide k-step per stage), 128 KiB
 constexpr int kStageBytes = (kRowTiles + kTokTiles) * kFragElems * 2;   // 32 KiB
 constexpr int kXcds = 8;
+constexpr int kGemmThreads = 512;  // 8 wavefronts: two per SIMD
 
 // Tile table: one entry per (slot, token tile), shared slots first, then the
 // routed experts in ascending order.  Built on the device after the
@@ -63,13 +65,13 @@ __global__ __launch_bounds__(64) void k_tile_list(Dims d, GemmTileParams p) {
 }
 
 template <bool UP>
-__global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
+__global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(Dims d, GemmParams p) {
   // LDS ring of kStages stages; a stage holds one 32-wide k-step: 16 weight
   // fragments then 16 token fragments, 1 KiB each, in MFMA operand order.
   extern __shared__ __align__(16) unsigned char smem[];
 
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int wr = wave / 2, wt = wave % 2;         // wavefront's row half / token half
+  const int wr = wave / 4, wt = wave % 4;         // wavefront's row half / token quarter
   const int n_ft = UP ? d.I / 128 : d.H / 256;     // feature tiles per slot
   const int n_items = *p.n_tiles * n_ft;
   const int chunk = (n_items + kXcds - 1) / kXcds;
@@ -98,14 +100,14 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
   const int zero_row = UP ? p.xhat_zero_row : p.act_zero_row;
   const int rows_per_expert_tiles = UP ? d.I / kTile : d.H / kTile;
 
-  // this wavefront fills weight fragments 4w..4w+3 and token fragments
-  // 4w..4w+3 of every stage; lane offsets (elements, 32-bit) advance by one
+  // this wavefront fills weight fragments 2w, 2w+1 and token fragments
+  // 2w, 2w+1 of every stage; lane offsets (elements, 32-bit) advance by one
   // k-step per stage
-  int woff[4], toff[4];
-  const bf16_t* wmat[4];
+  int woff[2], toff[2];
+  const bf16_t* wmat[2];
 #pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int r = wave * 4 + q;  // weight row tile of the item
+  for (int q = 0; q < 2; ++q) {
+    const int r = wave * 2 + q;  // weight row tile of the item
     int row_tile;
     if (UP) {
       const int half = r / 8, qq = r % 8;
@@ -124,53 +126,52 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
   auto issue = [&](int kt) {
     unsigned char* st = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
+    for (int q = 0; q < 2; ++q) {
       __builtin_amdgcn_global_load_lds((void*)(wmat[q] + woff[q] + kt * kFragElems),
-                                       (lds_ptr_t)(st + (wave * 4 + q) * 1024), 16, 0, 0);
+                                       (lds_ptr_t)(st + (wave * 2 + q) * 1024), 16, 0, 0);
       __builtin_amdgcn_global_load_lds((void*)(src + toff[q] + kt * kKStep),
-                                       (lds_ptr_t)(st + (kRowTiles + wave * 4 + q) * 1024), 16, 0, 0);
+                                       (lds_ptr_t)(st + (kRowTiles + wave * 2 + q) * 1024), 16, 0, 0);
     }
   };
 
-  f32x4_t acc[8][8];
+  f32x4_t acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // Fragment registers, double buffered: step k+1 is read from LDS while the
-  // 64 MFMAs of step k run.  KT is even (H and I are multiples of 128), so the
+  // 32 MFMAs of step k run.  KT is even (H and I are multiples of 128), so the
   // loop runs in pairs with the two register sets in fixed roles.
   //
   // The barriers are bare: a fenced barrier would wait for every load in
   // flight, later steps included, and drain the ring.  LDS-DMA writes are
   // complete once vmcnt says so; each wavefront waits for its own loads of a
   // step before the barrier, so after it every wavefront's share has landed.
-  bf16x8_t a0[8], b0[8], a1[8], b1[8];
+  bf16x8_t a0[8], b0[4], a1[8], b1[4];
 #define MOE_READ_STEP(K, A, B)                                                                     \
   {                                                                                                \
     const unsigned char* st_ = smem + ((K) % kStages) * kStageBytes;                               \
-    _Pragma("unroll") for (int j = 0; j < 8; ++j) B[j] =                                           \
-        *reinterpret_cast<const bf16x8_t*>(st_ + (kRowTiles + wt * 8 + j) * 1024 + lane * 16);     \
+    _Pragma("unroll") for (int j = 0; j < 4; ++j) B[j] =                                           \
+        *reinterpret_cast<const bf16x8_t*>(st_ + (kRowTiles + wt * 4 + j) * 1024 + lane * 16);     \
     _Pragma("unroll") for (int i = 0; i < 8; ++i) A[i] =                                           \
         *reinterpret_cast<const bf16x8_t*>(st_ + (wr * 8 + i) * 1024 + lane * 16);                 \
   }
 #define MOE_MMA_STEP(A, B)                                                                         \
   _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                    \
-  _Pragma("unroll") for (int j = 0; j < 8; ++j) acc[i][j] = mfma16(A[i], B[j], acc[i][j]);
+  _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(A[i], B[j], acc[i][j]);
   // wait for this wavefront's loads of step k+1 at iteration k: the steps
-  // issued after it (up to two) may stay in flight, 8 loads each
+  // issued after it (up to two) may stay in flight, 4 loads each
 #define MOE_WAIT_NEXT(K)                                                                           \
   {                                                                                                \
     const int later_ = min(KT, (K) + kStages) - (K) - 2;                                           \
-    if (later_ >= 3) __builtin_amdgcn_s_waitcnt(waitcnt_vm(24));                                   \
-    else if (later_ == 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(16));                              \
-    else if (later_ == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));                               \
+    if (later_ >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));                                    \
+    else if (later_ == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));                               \
     else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                                \
   }
 // One step: make step K+1 available (wait for this wavefront's loads, bare
-// barrier, refill the ring), then run step K's 64 MFMAs with step K+1's 16
-// fragment reads interleaved, one read after every 4 MFMAs.  Interleaving
+// barrier, refill the ring), then run step K's 32 MFMAs with step K+1's 12
+// fragment reads interleaved (a read after every 2 or 3 MFMAs).  Interleaving
 // matters: with all reads ahead of the MFMAs, the first MFMA waits for all of
 // them (the LDS counter cannot express "16 newer reads may stay in flight").
 // At the last step the reads fetch a stale stage that is never used.
@@ -183,8 +184,12 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
     }                                                                                              \
     MOE_MMA_STEP(CA, CB)                                                                           \
     MOE_READ_STEP((K) + 1, NA, NB)                                                                 \
-    _Pragma("unroll") for (int g_ = 0; g_ < 16; ++g_) {                                            \
-      __builtin_amdgcn_sched_group_barrier(0x008, 4, 0); /* 4 MFMA */                              \
+    _Pragma("unroll") for (int g_ = 0; g_ < 8; ++g_) {                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0); /* 3 MFMA */                              \
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* 1 LDS read */                          \
+    }                                                                                              \
+    _Pragma("unroll") for (int g_ = 0; g_ < 4; ++g_) {                                             \
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); /* 2 MFMA */                              \
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* 1 LDS read */                          \
     }                                                                                              \
   }
@@ -193,11 +198,11 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
   for (int s = 0; s < kStages; ++s)
     if (s < KT) issue(s);
   // step 0 landed once the other issued steps (up to kStages - 1) remain
+  static_assert(kStages == 4, "wait counts below assume a 4-stage ring");
   switch (min(KT, kStages) - 1) {
-    case 4: __builtin_amdgcn_s_waitcnt(waitcnt_vm(32)); break;
-    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(24)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(16)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(8)); break;
+    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(12)); break;
+    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(8)); break;
+    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); break;
     default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
   }
   __builtin_amdgcn_s_barrier();
@@ -218,8 +223,8 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
     for (int f = 0; f < 4; ++f) {
       const int feat = (ft * 8 + wr * 4 + f) * kTile + 4 * (lane / kTile);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int pr = pair_of((wt * 8 + j) * kTile + lane % kTile);
+      for (int j = 0; j < 4; ++j) {
+        const int pr = pair_of((wt * 4 + j) * kTile + lane % kTile);
         if (pr < 0) continue;
         ushort4 v;
         v.x = f32_to_bf16(silu_mul(acc[f][j][0], acc[f + 4][j][0]));
@@ -234,8 +239,8 @@ __global__ __launch_bounds__(kBlock) void k_grouped_gemm(Dims d, GemmParams p) {
     for (int i = 0; i < 8; ++i) {
       const int feat = (ft * 16 + wr * 8 + i) * kTile + 4 * (lane / kTile);
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int pr = pair_of((wt * 8 + j) * kTile + lane % kTile);
+      for (int j = 0; j < 4; ++j) {
+        const int pr = pair_of((wt * 4 + j) * kTile + lane % kTile);
         if (pr < 0) continue;
         *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(pr) * d.H + feat) =
             make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
@@ -266,9 +271,9 @@ hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipSt
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   const size_t smem = gemm_lds_bytes();
   if (up)
-    hipLaunchKernelGGL(k_grouped_gemm<true>, dim3(static_cast<unsigned>(grid)), dim3(kBlock), smem, s, d, p);
+    hipLaunchKernelGGL(k_grouped_gemm<true>, dim3(static_cast<unsigned>(grid)), dim3(kGemmThreads), smem, s, d, p);
   else
-    hipLaunchKernelGGL(k_grouped_gemm<false>, dim3(static_cast<unsigned>(grid)), dim3(kBlock), smem, s, d, p);
+    hipLaunchKernelGGL(k_grouped_gemm<false>, dim3(static_cast<unsigned>(grid)), dim3(kGemmThreads), smem, s, d, p);
   return hipGetLastError();
 }
 
