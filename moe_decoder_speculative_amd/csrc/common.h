@@ -22,12 +22,18 @@ __device__ __forceinline__ float bf16_to_f32(bf16_t v) {
   return __uint_as_float(static_cast<uint32_t>(v) << 16);
 }
 
-// float32 -> bfloat16, round to nearest, ties to even; NaN -> quiet NaN.
+// float32 -> bfloat16 on gfx950's conversion instruction: round to nearest,
+// ties to even; a NaN stays a (quiet) NaN.
 __device__ __forceinline__ bf16_t f32_to_bf16(float f) {
-  uint32_t u = __float_as_uint(f);
-  if ((u & 0x7fffffffu) > 0x7f800000u) return 0x7fc0;
-  u += 0x7fffu + ((u >> 16) & 1u);
-  return static_cast<bf16_t>(u >> 16);
+  return __builtin_bit_cast(bf16_t, static_cast<__bf16>(f));
+}
+
+// Two floats -> two bfloat16 in one 32-bit word (a in the low half), rounded
+// as f32_to_bf16 does, in a single conversion instruction.
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
 }
 
 // Storage-type traits: load one element as float, round a float to storage.
@@ -105,6 +111,12 @@ __device__ __forceinline__ uint32_t argmax_key_index(uint64_t key) {
   return 0xffffffffu - static_cast<uint32_t>(key & 0xffffffffu);
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// SwiGLU gate: silu(g) * u = g * u / (1 + e^-g), with e^-g = 2^(-g log2 e) on
+// the hardware exp2 and the quotient on the hardware reciprocal (about one ulp
+// each, far below the bfloat16 rounding that follows).  For very negative g,
+// e^-g overflows to inf and the result is a signed zero, the correct limit.
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * u * __builtin_amdgcn_rcpf(1.0f + __builtin_amdgcn_exp2f(-g * 1.44269504088896341f));
+}
 
 }  // namespace moe

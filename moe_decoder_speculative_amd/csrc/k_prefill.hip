@@ -134,6 +134,11 @@ __global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(Dims d, GemmParam
     }
   };
 
+  // result rows of this wavefront's 64 tokens, looked up while the loop runs
+  int out_pair[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) out_pair[j] = pair_of((wt * 4 + j) * kTile + lane % kTile);
+
   f32x4_t acc[8][4];
 #pragma unroll
   for (int i = 0; i < 8; ++i)
@@ -224,14 +229,12 @@ __global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(Dims d, GemmParam
       const int feat = (ft * 8 + wr * 4 + f) * kTile + 4 * (lane / kTile);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int pr = pair_of((wt * 4 + j) * kTile + lane % kTile);
+        const int pr = out_pair[j];
         if (pr < 0) continue;
-        ushort4 v;
-        v.x = f32_to_bf16(silu_mul(acc[f][j][0], acc[f + 4][j][0]));
-        v.y = f32_to_bf16(silu_mul(acc[f][j][1], acc[f + 4][j][1]));
-        v.z = f32_to_bf16(silu_mul(acc[f][j][2], acc[f + 4][j][2]));
-        v.w = f32_to_bf16(silu_mul(acc[f][j][3], acc[f + 4][j][3]));
-        *reinterpret_cast<ushort4*>(act + static_cast<int64_t>(pr) * d.I + feat) = v;
+        uint2 v;
+        v.x = pack_bf16x2(silu_mul(acc[f][j][0], acc[f + 4][j][0]), silu_mul(acc[f][j][1], acc[f + 4][j][1]));
+        v.y = pack_bf16x2(silu_mul(acc[f][j][2], acc[f + 4][j][2]), silu_mul(acc[f][j][3], acc[f + 4][j][3]));
+        *reinterpret_cast<uint2*>(act + static_cast<int64_t>(pr) * d.I + feat) = v;
       }
     }
   } else {
@@ -240,7 +243,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(Dims d, GemmParam
       const int feat = (ft * 16 + wr * 8 + i) * kTile + 4 * (lane / kTile);
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const int pr = pair_of((wt * 4 + j) * kTile + lane % kTile);
+        const int pr = out_pair[j];
         if (pr < 0) continue;
         *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(pr) * d.H + feat) =
             make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
