@@ -154,12 +154,14 @@ def cpu_baseline(w, weights, hidden_np, drafts_np, seconds: float):
             oracle.verify_step(shp, weights, h, d, Bs, K)
     else:
         rows = min(w.T, 256)
-        h = hidden_np[:rows]
-        what = f"{rows} token rows per oracle block call"
+        h = oracle.as_f32(hidden_np[:rows])
+        what = f"{rows} token rows through {w.L} block(s) per oracle call"
         tokens_per_call = rows
 
         def call():
-            oracle.moe_block(h, weights["layers"][0], shp)
+            x = h
+            for l in range(w.L):
+                x = oracle.moe_block(x, weights["layers"][l], shp).x_out
     t0 = time.perf_counter()
     n = 0
     while True:
@@ -182,7 +184,8 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b1",
-                    choices=["decode_b1", "decode_b32_zipf", "stack12_b32_zipf", "prefill_8pages"])
+                    choices=["decode_b1", "decode_b32_zipf", "stack12_b32_zipf", "prefill_8pages",
+                             "prefill_8pages_stack12"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for 1.5 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -235,15 +238,23 @@ def main():
     drafts_np = None
     committed_per_step = None
     if prefill:
-        y = torch.empty_like(hidden)
+        # the blocks in turn, residual stream ping-ponging between two buffers
+        ys = [torch.empty_like(hidden), torch.empty_like(hidden)]
         aux = model.alloc_aux(w.T, layers=1, with_hidden=False)
         aux.pop("tstar")
-        model.block_forward(0, hidden, w.T, y, aux)
-        torch.cuda.synchronize()
-        touched = [int((aux["expert_count"][0] > 0).sum().item())]
+        touched = []
+        src = hidden
+        for l in range(w.L):
+            model.block_forward(l, src, w.T, ys[l % 2], aux)
+            torch.cuda.synchronize()
+            touched.append(int((aux["expert_count"][0] > 0).sum().item()))
+            src = ys[l % 2]
 
         def run(c):
-            model.block_forward(0, hidden, w.T, y, copy=c)
+            x = hidden
+            for l in range(w.L):
+                model.block_forward(l, x, w.T, ys[l % 2], copy=c)
+                x = ys[l % 2]
     else:
         # drafts: each correct with probability p against this step's own greedy picks
         committed, counts = model.alloc_outputs(w.B, w.K)

@@ -98,6 +98,11 @@ WORKLOADS = {
                                has_lm_head=False, seed_id=4),
     # 12 blocks with residual between them, then the LM head
     "stack12_b32_zipf": _verify("stack12_b32_zipf", 5, B=32, L=12, routing="zipf"),
+    # the 8-page prefill through the same 12-block stack (no LM head)
+    "prefill_8pages_stack12": Workload("prefill_8pages_stack12", H=1280, E=64, k=6, S=2, I=896,
+                                       V=129280, L=12, B=0, K=0, T=8 * (1156 + 64),
+                                       dtype="bf16", routing="uniform", drafts="none",
+                                       has_lm_head=False, seed_id=6),
 }
 
 

@@ -86,6 +86,52 @@ def check_block(out: dict, l: int, blk, k: int, E: int, dtype: str, T: int, tag=
     return float(err.max())
 
 
+def check_rows_teacher_forced(per_layer: list, x0, weights: dict, shp, margin: float = 1e-3,
+                              slack: float = 2e-3) -> str:
+    """Sampled rows of a multi-block forward, block by block on the GPU's own
+    residual stream (an MoE block treats every row on its own, so the rows can
+    be checked apart from the rest).  per_layer[l] holds the GPU's topk_idx,
+    topk_w, moe_out and block output x_out for the rows; x0 their input rows
+    (storage).  Per block the oracle recomputes the block from the GPU's input:
+    expert sets equal where the oracle's top-k margin is >= margin (a valid
+    top-k within slack elsewhere); gate weights within W_TOL and the MoE output
+    within the storage tolerance wherever the sets are equal; and the GPU's
+    block output equal, bit for bit, to the residual rebuilt from its own MoE
+    output."""
+    from oracle import moe_oracle as O
+    store = O.storage_round(shp.dtype)
+    x = O.as_f32(x0)
+    undecided = 0
+    differing = 0
+    worst = 0.0
+    for l, g in enumerate(per_layer):
+        ref = O.moe_block(x, weights["layers"][l], shp)
+        idx = g["topk_idx"]
+        mg = O.topk_margin(ref.z, shp.k)
+        same = np.all(np.sort(idx, 1) == np.sort(ref.idx, 1), axis=1)
+        decided = mg >= margin
+        assert np.all(same[decided]), f"layer {l}: expert sets differ on rows {np.where(decided & ~same)[0]}"
+        for t in np.where(~decided)[0]:
+            sel = np.zeros(shp.E, bool)
+            sel[idx[t]] = True
+            assert ref.z[t, sel].min() >= ref.z[t, ~sel].max() - slack, f"layer {l} row {t}: invalid top-k"
+        undecided += int((~decided).sum())
+        differing += int((~same).sum())
+        o_sel = np.argsort(idx, 1, kind="stable")
+        r_sel = np.argsort(ref.idx, 1, kind="stable")
+        gw = np.take_along_axis(g["topk_w"], o_sel, 1)[same]
+        rw = np.take_along_axis(ref.w, r_sel, 1)[same]
+        assert np.abs(gw - rw).max() <= W_TOL, f"layer {l}: gate weights off by {np.abs(gw - rw).max()}"
+        err = rowwise_rel_err(g["moe_out"][same], ref.m[same])
+        assert err.max() <= REL_TOL[shp.dtype], f"layer {l}: moe_out rel err {err.max():.3e}"
+        worst = max(worst, float(err.max()))
+        rebuilt = store((x + g["moe_out"]).astype(np.float32))
+        assert np.array_equal(rebuilt, g["x_out"]), f"layer {l}: block output is not x + moe_out rounded"
+        x = g["x_out"]
+    return (f"{len(per_layer)} blocks x {x.shape[0]} rows: moe_out rel err {worst:.2e}; undecided top-k "
+            f"rows {undecided}, rows with another expert set {differing}")
+
+
 def check_step(out: dict, case, B: int, K: int, tag=""):
     ref = case.ref
     w = case.w

@@ -212,3 +212,45 @@ def test_block_forward_grouped_gemm_small(T):
 def test_prefill_8pages_full_shape():
     case = workloads.cached_case("prefill_8pages")
     _prefill_case_check(case, "prefill_8pages")
+
+
+@pytest.mark.slow
+def test_prefill_8pages_stack12_sampled():
+    """The 8-page prefill through the 12-block stack, grouped-GEMM path in every
+    block, as the bench runs it (moe_block_forward per block, the residual
+    stream alternating between two buffers).  The oracle follows a sample of
+    rows -- the first, the last, and 190 drawn at random -- block by block on
+    the GPU's own residual stream (see parity.check_rows_teacher_forced)."""
+    torch = _torch()
+    w = synth.WORKLOADS["prefill_8pages_stack12"]
+    shp = workloads.shape_of(w)
+    weights = synth.gen_weights(w)
+    noise = synth.HiddenNoise(w)
+    offset = synth.hidden_offset(w, weights, noise)
+    hidden = synth.to_storage(noise.draw(w.T) + offset, w.dtype)
+    rng = np.random.default_rng(6012)
+    rows = np.unique(np.concatenate([[0, w.T - 1], rng.choice(w.T, 190, replace=False)]))
+    parity.say(f"[prefill_stack12] T={w.T} L={w.L} sampled rows={rows.size} entry=moe_block_forward x {w.L}")
+    model = VerifyModel(w, weights, max_tokens=16, max_prefill_tokens=w.T)
+    per_layer = []
+    try:
+        x = to_device(hidden)
+        ys = [torch.empty_like(x), torch.empty_like(x)]
+        aux = model.alloc_aux(w.T, layers=1, with_hidden=False)
+        aux.pop("tstar")
+        r = torch.from_numpy(rows).to(x.device)
+        src = x
+        for l in range(w.L):
+            model.block_forward(l, src, w.T, ys[l % 2], aux)
+            torch.cuda.synchronize()
+            per_layer.append({
+                "topk_idx": aux["topk_idx"][0][r].cpu().numpy(),
+                "topk_w": aux["topk_w"][0][r].cpu().numpy(),
+                "moe_out": aux["moe_out"][0][r].cpu().numpy(),
+                "x_out": parity.storage_to_f32(ys[l % 2][r]),
+            })
+            src = ys[l % 2]
+    finally:
+        model.close()
+    stats = parity.check_rows_teacher_forced(per_layer, hidden[rows], weights, shp)
+    parity.say(f"[prefill_stack12] ok: {stats}")
