@@ -176,6 +176,73 @@ def cpu_baseline(w, weights, hidden_np, drafts_np, seconds: float):
             "sample": f"{n} calls of {what} in {el:.1f} s (numpy float32, BLAS threads {threads})"}
 
 
+# ---------------------------------------------------------------- decode-loop cost model
+
+def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, VerifyModel, to_device):
+    """Verify-step cost against the number of drafts K, eager launches against
+    a HIP-graph replay of the same step.  For each K in 0..3 on the
+    workload's B sequences: the step time both ways, the committed tokens per
+    sequence expected at per-draft acceptance p (sum of p^i, i = 0..K, the
+    accepted prefix plus the bonus), c_K = t_K / t_0 (the verify step's cost in
+    one-token steps, K = 0 being plain greedy decoding) and the speed-up over
+    greedy decoding S_K = tau_K / c_K (the pages' c = tau / S, page "jina-ocr-v1 :
+    Analyse de documents plus rapide sur des GPU a budget limite", section
+    "Decodage speculatif sur un L4")."""
+    B = w0.B
+    p = w0.accept_p
+    model = VerifyModel(w0, weights, max_tokens=B * 4, copies=copies)
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
+    ev = HipEvents()
+    rows = []
+    for K in range(4):
+        T = B * (K + 1)
+        hidden = to_device(hidden_np[:T])
+        committed, counts = model.alloc_outputs(B, K)
+        aux = model.alloc_aux(T, with_hidden=False)
+        model.step(hidden, to_device(np.zeros((B, K), np.int32)) if K else None, B, K, committed, counts, aux)
+        torch.cuda.synchronize()
+        wk = w0.with_(K=K, T=T)
+        drafts = to_device(synth.make_drafts(wk, aux["tstar"].cpu().numpy().reshape(B, K + 1))) if K else None
+        del aux
+
+        def timed(launch, n):
+            for i in range(args.warmup):
+                launch(i % copies)
+            stream.synchronize()
+            a, b = ev.create(), ev.create()
+            ev.record(a, sh)
+            for i in range(n):
+                launch(i % copies)
+            ev.record(b, sh)
+            stream.synchronize()
+            ms = ev.elapsed_ms(a, b) / n
+            ev.destroy(a)
+            ev.destroy(b)
+            return ms * 1e3
+
+        eager_us = timed(lambda c: model.step(hidden, drafts, B, K, committed, counts, stream=sh, copy=c),
+                         args.steps)
+        graphs = [binding.moe_verify_graph_create(model.ctxs[c], hidden, drafts, B, K, committed, counts, sh)
+                  for c in range(copies)]
+        try:
+            graph_us = timed(lambda c: binding.moe_verify_graph_launch(graphs[c], sh), args.steps)
+        finally:
+            for g in graphs:
+                binding.moe_verify_graph_destroy(g)
+        rows.append({"K": K, "tokens_per_step": T, "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
+                     "committed_per_seq_expected": round(sum(p ** i for i in range(K + 1)), 4),
+                     "committed_per_seq_this_input": round(float(counts.sum().item()) / B, 4)})
+    model.close()
+    for r in rows:
+        for mode in ("eager", "graph"):
+            c = r[f"{mode}_us"] / rows[0][f"{mode}_us"]
+            r[f"c_{mode}"] = round(c, 4)
+            r[f"S_{mode}"] = round(r["committed_per_seq_expected"] / c, 4)
+    print(json.dumps({"cost_model": {"workload": w0.name, "B": B, "p_accept": p, "weight_copies": copies,
+                                     "steps": args.steps, "rows": rows}}))
+
+
 # ---------------------------------------------------------------- main
 
 def main():
@@ -191,6 +258,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy 5 times (reference for HBM byte counters)")
+    ap.add_argument("--cost-model", action="store_true",
+                    help="only time the verify step for K = 0..3, eager and as a HIP graph (decode workloads)")
     args = ap.parse_args()
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -229,6 +298,12 @@ def main():
 
     copy_bytes = w.L * (w.E + w.S) * expert_bytes(w) + (w.V * w.H * 2 if w.has_lm_head else 0)
     copies = args.copies or max(1, math.ceil(1.5e9 / copy_bytes))
+    if args.cost_model:
+        if not w.has_lm_head:
+            sys.exit("--cost-model needs a decode workload")
+        # the bench's own rows (B x 4): at K = 3 the step is the benchmarked one
+        cost_model(args, w, weights, hidden_np, copies, torch, np, synth, binding, VerifyModel, to_device)
+        return
     prefill = not w.has_lm_head
     model = VerifyModel(w, weights, max_tokens=16 if prefill else w.T,
                         max_prefill_tokens=w.T if prefill else 0, copies=copies)

@@ -192,6 +192,32 @@ int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* d
 int moe_block_forward(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, void* y,
                       const moe_verify_aux* aux, void* hip_stream);
 
+/*
+ * The verify step replayed through a HIP graph.  The page "jina-ocr-v1 :
+ * Analyse de documents plus rapide sur des GPU a budget limite", section
+ * "Decodage speculatif sur un L4", finds that the verify step's fixed
+ * overhead decides the best K (CUDA graphs against eager execution); these
+ * calls let a caller run and time the step both ways.
+ * moe_verify_graph_create captures one moe_verify_step(ctx, hidden, drafts,
+ * B, K, committed, counts) enqueued on `hip_stream` into an executable graph
+ * (nothing runs; the stream may not be NULL, as the default stream cannot be
+ * captured).  Every moe_verify_graph_launch, on any stream, then runs that
+ * step on those same buffers -- their contents may change between launches,
+ * the pointers may not -- with moe_verify_step's results.  A graph belongs to
+ * its context: destroy it first, and do not let its launches overlap other
+ * calls on the context.  Timing hooks must be clear when capturing.
+ * Errors (create): those of moe_verify_step, MOE_EINVAL for a NULL `out` or
+ * stream or a timing hook that is set, MOE_ENOMEM, MOE_EHIP (capture or
+ * instantiation failed); *out is NULL on failure.  Launch: MOE_EINVAL for a
+ * NULL graph, MOE_EHIP.  Destroy accepts NULL.
+ */
+typedef struct moe_verify_graph moe_verify_graph;
+int moe_verify_graph_create(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
+                            int32_t B, int32_t K, int32_t* committed, int32_t* counts,
+                            void* hip_stream, moe_verify_graph** out);
+int moe_verify_graph_launch(moe_verify_graph* graph, void* hip_stream);
+void moe_verify_graph_destroy(moe_verify_graph* graph);
+
 /* Stages that can be bracketed by timing events. */
 #define MOE_STAGE_LMHEAD 0      /* LM head + arg-max + acceptance kernel of a verify step   */
 #define MOE_STAGE_EXPERT_UP 1   /* expert gate/up kernel of the first block of a call        */

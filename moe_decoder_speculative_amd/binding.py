@@ -16,6 +16,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libmoeverify.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_block_forward",
+            "moe_verify_graph_create", "moe_verify_graph_launch", "moe_verify_graph_destroy",
             "moe_verify_set_stage_events", "moe_verify_destroy", "moe_verify_last_error")
 MOE_STAGE_LMHEAD, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_ALL = 0, 1, 2, 3
 
@@ -67,6 +68,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_step_ex.restype = ctypes.c_int
     lib.moe_block_forward.argtypes = [vp, i32, vp, i32, vp, ctypes.POINTER(MoeVerifyAux), vp]
     lib.moe_block_forward.restype = ctypes.c_int
+    lib.moe_verify_graph_create.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, ctypes.POINTER(vp)]
+    lib.moe_verify_graph_create.restype = ctypes.c_int
+    lib.moe_verify_graph_launch.argtypes = [vp, vp]
+    lib.moe_verify_graph_launch.restype = ctypes.c_int
+    lib.moe_verify_graph_destroy.argtypes = [vp]
+    lib.moe_verify_graph_destroy.restype = None
     lib.moe_verify_set_stage_events.argtypes = [vp, i32, vp, vp]
     lib.moe_verify_set_stage_events.restype = ctypes.c_int
     lib.moe_verify_destroy.argtypes = [vp]
@@ -137,6 +144,22 @@ def moe_verify_step_ex(ctx: int, hidden, drafts, B: int, K: int, committed, coun
 def moe_block_forward(ctx: int, layer: int, x, T: int, y, aux: MoeVerifyAux | None = None, stream=None) -> None:
     _check(load_library().moe_block_forward(ctx, layer, _ptr(x), T, _ptr(y),
                                             ctypes.byref(aux) if aux is not None else None, _stream(stream)))
+
+
+def moe_verify_graph_create(ctx: int, hidden, drafts, B: int, K: int, committed, counts, stream) -> int:
+    """Capture one verify step on `stream` (not the default stream) into a graph handle."""
+    out = ctypes.c_void_p()
+    _check(load_library().moe_verify_graph_create(ctx, _ptr(hidden), _ptr(drafts), B, K, _ptr(committed),
+                                                  _ptr(counts), _stream(stream), ctypes.byref(out)))
+    return out.value
+
+
+def moe_verify_graph_launch(graph: int, stream=None) -> None:
+    _check(load_library().moe_verify_graph_launch(graph, _stream(stream)))
+
+
+def moe_verify_graph_destroy(graph: int | None) -> None:
+    load_library().moe_verify_graph_destroy(graph)
 
 
 def moe_verify_set_stage_events(ctx: int, stage: int, before: int | None, after: int | None) -> None:

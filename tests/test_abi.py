@@ -112,3 +112,15 @@ def test_binding_raises_with_message():
     with pytest.raises(B.MoeVerifyError) as ei:
         B.moe_verify_init(_cfg(hidden=3), _weights())
     assert ei.value.code == B.MOE_EINVAL and "hidden" in ei.value.message
+
+
+def test_graph_calls_reject_null_arguments():
+    lib = B.load_library()
+    out = ctypes.c_void_p(1)
+    rc = lib.moe_verify_graph_create(None, None, None, 1, 3, None, None, ctypes.c_void_p(1), ctypes.byref(out))
+    assert rc == B.MOE_EINVAL and "ctx" in B.moe_verify_last_error() and out.value is None
+    rc = lib.moe_verify_graph_create(ctypes.c_void_p(8), None, None, 1, 3, None, None, ctypes.c_void_p(1), None)
+    assert rc == B.MOE_EINVAL and "out" in B.moe_verify_last_error()
+    rc = lib.moe_verify_graph_launch(None, None)
+    assert rc == B.MOE_EINVAL and "graph" in B.moe_verify_last_error()
+    lib.moe_verify_graph_destroy(None)

@@ -254,3 +254,47 @@ def test_prefill_8pages_stack12_sampled():
         model.close()
     stats = parity.check_rows_teacher_forced(per_layer, hidden[rows], weights, shp)
     parity.say(f"[prefill_stack12] ok: {stats}")
+
+
+@pytest.mark.parametrize("which", ["small", "decode_b32_zipf"])
+def test_graph_replay_matches_eager(which):
+    """A verify step captured into a HIP graph (moe_verify_graph_create) and
+    replayed four times, with torch work, eager steps on other drafts and
+    synchronisations between the replays: every replay gives the eager step's
+    committed tokens and counts bit for bit, and those equal the oracle's."""
+    torch = _torch()
+    from moe_decoder_speculative_amd import binding as B_
+    case = workloads.build_case(workloads.small_bf16(B=5, K=3, L=2, seed_id=81)) if which == "small" \
+        else workloads.cached_case("decode_b32_zipf")
+    w = case.w
+    parity.say(f"[graph] {which}: B={w.B} K={w.K} T={w.T} entry=moe_verify_graph_create/launch")
+    model = VerifyModel(w, case.weights, max_tokens=w.T)
+    graph = None
+    try:
+        stream = torch.cuda.Stream()
+        hidden = to_device(case.hidden)
+        drafts = to_device(case.drafts.astype(np.int32))
+        wrong = to_device(np.full_like(case.drafts, w.V + 5).astype(np.int32))  # never match
+        committed, counts = model.alloc_outputs(w.B, w.K)
+        model.step(hidden, drafts, w.B, w.K, committed, counts)
+        torch.cuda.synchronize()
+        ref_c, ref_n = committed.cpu().numpy(), counts.cpu().numpy()
+        assert np.array_equal(ref_c, case.ref.committed) and np.array_equal(ref_n, case.ref.counts)
+        with torch.cuda.stream(stream):
+            graph = B_.moe_verify_graph_create(model.ctx, hidden, drafts, w.B, w.K, committed, counts, stream)
+        for rep in range(4):
+            committed.fill_(-7)
+            counts.fill_(-7)
+            torch.cuda.synchronize()
+            B_.moe_verify_graph_launch(graph, stream)
+            stream.synchronize()
+            assert np.array_equal(committed.cpu().numpy(), ref_c), f"replay {rep}: committed differs"
+            assert np.array_equal(counts.cpu().numpy(), ref_n), f"replay {rep}: counts differ"
+            # an eager step on drafts that never match, between the replays
+            model.step(hidden, wrong, w.B, w.K, committed, counts)
+            torch.cuda.synchronize()
+            assert np.all(counts.cpu().numpy() == 1)
+        parity.say(f"[graph] {which} ok: 4 replays equal the eager step")
+    finally:
+        B_.moe_verify_graph_destroy(graph)
+        model.close()
