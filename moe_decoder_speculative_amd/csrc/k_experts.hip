@@ -13,13 +13,16 @@
 // MFMAs.  The four partial sums are added through LDS.  For steps sorted by
 // the permutation kernel the slots are launched busiest first (the active
 // list is ordered by token count), so the longest workgroups do not trail
-// the kernel.
+// the kernel; the shared experts, which see every token, split their token
+// tiles over up to four workgroups (see split_index).
 //   up:   a[pair][i] = round(silu(Wg x)[i] * (Wu x)[i])        (pairs of the slot)
 //   down: y[pair][h] = (Wd a)[h]                                 (float32)
 // Shared experts occupy slots 0..S-1 and see every token.  The page "Jina AI
 // releases lightweight OCR model with built-in speculative decoding", section
 // "Lean architecture with a compressed encoder", fixes 64 routed and 2 shared
 // experts with top-6 routing; SwiGLU is this library's reading of the expert.
+#include <algorithm>
+
 #include "kernels.h"
 
 namespace moe {
@@ -58,15 +61,45 @@ __device__ __forceinline__ int slot_pair(const Dims& d, const ExpertParams& p, c
 
 // ---------------------------------------------------------------- bf16 ----
 
+// Workgroup b -> (slot, row tile r, chunk c, chunks n) for R row tiles.  The
+// shared experts see all T tokens, the most of any slot, and their workgroups
+// would run several times longer than the rest (latency-bound, one token tile
+// after another); so the first workgroups split each shared (slot, row tile)
+// `split` ways -- chunk c takes token tiles c, c + split, ... -- with the
+// chunks of one pair eight workgroups apart, i.e. on one XCD at about the
+// same time, where the weight tile they all read comes from L2.  The routed
+// slots follow, one workgroup per (slot, row tile), busiest first.  (The
+// shared part covers whole groups of 8; indices past it exit.)
+__device__ __forceinline__ void split_index(const Dims& d, int R, int b, int split, int& slot, int& r, int& c,
+                                           int& n) {
+  const int shared_wgs = (d.S * R + 7) / 8 * 8 * split;
+  if (b < shared_wgs) {
+    const int q = (b / (8 * split)) * 8 + b % 8;
+    c = (b / 8) % split;
+    n = split;
+    slot = q < d.S * R ? q / R : d.S + d.E;  // past the shared pairs: no slot
+    r = q % R;
+  } else {
+    const int q = b - shared_wgs;
+    c = 0;
+    n = 1;
+    slot = d.S + q / R;
+    r = q % R;
+  }
+}
+
 template <int KW>  // k-steps per wavefront: H / 32 / 4
-__global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p) {
+__global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int split) {
   __shared__ float red[4][2][kWave][4];
   __shared__ int pairs[kTile];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int RT = d.I / kTile, KT = d.H / kKStep;
-  const int slot = blockIdx.x / RT, rt = blockIdx.x % RT;
+  int slot, rt, c, split_;
+  split_index(d, RT, blockIdx.x, split, slot, rt, c, split_);
+  if (slot < d.S && c * kTile >= p.T) return;  // a chunk past the shared tokens
   SlotInfo si;
   if (!slot_info(d, p, slot, si)) return;
+  const int nt = (si.ntok + kTile - 1) / kTile;
 
   const int kt0 = wave * KW;
   const int64_t tile = (static_cast<int64_t>(si.expert) * RT + rt) * KT + kt0;
@@ -121,17 +154,17 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p) {
 
   int pair;
   bf16x8_t b[KW];
-  load_tile(0, pair, b);
-  if (si.ntok <= kTile) {
+  load_tile(c * kTile, pair, b);
+  if (c + split_ >= nt) {
     do_tile(pair, b);
     return;
   }
   // several token tiles: the next tile's fragments are requested before this
   // tile's MFMAs (unconditionally; past the last tile they are never used)
-  for (int tile0 = 0; tile0 < si.ntok; tile0 += kTile) {
+  for (int t = c; t < nt; t += split_) {
     int pair_n;
     bf16x8_t bn[KW];
-    load_tile(tile0 + kTile, pair_n, bn);
+    load_tile((t + split_) * kTile, pair_n, bn);
     do_tile(pair, b);
     pair = pair_n;
 #pragma unroll
@@ -140,14 +173,17 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p) {
 }
 
 template <int KW, int RPW>  // KW: k-steps per wavefront (I/32/4); RPW: row tiles per workgroup
-__global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p) {
+__global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, int split) {
   __shared__ float red[4][RPW][kWave][4];
   __shared__ int pairs[kTile];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int RB = d.H / (kTile * RPW), KT = d.I / kKStep;
-  const int slot = blockIdx.x / RB, rb = blockIdx.x % RB;
+  int slot, rb, c, split_;
+  split_index(d, RB, blockIdx.x, split, slot, rb, c, split_);
+  if (slot < d.S && c * kTile >= p.T) return;  // a chunk past the shared tokens
   SlotInfo si;
   if (!slot_info(d, p, slot, si)) return;
+  const int nt = (si.ntok + kTile - 1) / kTile;
 
   const int kt0 = wave * KW;
   bf16x8_t a[RPW][KW];
@@ -196,17 +232,17 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p) {
 
   int pair;
   bf16x8_t b[KW];
-  load_tile(0, pair, b);
-  if (si.ntok <= kTile) {
+  load_tile(c * kTile, pair, b);
+  if (c + split_ >= nt) {
     do_tile(pair, b);
     return;
   }
   // several token tiles: the next tile's fragments are requested before this
   // tile's MFMAs (unconditionally; past the last tile they are never used)
-  for (int tile0 = 0; tile0 < si.ntok; tile0 += kTile) {
+  for (int t = c; t < nt; t += split_) {
     int pair_n;
     bf16x8_t bn[KW];
-    load_tile(tile0 + kTile, pair_n, bn);
+    load_tile((t + split_) * kTile, pair_n, bn);
     do_tile(pair, b);
     pair = pair_n;
 #pragma unroll
@@ -255,22 +291,31 @@ __global__ __launch_bounds__(kBlock) void k_down_f32(Dims d, ExpertParams p) {
   }
 }
 
+// Ways to split a shared expert's T tokens over workgroups: at most two
+// token tiles per workgroup, at most four ways.
+int token_split(int T) { return std::min(4, std::max(1, (T + 2 * kTile - 1) / (2 * kTile))); }
+// grid for R row tiles: the shared part (whole groups of 8 pairs, `split`
+// ways), then one workgroup per routed (slot, row tile)
+int split_grid(const Dims& d, int R, int split) { return (d.S * R + 7) / 8 * 8 * split + d.E * R; }
+
 template <int KW>
 hipError_t up_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
-  const int grid = (d.S + d.E) * (d.I / kTile);
-  hipLaunchKernelGGL(k_up_mfma<KW>, dim3(grid), dim3(kBlock), 0, s, d, p);
+  const int split = token_split(p.T);
+  const int grid = split_grid(d, d.I / kTile, split);
+  hipLaunchKernelGGL(k_up_mfma<KW>, dim3(grid), dim3(kBlock), 0, s, d, p, split);
   return hipGetLastError();
 }
 
 template <int KW>
 hipError_t down_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
   constexpr int RPW = 2;
+  const int split = token_split(p.T);
   if ((d.H / kTile) % RPW == 0) {
-    const int grid = (d.S + d.E) * (d.H / (kTile * RPW));
-    hipLaunchKernelGGL((k_down_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p);
+    const int grid = split_grid(d, d.H / (kTile * RPW), split);
+    hipLaunchKernelGGL((k_down_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p, split);
   } else {
-    const int grid = (d.S + d.E) * (d.H / kTile);
-    hipLaunchKernelGGL((k_down_mfma<KW, 1>), dim3(grid), dim3(kBlock), 0, s, d, p);
+    const int grid = split_grid(d, d.H / kTile, split);
+    hipLaunchKernelGGL((k_down_mfma<KW, 1>), dim3(grid), dim3(kBlock), 0, s, d, p, split);
   }
   return hipGetLastError();
 }
