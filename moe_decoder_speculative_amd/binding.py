@@ -1,4 +1,5 @@
-"""Thin ctypes binding of libmoeverify.so (C ABI in include/moe_verify.h).
+"""Thin ctypes binding of libmoeverify.so (C ABI in include/moe_verify.h and
+include/moe_draft.h).
 
 The functions keep the C names.  They only marshal arguments: torch tensors
 supply device memory (data_ptr) and the HIP stream (the current torch stream
@@ -17,7 +18,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_block_forward",
             "moe_verify_graph_create", "moe_verify_graph_launch", "moe_verify_graph_destroy",
-            "moe_verify_set_stage_events", "moe_verify_destroy", "moe_verify_last_error")
+            "moe_verify_set_stage_events", "moe_verify_destroy", "moe_verify_last_error",
+            "moe_draft_init", "moe_draft_step", "moe_draft_set_stage_events", "moe_draft_destroy")
 MOE_STAGE_LMHEAD, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_ALL = 0, 1, 2, 3
 
 
@@ -44,6 +46,16 @@ class MoeVerifyWeights(ctypes.Structure):
 class MoeVerifyAux(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_w", "expert_count", "expert_offset",
                                                 "perm", "moe_out", "hidden_out", "tstar")]
+
+
+class MoeDraftConfig(ctypes.Structure):
+    _fields_ = [("inter", ctypes.c_int32), ("head_rows", ctypes.c_int32), ("max_batch", ctypes.c_int32),
+                ("k_max", ctypes.c_int32)]
+
+
+class MoeDraftWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ("embed", "gamma_h", "gamma_e", "w_proj", "gamma_f", "w_gate",
+                                                "w_up", "w_down", "gamma_o", "head", "head_ids")]
 
 
 _lib = None
@@ -80,6 +92,15 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_destroy.restype = None
     lib.moe_verify_last_error.argtypes = []
     lib.moe_verify_last_error.restype = ctypes.c_char_p
+    lib.moe_draft_init.argtypes = [vp, ctypes.POINTER(MoeDraftConfig), ctypes.POINTER(MoeDraftWeights), vp,
+                                   ctypes.POINTER(vp)]
+    lib.moe_draft_init.restype = ctypes.c_int
+    lib.moe_draft_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
+    lib.moe_draft_step.restype = ctypes.c_int
+    lib.moe_draft_set_stage_events.argtypes = [vp, i32, vp, vp]
+    lib.moe_draft_set_stage_events.restype = ctypes.c_int
+    lib.moe_draft_destroy.argtypes = [vp]
+    lib.moe_draft_destroy.restype = None
     _lib = lib
     return lib
 
@@ -169,3 +190,25 @@ def moe_verify_set_stage_events(ctx: int, stage: int, before: int | None, after:
 
 def moe_verify_destroy(ctx: int | None) -> None:
     load_library().moe_verify_destroy(ctx)
+
+
+def moe_draft_init(verifier: int, cfg: MoeDraftConfig, weights: MoeDraftWeights, stream=None) -> int:
+    """Create a draft context bound to a verifier context; returns its handle."""
+    out = ctypes.c_void_p()
+    _check(load_library().moe_draft_init(verifier, ctypes.byref(cfg), ctypes.byref(weights), _stream(stream),
+                                         ctypes.byref(out)))
+    return out.value
+
+
+def moe_draft_step(ctx: int, hidden, committed, counts, R: int, B: int, K: int, drafts, states=None,
+                   stream=None) -> None:
+    _check(load_library().moe_draft_step(ctx, _ptr(hidden), _ptr(committed), _ptr(counts), R, B, K, _ptr(drafts),
+                                         _ptr(states), _stream(stream)))
+
+
+def moe_draft_set_stage_events(ctx: int, stage: int, before: int | None, after: int | None) -> None:
+    _check(load_library().moe_draft_set_stage_events(ctx, stage, before, after))
+
+
+def moe_draft_destroy(ctx: int | None) -> None:
+    load_library().moe_draft_destroy(ctx)

@@ -12,6 +12,7 @@
 #include <string>
 #include <vector>
 
+#include "api_internal.h"
 #include "kernels.h"
 #include "moe_verify.h"
 
@@ -21,59 +22,61 @@ namespace moe {
 int lmhead_row_multiple();
 }
 
-struct moe_verify_ctx {
-  moe_verify_config cfg;
-  moe::Dims d;
-  int device = 0;
-  size_t esize = 0;         // bytes per stored element
-  int64_t tw = 0;           // workspace token capacity
-  std::vector<void*> allocs;
-
-  // repacked weights
-  char* router = nullptr;   // bf16 tiled [L][64/16][H/32][512]; f32 [L][E][H]
-  char* gate = nullptr;     // [L][E+S] experts (tiled or row-major)
-  char* up = nullptr;
-  char* down = nullptr;
-  char* gamma = nullptr;    // [L][H] storage
-  char* final_gamma = nullptr;
-  char* lm = nullptr;       // bf16 tiled [Vpad/16][H/32][512]; f32 [V][H]
-  size_t router_layer = 0, gate_layer = 0, down_layer = 0;
-
-  // workspace
-  char* xres = nullptr;     // [tw][H] storage
-  char* xhat = nullptr;     // [tw][H] storage
-  int* idx[2] = {nullptr, nullptr};   // [tw][k]
-  float* w[2] = {nullptr, nullptr};   // [tw][k]
-  int* cnt = nullptr;       // [E]
-  int* off = nullptr;       // [E+1]
-  int* perm = nullptr;      // [tw*k]
-  int* active = nullptr;    // [E]
-  int* n_active = nullptr;  // [1]
-  char* act = nullptr;      // [tw*(k+S)][I] storage
-  float* y = nullptr;       // [tw*(k+S)][H]
-  unsigned long long* keys = nullptr;  // [kKeySlots][tw]
-
-  int4* tiles = nullptr;               // grouped-GEMM tile table
-  int* n_tiles = nullptr;
-  bool gemm_ok = false;                // LDS allows the prefill grouped GEMM
-
-  // one-call timing hooks (moe_verify_set_stage_events)
-  hipEvent_t ev_before[MOE_STAGE_COUNT] = {};
-  hipEvent_t ev_after[MOE_STAGE_COUNT] = {};
-};
+namespace moe {
+namespace api {
 
 namespace {
-
 thread_local std::string g_last_error;
+}
 
 int fail(int code, const std::string& msg) {
   g_last_error = msg;
   return code;
 }
 
-bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+void clear_error() { g_last_error.clear(); }
+const char* last_error() { return g_last_error.c_str(); }
 
-hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
+int check_ptr(const void* p, const char* name, bool required) {
+  if (!p) return required ? fail(MOE_EINVAL, std::string(name) + " is NULL") : MOE_OK;
+  if (!aligned16(p)) return fail(MOE_EINVAL, std::string(name) + " is not 16-byte aligned");
+  return MOE_OK;
+}
+
+int dev_alloc(std::vector<void*>& allocs, size_t bytes, char** out) {
+  void* p = nullptr;
+  if (bytes == 0) bytes = 16;
+  if (std::getenv("MOE_VERIFY_FAULT") && std::strcmp(std::getenv("MOE_VERIFY_FAULT"), "alloc") == 0)
+    return fail(MOE_ENOMEM, "device allocation failed (injected by MOE_VERIFY_FAULT=alloc)");
+  const hipError_t e = hipMalloc(&p, bytes);
+  if (e != hipSuccess) {
+    (void)hipGetLastError();
+    return fail(MOE_ENOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
+  }
+  allocs.push_back(p);
+  *out = static_cast<char*>(p);
+  return MOE_OK;
+}
+
+void dev_free_all(std::vector<void*>& allocs, int device) {
+  if (allocs.empty()) return;
+  int cur = 0;
+  if (hipGetDevice(&cur) == hipSuccess && cur != device) (void)hipSetDevice(device);
+  (void)hipDeviceSynchronize();
+  for (void* p : allocs) (void)hipFree(p);
+  allocs.clear();
+  if (cur != device) (void)hipSetDevice(cur);
+}
+
+}  // namespace api
+}  // namespace moe
+
+namespace {
+
+using moe::api::aligned16;
+using moe::api::check_ptr;
+using moe::api::fail;
+using moe::api::mark;
 
 // Token rows from which a block's experts run as grouped GEMMs on LDS-staged
 // MFMA tiles instead of the weight-streaming decode kernels.
@@ -82,12 +85,6 @@ constexpr int kGemmMinTokens = 512;
 void clear_hooks(moe_verify_ctx* c) {
   for (int i = 0; i < MOE_STAGE_COUNT; ++i) c->ev_before[i] = c->ev_after[i] = nullptr;
 }
-
-#define MOE_HIP(expr)                                                                        \
-  do {                                                                                       \
-    hipError_t e_ = (expr);                                                                  \
-    if (e_ != hipSuccess) return fail(MOE_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
-  } while (0)
 
 int validate_config(const moe_verify_config& c) {
   auto bad = [](const std::string& m) { return fail(MOE_EINVAL, "config: " + m); };
@@ -126,12 +123,6 @@ int validate_weights(const moe_verify_config& c, const moe_verify_weights& w) {
   return MOE_OK;
 }
 
-int check_ptr(const void* p, const char* name, bool required) {
-  if (!p) return required ? fail(MOE_EINVAL, std::string(name) + " is NULL") : MOE_OK;
-  if (!aligned16(p)) return fail(MOE_EINVAL, std::string(name) + " is not 16-byte aligned");
-  return MOE_OK;
-}
-
 int check_aux(const moe_verify_aux* a) {
   if (!a) return MOE_OK;
   int r;
@@ -146,20 +137,7 @@ int check_aux(const moe_verify_aux* a) {
   return MOE_OK;
 }
 
-int ctx_alloc(moe_verify_ctx* c, size_t bytes, char** out) {
-  void* p = nullptr;
-  if (bytes == 0) bytes = 16;
-  if (std::getenv("MOE_VERIFY_FAULT") && std::strcmp(std::getenv("MOE_VERIFY_FAULT"), "alloc") == 0)
-    return fail(MOE_ENOMEM, "device allocation failed (injected by MOE_VERIFY_FAULT=alloc)");
-  const hipError_t e = hipMalloc(&p, bytes);
-  if (e != hipSuccess) {
-    (void)hipGetLastError();
-    return fail(MOE_ENOMEM, "hipMalloc of " + std::to_string(bytes) + " bytes failed: " + hipGetErrorString(e));
-  }
-  c->allocs.push_back(p);
-  *out = static_cast<char*>(p);
-  return MOE_OK;
-}
+int ctx_alloc(moe_verify_ctx* c, size_t bytes, char** out) { return moe::api::dev_alloc(c->allocs, bytes, out); }
 
 template <typename P>
 int ctx_alloc_t(moe_verify_ctx* c, size_t bytes, P** out) {
@@ -171,13 +149,7 @@ int ctx_alloc_t(moe_verify_ctx* c, size_t bytes, P** out) {
 
 void ctx_free(moe_verify_ctx* c) {
   if (!c) return;
-  if (!c->allocs.empty()) {
-    int cur = 0;
-    if (hipGetDevice(&cur) == hipSuccess && cur != c->device) (void)hipSetDevice(c->device);
-    (void)hipDeviceSynchronize();
-    for (void* p : c->allocs) (void)hipFree(p);
-    if (cur != c->device) (void)hipSetDevice(cur);
-  }
+  moe::api::dev_free_all(c->allocs, c->device);
   delete c;
 }
 
@@ -485,13 +457,13 @@ int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* weig
     r = fail(MOE_ENOMEM, "host exception during init");
   }
   if (r != MOE_OK) {
-    const std::string keep = g_last_error;
+    const std::string keep = moe::api::last_error();
     ctx_free(c);
-    g_last_error = keep;
+    fail(r, keep);
     return r;
   }
   *out = c;
-  g_last_error.clear();
+  moe::api::clear_error();
   return MOE_OK;
 }
 
@@ -615,6 +587,6 @@ int moe_verify_set_stage_events(moe_verify_ctx* ctx, int32_t stage, void* before
 
 void moe_verify_destroy(moe_verify_ctx* ctx) { ctx_free(ctx); }
 
-const char* moe_verify_last_error(void) { return g_last_error.c_str(); }
+const char* moe_verify_last_error(void) { return moe::api::last_error(); }
 
 }  // extern "C"

@@ -1,0 +1,83 @@
+// Internals shared by the C ABI sources (api.cpp: verify step; api_draft.cpp:
+// draft head): the verify context, error reporting and argument checks.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <string>
+#include <vector>
+
+#include "kernels.h"
+#include "moe_verify.h"
+
+struct moe_verify_ctx {
+  moe_verify_config cfg;
+  moe::Dims d;
+  int device = 0;
+  size_t esize = 0;         // bytes per stored element
+  int64_t tw = 0;           // workspace token capacity
+  std::vector<void*> allocs;
+
+  // repacked weights
+  char* router = nullptr;   // bf16 tiled [L][64/16][H/32][512]; f32 [L][E][H]
+  char* gate = nullptr;     // [L][E+S] experts (tiled or row-major)
+  char* up = nullptr;
+  char* down = nullptr;
+  char* gamma = nullptr;    // [L][H] storage
+  char* final_gamma = nullptr;
+  char* lm = nullptr;       // bf16 tiled [Vpad/16][H/32][512]; f32 [V][H]
+  size_t router_layer = 0, gate_layer = 0, down_layer = 0;
+
+  // workspace
+  char* xres = nullptr;     // [tw][H] storage
+  char* xhat = nullptr;     // [tw][H] storage
+  int* idx[2] = {nullptr, nullptr};   // [tw][k]
+  float* w[2] = {nullptr, nullptr};   // [tw][k]
+  int* cnt = nullptr;       // [E]
+  int* off = nullptr;       // [E+1]
+  int* perm = nullptr;      // [tw*k]
+  int* active = nullptr;    // [E]
+  int* n_active = nullptr;  // [1]
+  char* act = nullptr;      // [tw*(k+S)][I] storage
+  float* y = nullptr;       // [tw*(k+S)][H]
+  unsigned long long* keys = nullptr;  // [kKeySlots][tw]
+
+  int4* tiles = nullptr;               // grouped-GEMM tile table
+  int* n_tiles = nullptr;
+  bool gemm_ok = false;                // LDS allows the prefill grouped GEMM
+
+  // one-call timing hooks (moe_verify_set_stage_events)
+  hipEvent_t ev_before[MOE_STAGE_COUNT] = {};
+  hipEvent_t ev_after[MOE_STAGE_COUNT] = {};
+};
+
+namespace moe {
+namespace api {
+
+// Record `msg` as the calling thread's last error and return `code`.
+int fail(int code, const std::string& msg);
+void clear_error();
+const char* last_error();
+
+inline bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+// NULL (an error when required) or 16-byte aligned.
+int check_ptr(const void* p, const char* name, bool required);
+
+inline hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecord(ev, s) : hipSuccess; }
+
+// hipMalloc recorded in `allocs` (freed by the owner); MOE_ENOMEM on failure.
+int dev_alloc(std::vector<void*>& allocs, size_t bytes, char** out);
+
+// Synchronise `device` and free every allocation in `allocs`.
+void dev_free_all(std::vector<void*>& allocs, int device);
+
+}  // namespace api
+}  // namespace moe
+
+#define MOE_HIP(expr)                                                                                  \
+  do {                                                                                                 \
+    hipError_t e_ = (expr);                                                                            \
+    if (e_ != hipSuccess) return ::moe::api::fail(MOE_EHIP, std::string(#expr) + ": " + hipGetErrorString(e_)); \
+  } while (0)

@@ -137,6 +137,40 @@ hipError_t launch_final_norm(const Dims& d, const LmHeadParams& p, hipStream_t s
 hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s);  // keys only
 hipError_t launch_accept(const LmHeadParams& p, hipStream_t s);  // picks + acceptance, keys cleared
 
+// Draft head row kernels (one 256-thread workgroup per sequence; d.H <= 2048).
+// Row layouts: x holds [2][B][H] (normalised state rows, then normalised
+// token-embedding rows: the projection's two slots), yp [2][B][H] their
+// projections, y [Sf][B][H] the FFN slots' outputs.
+struct DraftParams {
+  int B, R, V, Vd, K;
+  int step;                    // 0-based step of this launch
+  int last;                    // 1: the final step (no next-step inputs are written)
+  int Sf;                      // FFN slots
+  const bf16_t* hidden;        // [B][R][H] (k_draft_in)
+  const int* committed;        // [B][R] (k_draft_in)
+  const int* counts;           // [B] or null (k_draft_in)
+  const bf16_t* embed;         // [V][H]
+  const bf16_t* gamma_h;
+  const bf16_t* gamma_e;
+  const bf16_t* gamma_f;
+  const bf16_t* gamma_o;
+  bf16_t* x;                   // [2][B][H]
+  const float* yp;             // [2][B][H]
+  bf16_t* u;                   // [B][H]
+  bf16_t* uh;                  // [B][H] FFN input
+  const float* y;              // [Sf][B][H]
+  bf16_t* xf;                  // [B][H] head input
+  bf16_t* states;              // [K][B][H] or null
+  unsigned long long* keys;    // [kKeySlots][key_stride]
+  int key_stride;
+  const int* head_ids;         // [Vd] or null (row = token)
+  int* drafts;                 // [B][K]
+};
+hipError_t launch_draft_in(const Dims& d, const DraftParams& p, hipStream_t s);
+hipError_t launch_draft_mid(const Dims& d, const DraftParams& p, hipStream_t s);
+hipError_t launch_draft_out(const Dims& d, const DraftParams& p, hipStream_t s);
+hipError_t launch_draft_pick(const Dims& d, const DraftParams& p, hipStream_t s);
+
 // Weight repacking.  Tiled layout of an [R][C] bf16 matrix (R padded to Rpad
 // with zero rows): tile (rt, kt) of 16 rows x 32 columns is 512 contiguous
 // elements in which lane l of a wavefront owns the 8 elements of row
@@ -144,5 +178,9 @@ hipError_t launch_accept(const LmHeadParams& p, hipStream_t s);  // picks + acce
 // 16x16x32 MFMA, so a wavefront loads a tile with one coalesced 1 KiB read.
 hipError_t launch_tile_bf16(const bf16_t* src, int64_t src_mat_stride, bf16_t* dst,
                             int64_t n_mats, int R, int C, int Rpad, hipStream_t s);
+// The same for matrices whose rows are `ld` elements apart (column slices of a
+// wider matrix); ld and src_mat_stride are multiples of 8.
+hipError_t launch_tile_bf16_ld(const bf16_t* src, int64_t src_mat_stride, int64_t ld, bf16_t* dst,
+                               int64_t n_mats, int R, int C, int Rpad, hipStream_t s);
 
 }  // namespace moe

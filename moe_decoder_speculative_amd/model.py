@@ -127,3 +127,43 @@ class VerifyModel:
             self.close()
         except Exception:
             pass
+
+
+class DraftModel:
+    """A draft-head context bound to a VerifyModel's context (sharing its LM
+    head when the draft head has no rows of its own)."""
+
+    def __init__(self, verifier: VerifyModel, Id: int, dweights: dict, max_batch: int, k_max: int = 7,
+                 device="cuda", stream=None):
+        torch = _torch()
+        self.verifier = verifier
+        self.device = device
+        self.H = verifier.w.H
+        names = ("embed", "gamma_h", "gamma_e", "w_proj", "gamma_f", "w_gate", "w_up", "w_down", "gamma_o")
+        t = {k: to_device(dweights[k], device) for k in names}
+        own_head = "head_ids" in dweights
+        head = to_device(dweights["head"], device) if own_head else None
+        ids = to_device(np.asarray(dweights["head_ids"], np.int32), device) if own_head else None
+        cfg = B_.MoeDraftConfig(inter=Id, head_rows=len(dweights["head_ids"]) if own_head else 0,
+                                max_batch=max_batch, k_max=k_max)
+        wts = B_.MoeDraftWeights(**{k: t[k].data_ptr() for k in names},
+                                 head=head.data_ptr() if own_head else None,
+                                 head_ids=ids.data_ptr() if own_head else None)
+        torch.cuda.synchronize()
+        self.ctx = B_.moe_draft_init(verifier.ctx, cfg, wts, stream)
+        del t, head, ids
+        torch.cuda.synchronize()
+
+    def step(self, hidden, committed, counts, R: int, B: int, K: int, drafts, states=None, stream=None):
+        B_.moe_draft_step(self.ctx, hidden, committed, counts, R, B, K, drafts, states, stream)
+
+    def close(self):
+        if getattr(self, "ctx", None):
+            B_.moe_draft_destroy(self.ctx)
+        self.ctx = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -295,3 +295,93 @@ def make_drafts(w: Workload, tstar_bk1: np.ndarray, u=None, r=None) -> np.ndarra
     if w.drafts == "independent":
         return np.where(u < w.accept_p, correct, wrong_token(correct, r)).astype(np.int32)
     raise ValueError(f"workload {w.name} has no drafts")
+
+
+# --------------------------------------------------------------------------
+# draft head
+# --------------------------------------------------------------------------
+
+@dataclass(frozen=True)
+class DraftWorkload:
+    """A draft-head workload on top of a verify workload, whose hidden size,
+    vocabulary and LM head it shares.
+
+    The pages fix one dense block applied recursively for K = 3 steps ("Jina
+    AI releases lightweight OCR model with built-in speculative decoding",
+    section "Speculative decoding without accuracy loss") but not its width:
+    Id = (k + S) * I = 7168, the SwiGLU width a verifier block activates per
+    token, is this library's reading.  head_rows = 0 drafts over the whole
+    vocabulary; a positive value restricts the draft head to that many rows
+    (a seeded subset of token ids)."""
+
+    name: str
+    base: str
+    Id: int
+    head_rows: int
+    B: int
+    K: int
+    R: int          # verifier rows per sequence handed to the draft (K + 1)
+    seed_id: int
+
+    @property
+    def weight_seed(self) -> int:
+        return 5000 + self.seed_id
+
+    @property
+    def input_seed(self) -> int:
+        return 6000 + self.seed_id
+
+    def with_(self, **kw) -> "DraftWorkload":
+        return replace(self, **kw)
+
+
+DRAFT_WORKLOADS = {
+    "draft_b1": DraftWorkload("draft_b1", "decode_b1", Id=7168, head_rows=0, B=1, K=3, R=4, seed_id=1),
+    "draft_b32": DraftWorkload("draft_b32", "decode_b32_zipf", Id=7168, head_rows=0, B=32, K=3, R=4, seed_id=2),
+    "draft_b1_head32k": DraftWorkload("draft_b1_head32k", "decode_b1", Id=7168, head_rows=32768, B=1, K=3, R=4,
+                                      seed_id=3),
+}
+
+DRAFT_GAIN_SPREAD = 0.1
+
+
+def gen_draft_weights(dw: DraftWorkload, base: Workload, lm_head: np.ndarray) -> dict:
+    """Seeded draft-head weights in the base workload's storage type.
+
+    embed [V, H], w_proj [H, 2H], w_gate / w_up [Id, H], w_down [H, Id] are
+    N(0, 0.02^2); the four RMSNorm gains are 1 + U(-0.1, 0.1) (distinct, so a
+    gain used in the wrong place shows); head is lm_head itself or its rows
+    head_ids (a sorted seeded subset)."""
+    H, V, Id = base.H, base.V, dw.Id
+    ch = np.random.SeedSequence(dw.weight_seed).spawn(10)
+
+    def normal(c, shape):
+        vals = _rng(c).standard_normal(int(np.prod(shape)), dtype=np.float32)
+        vals *= np.float32(WEIGHT_STD)
+        return to_storage(vals.reshape(shape), base.dtype)
+
+    def gain(c):
+        return to_storage((1.0 + DRAFT_GAIN_SPREAD * _rng(c).uniform(-1, 1, H)).astype(np.float32), base.dtype)
+
+    out = dict(embed=normal(ch[0], (V, H)), gamma_h=gain(ch[1]), gamma_e=gain(ch[2]), gamma_f=gain(ch[3]),
+               gamma_o=gain(ch[4]), w_proj=normal(ch[5], (H, 2 * H)), w_gate=normal(ch[6], (Id, H)),
+               w_up=normal(ch[7], (Id, H)), w_down=normal(ch[8], (H, Id)))
+    if dw.head_rows > 0:
+        ids = np.sort(_rng(ch[9]).choice(V, size=dw.head_rows, replace=False)).astype(np.int32)
+        out["head"] = np.ascontiguousarray(lm_head[ids])
+        out["head_ids"] = ids
+    else:
+        out["head"] = lm_head
+    return out
+
+
+def draft_inputs(dw: DraftWorkload, base: Workload, B: int | None = None):
+    """What a draft call continues from: hidden [B*R, H] N(0, 1) rows in the
+    storage type, committed [B, R] token ids uniform over [0, V), counts [B]
+    uniform over 1..R."""
+    B = dw.B if B is None else B
+    g = _rng(np.random.SeedSequence(dw.input_seed))
+    hidden = to_storage(g.standard_normal((B * dw.R, base.H), dtype=np.float32), base.dtype)
+    committed = g.integers(0, base.V, size=(B, dw.R)).astype(np.int32)
+    counts = g.integers(1, dw.R + 1, size=B).astype(np.int32)
+    return hidden, committed, counts

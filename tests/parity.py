@@ -191,3 +191,46 @@ def check_stack_teacher_forced(out: dict, case, margin: float = 1e-3, slack: flo
     return (f"moe_out rel err {worst_m:.2e}; undecided top-k rows {undecided}, undecided picks "
             f"{int((~decided).sum())}; rows on the oracle's exact trajectory {exact_traj_rows}/{len(ts)}; "
             f"picks equal to the oracle's own step {same_tokens}/{len(ts)}; committed {int(counts.sum())}")
+
+
+def check_draft_teacher_forced(drafts, states, hidden, committed, counts, R: int, dw: dict, dshp,
+                               margin: float = 2e-3, slack: float = 2e-3) -> str:
+    """K draft steps, step by step on the GPU's own trajectory.
+
+    drafts [B, K] and states [K, B, H] are the GPU's tokens and step outputs;
+    hidden [B*R, H], committed [B, R] and counts [B] (or None) what the call
+    continued from.  The oracle runs step 1 from the same start and step j+1
+    from the GPU's step-j output and token: each step output within the
+    storage tolerance; each token equal to the oracle's where the oracle's
+    top-two logit margin is >= margin, elsewhere a row whose logit is within
+    slack of the maximum."""
+    from oracle import draft_oracle as D
+    from oracle import moe_oracle as O
+    h, t = D.continue_from_verify(hidden, committed, counts, R)
+    B, K = drafts.shape
+    ids = dw.get("head_ids")
+    worst, undecided, equal_traj = 0.0, 0, 0
+    for j in range(K):
+        ref = D.draft_block(h, t, dw, dshp)
+        err = rowwise_rel_err(states[j], ref.v)
+        assert err.max() <= REL_TOL[dshp.dtype], f"step {j + 1}: state rel err {err.max():.3e}"
+        worst = max(worst, float(err.max()))
+        equal_traj += int(np.sum(np.all(states[j] == ref.v, axis=1)))
+        tok = drafts[:, j]
+        if ids is None:
+            assert np.all((tok >= 0) & (tok < dshp.Vd)), f"step {j + 1}: a token outside the head"
+            rows = tok.astype(np.int64)
+        else:
+            rows = np.searchsorted(ids, tok)
+            assert np.all(rows < len(ids)) and np.array_equal(ids[np.minimum(rows, len(ids) - 1)], tok), \
+                f"step {j + 1}: a token that is not one of the head's ids"
+        am = O.argmax_margin(ref.logits)
+        decided = am >= margin
+        assert np.array_equal(tok[decided], ref.tokens[decided]), \
+            f"step {j + 1}: tokens differ on decided rows {np.where(decided & (tok != ref.tokens))[0]}"
+        lg = ref.logits
+        assert np.all(lg[np.arange(B), rows] >= lg.max(1) - slack), f"step {j + 1}: a pick is not within slack"
+        undecided += int((~decided).sum())
+        h, t = states[j], tok
+    return (f"{K} steps x {B} rows: state rel err {worst:.2e}; states equal to the oracle's bit for bit "
+            f"{equal_traj}/{K * B}; undecided picks {undecided}")

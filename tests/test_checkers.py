@@ -52,3 +52,59 @@ def test_rows_teacher_forced_rejects(plant):
         g["topk_idx"][t, -1] = unused
     with pytest.raises(AssertionError):
         parity.check_rows_teacher_forced(per, x0, weights, shp)
+
+
+# ------------------------------------------------------------ draft head ----
+
+def _draft_case(head_rows=0, B=9, K=3):
+    from oracle import draft_oracle as D
+    base = workloads.small_bf16(B=B, K=K, L=1, seed_id=91)
+    dwl = synth.DraftWorkload("draft_chk", base.name, Id=384, head_rows=head_rows, B=B, K=K, R=K + 1, seed_id=91)
+    lm = synth.gen_weights(base)["lm_head"]
+    dw = synth.gen_draft_weights(dwl, base, lm)
+    dshp = D.DraftShape(H=base.H, Id=dwl.Id, V=base.V, Vd=head_rows or base.V, dtype="bf16")
+    hidden, committed, counts = synth.draft_inputs(dwl, base)
+    h0, t0 = D.continue_from_verify(hidden, committed, counts, dwl.R)
+    ch = D.draft_chain(h0, t0, K, dw, dshp)
+    states = np.stack([s.v for s in ch.states])
+    return dict(drafts=ch.drafts.copy(), states=states, hidden=hidden, committed=committed, counts=counts,
+                R=dwl.R, dw=dw, dshp=dshp, chain=ch)
+
+
+@pytest.mark.parametrize("head_rows", [0, 200])
+def test_draft_checker_accepts_the_oracle(head_rows):
+    c = _draft_case(head_rows)
+    msg = parity.check_draft_teacher_forced(c["drafts"], c["states"], c["hidden"], c["committed"], c["counts"],
+                                            c["R"], c["dw"], c["dshp"])
+    assert "undecided" in msg
+
+
+@pytest.mark.parametrize("plant", ["state_scale", "token", "reset", "not_an_id", "start_row"])
+def test_draft_checker_rejects(plant):
+    from oracle import moe_oracle as O
+    c = _draft_case(head_rows=200 if plant == "not_an_id" else 0)
+    drafts, states, counts = c["drafts"], c["states"], c["counts"]
+    if plant == "state_scale":
+        states[1, 2] *= 1.05
+    elif plant == "token":
+        # the best-separated pick of step 2 replaced by another token
+        lg = c["chain"].states[1].logits
+        b = int(np.argmax(O.argmax_margin(lg)))
+        drafts[b, 1] = (drafts[b, 1] + 1) % c["dshp"].Vd
+    elif plant == "reset":
+        # every step restarted from the verifier's state (no hidden-state feedback)
+        states[1] = states[0]
+        states[2] = states[0]
+        drafts[:, 1] = drafts[:, 0]
+        drafts[:, 2] = drafts[:, 0]
+    elif plant == "not_an_id":
+        ids = c["dw"]["head_ids"]
+        drafts[0, 0] = np.setdiff1d(np.arange(c["dshp"].V), ids)[0]
+    else:
+        # continuing from the last row instead of the row of the last committed token
+        counts = np.full_like(counts, c["R"])
+        if np.array_equal(counts, c["counts"]):
+            pytest.skip("every sequence committed all rows")
+    with pytest.raises(AssertionError):
+        parity.check_draft_teacher_forced(drafts, states, c["hidden"], c["committed"], counts, c["R"], c["dw"],
+                                          c["dshp"])
