@@ -14,6 +14,11 @@ the timed region.  Several independent weight copies are rotated so that no
 weight byte of a step is served by the 256 MB last-level cache from an earlier
 step.
 
+The draft-head workloads (draft_b1, draft_b32, draft_b1_head32k) time one
+moe_draft_step instead: K recursive applications of the dense draft block
+for B sequences, reported as draft tokens per second (B*K per call) with the
+draft's LM-head kernel against the HBM roofline.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
 """
 from __future__ import annotations
@@ -33,6 +38,7 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0           # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA, published
 METRIC = "verified tokens/s per MoE verify step (B×4 tokens); % HBM or MFMA peak"
+DRAFT_METRIC = "draft tokens/s per draft call (B×K tokens, K recursive dense-block steps); % HBM peak"
 EVERY = 8
 EXPERT_BYTES = None  # filled per workload
 
@@ -102,6 +108,23 @@ def step_flops(w) -> int:
 def lmhead_bytes(w) -> int:
     # weights once + final-norm activations in + one 8-byte key per token
     return w.V * w.H * 2 + w.T * w.H * 2 + w.T * 8
+
+
+def draft_head_bytes(H, Vd, B) -> int:
+    # head rows once + head-input rows in + one 8-byte key per row
+    return Vd * H * 2 + B * H * 2 + B * 8
+
+
+def draft_call_bytes(H, Id, Vd, B, K) -> int:
+    """Bytes one draft call must move: per step the projection (2H x H), the
+    dense SwiGLU (3 x Id x H) and the head rows, plus the rows it reads and
+    writes (state and embedding rows, the drafts)."""
+    per_step = 2 * H * H * 2 + 3 * Id * H * 2 + draft_head_bytes(H, Vd, B) + 2 * B * H * 2
+    return K * per_step + B * H * 2 + B * K * 4
+
+
+def draft_call_flops(H, Id, Vd, B, K) -> int:
+    return K * B * 2 * (2 * H * H + 3 * Id * H + Vd * H)
 
 
 # ------------------------------------------------------------ counter file
@@ -187,10 +210,26 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
     one-token steps, K = 0 being plain greedy decoding) and the speed-up over
     greedy decoding S_K = tau_K / c_K (the pages' c = tau / S, page "jina-ocr-v1 :
     Analyse de documents plus rapide sur des GPU a budget limite", section
-    "Decodage speculatif sur un L4")."""
+    "Decodage speculatif sur un L4").
+
+    When a draft workload is defined on this verify workload, the draft call
+    (K recursive dense-block steps, continuing from the step's own rows and
+    counts) is timed the same two ways, and so is the whole decode-loop
+    iteration, verify then draft on one stream: c_loop_K = t_loop_K / t_0 and
+    S_loop_K = tau_K / c_loop_K are the figures that compare with the pages'
+    (their c includes the draft head).  The drafts of random weights are never
+    accepted, so tau_K is the expected count at acceptance p, not this run's."""
+    from moe_decoder_speculative_amd.model import DraftModel
     B = w0.B
     p = w0.accept_p
     model = VerifyModel(w0, weights, max_tokens=B * 4, copies=copies)
+    dname = next((n for n, d in synth.DRAFT_WORKLOADS.items() if d.base == w0.name and d.head_rows == 0), None)
+    dms = []
+    if dname:
+        dwl = synth.DRAFT_WORKLOADS[dname]
+        dw = synth.gen_draft_weights(dwl, w0, weights["lm_head"])
+        dms = [DraftModel(model, dwl.Id, dw, max_batch=B, k_max=3, copy=c) for c in range(copies)]
+        del dw
     stream = torch.cuda.Stream()
     sh = stream.cuda_stream
     ev = HipEvents()
@@ -230,17 +269,175 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
         finally:
             for g in graphs:
                 binding.moe_verify_graph_destroy(g)
-        rows.append({"K": K, "tokens_per_step": T, "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
-                     "committed_per_seq_expected": round(sum(p ** i for i in range(K + 1)), 4),
-                     "committed_per_seq_this_input": round(float(counts.sum().item()) / B, 4)})
+        row = {"K": K, "tokens_per_step": T, "eager_us": round(eager_us, 2), "graph_us": round(graph_us, 2),
+               "committed_per_seq_expected": round(sum(p ** i for i in range(K + 1)), 4),
+               "committed_per_seq_this_input": round(float(counts.sum().item()) / B, 4)}
+        if dms and K > 0:
+            row["draft_eager_us"] = round(timed(lambda c: dms[c].step(hidden, committed, counts, K + 1, B, K, drafts,
+                                                                      stream=sh), args.steps), 2)
+            graphs = [binding.moe_verify_graph_create(model.ctxs[c], hidden, drafts, B, K, committed, counts, sh)
+                      for c in range(copies)]
+            dgraphs = [binding.moe_draft_graph_create(dms[c].ctx, hidden, committed, counts, K + 1, B, K, drafts,
+                                                      None, sh) for c in range(copies)]
+            try:
+                row["draft_graph_us"] = round(timed(lambda c: binding.moe_verify_graph_launch(dgraphs[c], sh),
+                                                    args.steps), 2)
+
+                def loop_eager(c):
+                    model.step(hidden, drafts, B, K, committed, counts, stream=sh, copy=c)
+                    dms[c].step(hidden, committed, counts, K + 1, B, K, drafts, stream=sh)
+
+                def loop_graph(c):
+                    binding.moe_verify_graph_launch(graphs[c], sh)
+                    binding.moe_verify_graph_launch(dgraphs[c], sh)
+
+                row["loop_eager_us"] = round(timed(loop_eager, args.steps), 2)
+                row["loop_graph_us"] = round(timed(loop_graph, args.steps), 2)
+            finally:
+                for g in graphs + dgraphs:
+                    binding.moe_verify_graph_destroy(g)
+        elif dms:
+            row["loop_eager_us"], row["loop_graph_us"] = row["eager_us"], row["graph_us"]
+        rows.append(row)
+    for d in dms:
+        d.close()
     model.close()
     for r in rows:
         for mode in ("eager", "graph"):
             c = r[f"{mode}_us"] / rows[0][f"{mode}_us"]
             r[f"c_{mode}"] = round(c, 4)
             r[f"S_{mode}"] = round(r["committed_per_seq_expected"] / c, 4)
+            if dms:
+                cl = r[f"loop_{mode}_us"] / rows[0][f"{mode}_us"]
+                r[f"c_loop_{mode}"] = round(cl, 4)
+                r[f"S_loop_{mode}"] = round(r["committed_per_seq_expected"] / cl, 4)
     print(json.dumps({"cost_model": {"workload": w0.name, "B": B, "p_accept": p, "weight_copies": copies,
-                                     "steps": args.steps, "rows": rows}}))
+                                     "draft_workload": dname, "steps": args.steps, "rows": rows}}))
+
+
+# ---------------------------------------------------------------- draft head
+
+def cpu_baseline_draft(dwl, base, dw, hidden_np, committed_np, counts_np, seconds: float):
+    """The draft oracle, as it stands, on the same B rows (whole draft calls)."""
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = 1
+    from oracle import draft_oracle as D
+    dshp = D.DraftShape(H=base.H, Id=dwl.Id, V=base.V, Vd=dwl.head_rows or base.V, dtype=base.dtype)
+    h0, t0 = D.continue_from_verify(hidden_np, committed_np, counts_np, dwl.R)
+    t_start = time.perf_counter()
+    n = 0
+    while True:
+        D.draft_chain(h0, t0, dwl.K, dw, dshp)
+        n += 1
+        el = time.perf_counter() - t_start
+        if el >= seconds:
+            break
+    return {"value": n * dwl.B * dwl.K / el, "unit": "draft tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{n} oracle draft calls of {dwl.B} sequence(s) x {dwl.K} steps in {el:.1f} s "
+                      f"(numpy float32, BLAS threads {threads})"}
+
+
+def bench_draft(args, name, torch, np, synth, binding, VerifyModel, to_device):
+    from moe_decoder_speculative_amd.model import DraftModel
+    dwl = synth.DRAFT_WORKLOADS[name]
+    # the verifier context only lends the LM head: one block is enough
+    base = synth.WORKLOADS[dwl.base].with_(L=1)
+    B, K, H, V = dwl.B, dwl.K, base.H, base.V
+    Vd = dwl.head_rows or V
+    log(f"draft workload {name}: B={B} K={K} R={dwl.R} H={H} Id={dwl.Id} V={V} head rows={Vd}")
+    t = time.time()
+    weights = synth.gen_weights(base)
+    dw = synth.gen_draft_weights(dwl, base, weights["lm_head"])
+    hidden_np, committed_np, counts_np = synth.draft_inputs(dwl, base)
+    log(f"generated weights in {time.time() - t:.1f}s")
+    cbytes = draft_call_bytes(H, dwl.Id, Vd, B, K)
+    # distinct weight bytes one call reads (the head is read once per step,
+    # but from the same rows) decide how many copies keep calls out of the LLC
+    distinct = 2 * H * H * 2 + 3 * dwl.Id * H * 2 + Vd * H * 2
+    copies = args.copies or max(1, math.ceil(1.5e9 / distinct))
+    vm = VerifyModel(base, weights, max_tokens=base.T, copies=copies)
+    dms = [DraftModel(vm, dwl.Id, dw, max_batch=B, k_max=K, copy=c) for c in range(copies)]
+    log(f"{copies} draft/verifier copies")
+    hidden = to_device(hidden_np)
+    committed = to_device(committed_np)
+    counts = to_device(counts_np)
+    drafts = torch.empty((B, K), dtype=torch.int32, device="cuda")
+
+    def run(c):
+        dms[c].step(hidden, committed, counts, dwl.R, B, K, drafts)
+
+    ev = HipEvents()
+    stream = torch.cuda.current_stream().cuda_stream
+    for i in range(args.warmup):
+        run(i % copies)
+    torch.cuda.synchronize()
+    n = args.steps
+    sampled = list(range(0, n, EVERY))
+    before = [ev.create() for _ in sampled]
+    after = [ev.create() for _ in sampled]
+    g0, g1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev.record(g0, stream)
+    for i in range(n):
+        c = i % copies
+        if i % EVERY == 0:
+            binding.moe_draft_set_stage_events(dms[c].ctx, binding.MOE_STAGE_LMHEAD, before[i // EVERY],
+                                               after[i // EVERY])
+        run(c)
+    ev.record(g1, stream)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_call = (t1 - t0) * 1e3 / n
+    gpu_ms_call = ev.elapsed_ms(g0, g1) / n
+    kern_ms = sorted(ev.elapsed_ms(b, a) for b, a in zip(before, after))
+    kern_avg_ms = sum(kern_ms) / len(kern_ms)
+    for e in before + after + [g0, g1]:
+        ev.destroy(e)
+    kname = "k_lmhead_stream" if B <= 16 else ("k_lmhead_wide" if B <= 128 else "k_lmhead_mfma")
+    kbytes = draft_head_bytes(H, Vd, B)
+    achieved = kbytes / (kern_avg_ms * 1e-3) / 1e9
+    roof = {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": achieved / HBM_PEAK_GBS, "traffic": traffic_from_profiles("k_lmhead.hip", name),
+            "kernel": kname, "bytes_per_launch": kbytes, "avg_us": kern_avg_ms * 1e3,
+            "median_us": kern_ms[len(kern_ms) // 2] * 1e3, "launches_timed": len(kern_ms)}
+    cflops = draft_call_flops(H, dwl.Id, Vd, B, K)
+    step = {"gpu_ms_per_call": gpu_ms_call, "algorithmic_bytes": cbytes,
+            "hbm_frac": cbytes / (ms_call * 1e-3) / (HBM_PEAK_GBS * 1e9), "flops": cflops,
+            "mfma_frac": cflops / (ms_call * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
+            "drafts_first_sequence": drafts[0].cpu().tolist()}
+    res = {
+        "metric": DRAFT_METRIC,
+        "value": B * K / (ms_call * 1e-3),
+        "unit": "draft tokens/s",
+        "n_gpus": 1,
+        "steps": n,
+        "warmup": args.warmup,
+        "ms_per_step": ms_call,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": name, "B": B, "K": K, "rows_per_sequence": dwl.R, "hidden": H,
+                   "draft_inter": dwl.Id, "vocab": V, "draft_head_rows": Vd, "weight_copies": copies},
+        "roofline": roof,
+        "step": step,
+    }
+    for d in dms:
+        d.close()
+    vm.close()
+    torch.cuda.synchronize()
+    if not args.no_cpu_baseline:
+        log("timing the CPU oracle on a bounded sample")
+        res["cpu_baseline"] = cpu_baseline_draft(dwl, base, dw, hidden_np, committed_np, counts_np,
+                                                 args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
 
 
 # ---------------------------------------------------------------- main
@@ -252,7 +449,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b1",
                     choices=["decode_b1", "decode_b32_zipf", "stack12_b32_zipf", "prefill_8pages",
-                             "prefill_8pages_stack12"])
+                             "prefill_8pages_stack12", "draft_b1", "draft_b32", "draft_b1_head32k"])
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for 1.5 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -286,6 +483,9 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "dispatches": 5}))
+        return
+    if args.workload in synth.DRAFT_WORKLOADS:
+        bench_draft(args, args.workload, torch, np, synth, binding, VerifyModel, to_device)
         return
     w = synth.WORKLOADS[args.workload]
     log(f"workload {w.name}: B={w.B} K={w.K} T={w.T} L={w.L} H={w.H} E={w.E} k={w.k} S={w.S} I={w.I} V={w.V}")

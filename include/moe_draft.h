@@ -123,6 +123,22 @@ int moe_draft_step(moe_draft_ctx* ctx, const void* hidden, const int32_t* commit
                    int32_t R, int32_t B, int32_t K, int32_t* drafts, void* states, void* hip_stream);
 
 /*
+ * One moe_draft_step(ctx, hidden, committed, counts, R, B, K, drafts, states)
+ * enqueued on `hip_stream` captured into an executable graph, run with
+ * moe_verify_graph_launch and freed with moe_verify_graph_destroy (the same
+ * handle type as a captured verify step; semantics and errors as
+ * moe_verify_graph_create: the buffers are fixed, their contents may change
+ * between launches; destroy the graph before the context).  The draft call is
+ * K * 7 + 1 launches, so it is the call whose fixed launch cost a graph
+ * replay would save, if any (page "jina-ocr-v1 : Analyse de documents plus
+ * rapide sur des GPU a budget limite", section "Decodage speculatif sur un
+ * L4", on graphs against eager execution).
+ */
+int moe_draft_graph_create(moe_draft_ctx* ctx, const void* hidden, const int32_t* committed, const int32_t* counts,
+                           int32_t R, int32_t B, int32_t K, int32_t* drafts, void* states, void* hip_stream,
+                           moe_verify_graph** out);
+
+/*
  * Timing hook of the next moe_draft_step on `ctx` (as
  * moe_verify_set_stage_events): MOE_STAGE_LMHEAD brackets the first step's
  * head kernel, MOE_STAGE_EXPERT_UP / MOE_STAGE_EXPERT_DOWN the first step's

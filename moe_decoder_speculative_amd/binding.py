@@ -19,7 +19,8 @@ MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_block_forward",
             "moe_verify_graph_create", "moe_verify_graph_launch", "moe_verify_graph_destroy",
             "moe_verify_set_stage_events", "moe_verify_destroy", "moe_verify_last_error",
-            "moe_draft_init", "moe_draft_step", "moe_draft_set_stage_events", "moe_draft_destroy")
+            "moe_draft_init", "moe_draft_step", "moe_draft_graph_create", "moe_draft_set_stage_events",
+            "moe_draft_destroy")
 MOE_STAGE_LMHEAD, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_ALL = 0, 1, 2, 3
 
 
@@ -97,6 +98,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_draft_init.restype = ctypes.c_int
     lib.moe_draft_step.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp]
     lib.moe_draft_step.restype = ctypes.c_int
+    lib.moe_draft_graph_create.argtypes = [vp, vp, vp, vp, i32, i32, i32, vp, vp, vp, ctypes.POINTER(vp)]
+    lib.moe_draft_graph_create.restype = ctypes.c_int
     lib.moe_draft_set_stage_events.argtypes = [vp, i32, vp, vp]
     lib.moe_draft_set_stage_events.restype = ctypes.c_int
     lib.moe_draft_destroy.argtypes = [vp]
@@ -204,6 +207,16 @@ def moe_draft_step(ctx: int, hidden, committed, counts, R: int, B: int, K: int, 
                    stream=None) -> None:
     _check(load_library().moe_draft_step(ctx, _ptr(hidden), _ptr(committed), _ptr(counts), R, B, K, _ptr(drafts),
                                          _ptr(states), _stream(stream)))
+
+
+def moe_draft_graph_create(ctx: int, hidden, committed, counts, R: int, B: int, K: int, drafts, states,
+                           stream) -> int:
+    """Capture one draft call on `stream` into a graph handle (launch / destroy
+    with moe_verify_graph_launch / moe_verify_graph_destroy)."""
+    out = ctypes.c_void_p()
+    _check(load_library().moe_draft_graph_create(ctx, _ptr(hidden), _ptr(committed), _ptr(counts), R, B, K,
+                                                 _ptr(drafts), _ptr(states), _stream(stream), ctypes.byref(out)))
+    return out.value
 
 
 def moe_draft_set_stage_events(ctx: int, stage: int, before: int | None, after: int | None) -> None:

@@ -8,6 +8,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <functional>
 #include <new>
 #include <string>
 #include <vector>
@@ -55,6 +56,37 @@ int dev_alloc(std::vector<void*>& allocs, size_t bytes, char** out) {
   }
   allocs.push_back(p);
   *out = static_cast<char*>(p);
+  return MOE_OK;
+}
+
+int capture_graph(void* hip_stream, const std::function<int()>& enqueue, moe_verify_graph** out) {
+  *out = nullptr;
+  if (!hip_stream) return fail(MOE_EINVAL, "capture needs a stream other than the default stream");
+  hipStream_t s = static_cast<hipStream_t>(hip_stream);
+  const hipError_t eb = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+  if (eb != hipSuccess) return fail(MOE_EHIP, std::string("hipStreamBeginCapture: ") + hipGetErrorString(eb));
+  const int r = enqueue();
+  hipGraph_t graph = nullptr;
+  const hipError_t e = hipStreamEndCapture(s, &graph);
+  if (r != MOE_OK || e != hipSuccess) {
+    if (graph) (void)hipGraphDestroy(graph);
+    return r != MOE_OK ? r : fail(MOE_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
+  }
+  hipGraphExec_t exec = nullptr;
+  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
+  if (ei != hipSuccess) {
+    (void)hipGraphDestroy(graph);
+    return fail(MOE_EHIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(ei));
+  }
+  moe_verify_graph* g = new (std::nothrow) moe_verify_graph;
+  if (!g) {
+    (void)hipGraphExecDestroy(exec);
+    (void)hipGraphDestroy(graph);
+    return fail(MOE_ENOMEM, "graph handle");
+  }
+  g->graph = graph;
+  g->exec = exec;
+  *out = g;
   return MOE_OK;
 }
 
@@ -481,45 +513,17 @@ int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* d
   return r;
 }
 
-struct moe_verify_graph {
-  hipGraph_t graph = nullptr;
-  hipGraphExec_t exec = nullptr;
-};
-
 int moe_verify_graph_create(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B,
                             int32_t K, int32_t* committed, int32_t* counts, void* hip_stream,
                             moe_verify_graph** out) {
   if (!out) return fail(MOE_EINVAL, "out is NULL");
   *out = nullptr;
   if (!ctx) return fail(MOE_EINVAL, "ctx is NULL");
-  if (!hip_stream) return fail(MOE_EINVAL, "capture needs a stream other than the default stream");
   for (int i = 0; i < MOE_STAGE_COUNT; ++i)
     if (ctx->ev_before[i] || ctx->ev_after[i]) return fail(MOE_EINVAL, "a timing hook is set; clear it first");
-  hipStream_t s = static_cast<hipStream_t>(hip_stream);
-  MOE_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-  const int r = step_impl(ctx, hidden, drafts, B, K, committed, counts, nullptr, hip_stream);
-  hipGraph_t graph = nullptr;
-  const hipError_t e = hipStreamEndCapture(s, &graph);
-  if (r != MOE_OK || e != hipSuccess) {
-    if (graph) (void)hipGraphDestroy(graph);
-    return r != MOE_OK ? r : fail(MOE_EHIP, std::string("hipStreamEndCapture: ") + hipGetErrorString(e));
-  }
-  hipGraphExec_t exec = nullptr;
-  const hipError_t ei = hipGraphInstantiate(&exec, graph, nullptr, nullptr, 0);
-  if (ei != hipSuccess) {
-    (void)hipGraphDestroy(graph);
-    return fail(MOE_EHIP, std::string("hipGraphInstantiate: ") + hipGetErrorString(ei));
-  }
-  moe_verify_graph* g = new (std::nothrow) moe_verify_graph;
-  if (!g) {
-    (void)hipGraphExecDestroy(exec);
-    (void)hipGraphDestroy(graph);
-    return fail(MOE_ENOMEM, "graph handle");
-  }
-  g->graph = graph;
-  g->exec = exec;
-  *out = g;
-  return MOE_OK;
+  return moe::api::capture_graph(
+      hip_stream, [&]() { return step_impl(ctx, hidden, drafts, B, K, committed, counts, nullptr, hip_stream); },
+      out);
 }
 
 int moe_verify_graph_launch(moe_verify_graph* graph, void* hip_stream) {

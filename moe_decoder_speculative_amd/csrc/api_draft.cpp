@@ -311,6 +311,19 @@ int moe_draft_step(moe_draft_ctx* ctx, const void* hidden, const int32_t* commit
   return r;
 }
 
+int moe_draft_graph_create(moe_draft_ctx* ctx, const void* hidden, const int32_t* committed, const int32_t* counts,
+                           int32_t R, int32_t B, int32_t K, int32_t* drafts, void* states, void* hip_stream,
+                           moe_verify_graph** out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!ctx) return fail(MOE_EINVAL, "draft ctx is NULL");
+  for (int i = 0; i < MOE_STAGE_COUNT; ++i)
+    if (ctx->ev_before[i] || ctx->ev_after[i]) return fail(MOE_EINVAL, "a timing hook is set; clear it first");
+  return moe::api::capture_graph(
+      hip_stream,
+      [&]() { return step_impl(ctx, hidden, committed, counts, R, B, K, drafts, states, hip_stream); }, out);
+}
+
 int moe_draft_set_stage_events(moe_draft_ctx* ctx, int32_t stage, void* before, void* after) {
   if (!ctx) return fail(MOE_EINVAL, "draft ctx is NULL");
   if (stage < 0 || stage >= MOE_STAGE_COUNT) return fail(MOE_EINVAL, "stage out of range");

@@ -5,6 +5,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <functional>
 #include <string>
 #include <vector>
 
@@ -52,6 +53,12 @@ struct moe_verify_ctx {
   hipEvent_t ev_after[MOE_STAGE_COUNT] = {};
 };
 
+// An instantiated HIP graph of one captured call (verify step or draft call).
+struct moe_verify_graph {
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+};
+
 namespace moe {
 namespace api {
 
@@ -69,6 +76,10 @@ inline hipError_t mark(hipEvent_t ev, hipStream_t s) { return ev ? hipEventRecor
 
 // hipMalloc recorded in `allocs` (freed by the owner); MOE_ENOMEM on failure.
 int dev_alloc(std::vector<void*>& allocs, size_t bytes, char** out);
+
+// Capture what `enqueue` launches on `hip_stream` (not the default stream)
+// into an instantiated graph; *out is NULL on failure.
+int capture_graph(void* hip_stream, const std::function<int()>& enqueue, moe_verify_graph** out);
 
 // Synchronise `device` and free every allocation in `allocs`.
 void dev_free_all(std::vector<void*>& allocs, int device);

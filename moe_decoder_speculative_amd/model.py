@@ -134,7 +134,7 @@ class DraftModel:
     head when the draft head has no rows of its own)."""
 
     def __init__(self, verifier: VerifyModel, Id: int, dweights: dict, max_batch: int, k_max: int = 7,
-                 device="cuda", stream=None):
+                 device="cuda", stream=None, copy: int = 0):
         torch = _torch()
         self.verifier = verifier
         self.device = device
@@ -150,7 +150,7 @@ class DraftModel:
                                  head=head.data_ptr() if own_head else None,
                                  head_ids=ids.data_ptr() if own_head else None)
         torch.cuda.synchronize()
-        self.ctx = B_.moe_draft_init(verifier.ctx, cfg, wts, stream)
+        self.ctx = B_.moe_draft_init(verifier.ctxs[copy], cfg, wts, stream)
         del t, head, ids
         torch.cuda.synchronize()
 

@@ -127,3 +127,21 @@ def test_graph_calls_reject_null_arguments():
     rc = lib.moe_verify_graph_launch(None, None)
     assert rc == B.MOE_EINVAL and "graph" in B.moe_verify_last_error()
     lib.moe_verify_graph_destroy(None)
+
+
+def test_draft_calls_reject_null_arguments():
+    lib = B.load_library()
+    out = ctypes.c_void_p(99)
+    cfg = B.MoeDraftConfig(inter=256, head_rows=0, max_batch=4, k_max=3)
+    w = B.MoeDraftWeights(**{n: FAKE for n, _ in B.MoeDraftWeights._fields_})
+    assert lib.moe_draft_init(None, ctypes.byref(cfg), ctypes.byref(w), None, ctypes.byref(out)) == B.MOE_EINVAL
+    assert out.value is None
+    assert lib.moe_draft_step(None, FAKE, FAKE, None, 4, 1, 3, FAKE, None, None) == B.MOE_EINVAL
+    assert "NULL" in B.moe_verify_last_error()
+    assert lib.moe_draft_graph_create(None, FAKE, FAKE, None, 4, 1, 3, FAKE, None, FAKE, None) == B.MOE_EINVAL
+    g = ctypes.c_void_p(5)
+    assert lib.moe_draft_graph_create(None, FAKE, FAKE, None, 4, 1, 3, FAKE, None, FAKE, ctypes.byref(g)) == \
+        B.MOE_EINVAL
+    assert g.value is None
+    assert lib.moe_draft_set_stage_events(None, 0, None, None) == B.MOE_EINVAL
+    lib.moe_draft_destroy(None)

@@ -160,3 +160,47 @@ def test_draft_full_size(name):
         parity.say(f"[draft full] {name} ok: {msg}")
     finally:
         s.close()
+
+
+def test_draft_graph_replay_matches_eager():
+    """A captured draft call replayed four times, with eager calls of the same
+    context between the replays: every replay equals the eager result bit for
+    bit."""
+    torch = _torch()
+    from moe_decoder_speculative_amd import binding
+    base, dwl = _small(1280, 0, seed=55)
+    B, K, R = 12, 3, 4
+    parity.say(f"[draft graph] B={B} K={K} R={R} entry=moe_draft_graph_create/moe_verify_graph_launch")
+    s = _Setup(base, dwl, max_batch=B)
+    g = None
+    try:
+        hidden, committed, counts = _inputs(s, B, R, seed=5)
+        h = to_device(hidden)
+        c = to_device(committed)
+        n = to_device(counts)
+        ref_d = torch.full((B, K), -7, dtype=torch.int32, device="cuda")
+        ref_s = torch.empty((K, B, base.H), dtype=torch.bfloat16, device="cuda")
+        s.dm.step(h, c, n, R, B, K, ref_d, ref_s)
+        torch.cuda.synchronize()
+        stream = torch.cuda.Stream()
+        gd = torch.full((B, K), -7, dtype=torch.int32, device="cuda")
+        gs = torch.zeros((K, B, base.H), dtype=torch.bfloat16, device="cuda")
+        torch.cuda.synchronize()
+        g = binding.moe_draft_graph_create(s.dm.ctx, h, c, n, R, B, K, gd, gs, stream)
+        other_d = torch.empty_like(ref_d)
+        for rep in range(4):
+            gd.fill_(-7)
+            gs.zero_()
+            torch.cuda.synchronize()
+            binding.moe_verify_graph_launch(g, stream)
+            stream.synchronize()
+            assert torch.equal(gd, ref_d), f"replay {rep}: drafts differ"
+            assert torch.equal(gs, ref_s), f"replay {rep}: states differ"
+            s.dm.step(h, c, n, R, B, K, other_d)
+            torch.cuda.synchronize()
+            assert torch.equal(other_d, ref_d)
+        parity.say(f"[draft graph] ok: 4 replays equal to eager, drafts[0] {ref_d[0].tolist()}")
+    finally:
+        if g:
+            binding.moe_verify_graph_destroy(g)
+        s.close()
