@@ -213,8 +213,8 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
     "Decodage speculatif sur un L4").
 
     When a draft workload is defined on this verify workload, the draft call
-    (K recursive dense-block steps, continuing from the step's own rows and
-    counts) is timed the same two ways, and so is the whole decode-loop
+    of the same batch and shapes (K recursive dense-block steps, continuing
+    from the step's own rows and counts) is timed the same two ways, and so is the whole decode-loop
     iteration, verify then draft on one stream: c_loop_K = t_loop_K / t_0 and
     S_loop_K = tau_K / c_loop_K are the figures that compare with the pages'
     (their c includes the draft head).  The drafts of random weights are never
@@ -223,7 +223,10 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
     B = w0.B
     p = w0.accept_p
     model = VerifyModel(w0, weights, max_tokens=B * 4, copies=copies)
-    dname = next((n for n, d in synth.DRAFT_WORKLOADS.items() if d.base == w0.name and d.head_rows == 0), None)
+    # the draft workload of the same batch and shapes (whole-vocabulary head unless --draft names one)
+    dname = args.draft or next((n for n, d in synth.DRAFT_WORKLOADS.items()
+                                if d.B == B and d.head_rows == 0 and synth.WORKLOADS[d.base].H == w0.H
+                                and synth.WORKLOADS[d.base].V == w0.V), None)
     dms = []
     if dname:
         dwl = synth.DRAFT_WORKLOADS[dname]
@@ -449,7 +452,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b1",
                     choices=["decode_b1", "decode_b32_zipf", "stack12_b32_zipf", "prefill_8pages",
-                             "prefill_8pages_stack12", "draft_b1", "draft_b32", "draft_b1_head32k"])
+                             "prefill_8pages_stack12", "stack12_b1", "draft_b1", "draft_b32", "draft_b1_head32k"])
+    ap.add_argument("--draft", default=None, help="draft workload of the cost model (default: same B, whole head)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for 1.5 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")

@@ -98,6 +98,8 @@ WORKLOADS = {
                                has_lm_head=False, seed_id=4),
     # 12 blocks with residual between them, then the LM head
     "stack12_b32_zipf": _verify("stack12_b32_zipf", 5, B=32, L=12, routing="zipf"),
+    # batch 1 through the 12 blocks + LM head (the decode-loop cost model's verifier)
+    "stack12_b1": _verify("stack12_b1", 7, B=1, L=12),
     # the 8-page prefill through the same 12-block stack (no LM head)
     "prefill_8pages_stack12": Workload("prefill_8pages_stack12", H=1280, E=64, k=6, S=2, I=896,
                                        V=129280, L=12, B=0, K=0, T=8 * (1156 + 64),
