@@ -83,6 +83,12 @@ typedef struct moe_verify_ctx moe_verify_ctx;
  *   rms_eps    RMSNorm epsilon, > 0
  *   dtype      MOE_DTYPE_F32 or MOE_DTYPE_BF16 (storage of every tensor)
  *   has_lm_head 1: verify steps available; 0: only moe_block_forward
+ *   n_heads    0: the blocks are MoE-FFN only (moe_verify_step); otherwise
+ *              every layer is attention then MoE (moe_verify_step_kv) with
+ *              n_heads heads of 128 (hidden == 128 * n_heads), bf16 only
+ *   max_positions  KV-cache positions per sequence, 8..32768 (attention only)
+ *   max_seqs   KV-cache sequences, 1..1024 (attention only)
+ *   rope_theta rotary base, > 0 (attention only)
  */
 typedef struct moe_verify_config {
   int32_t hidden;
@@ -98,6 +104,10 @@ typedef struct moe_verify_config {
   float rms_eps;
   int32_t dtype;
   int32_t has_lm_head;
+  int32_t n_heads;
+  int32_t max_positions;
+  int32_t max_seqs;
+  float rope_theta;
 } moe_verify_config;
 
 /*
@@ -109,6 +119,8 @@ typedef struct moe_verify_config {
  *   norm_gamma  [L][H]   pre-block RMSNorm gains
  *   final_gamma [H]      final RMSNorm gain (NULL when has_lm_head == 0)
  *   lm_head     [V][H]   (NULL when has_lm_head == 0)
+ *   attn_gamma  [L][H]   pre-attention RMSNorm gains        (NULL when n_heads == 0)
+ *   w_q, w_k, w_v, w_o   [L][H][H] attention projections    (NULL when n_heads == 0)
  * moe_verify_init copies them (repacked); no pointer is kept afterwards.
  */
 typedef struct moe_verify_weights {
@@ -122,6 +134,11 @@ typedef struct moe_verify_weights {
   const void* norm_gamma;
   const void* final_gamma;
   const void* lm_head;
+  const void* attn_gamma;
+  const void* w_q;
+  const void* w_k;
+  const void* w_v;
+  const void* w_o;
 } moe_verify_weights;
 
 /*
@@ -136,6 +153,8 @@ typedef struct moe_verify_weights {
  *   moe_out       float [L][T][H]  block output before the residual add
  *   hidden_out    storage [T][H]   residual stream after the last block
  *   tstar         int32 [T]        greedy pick after each position
+ *   attn_out      storage [L][T][H] each layer's attention-sublayer output
+ *                 x + W_o attn (moe_verify_step_kv only)
  */
 typedef struct moe_verify_aux {
   int32_t* topk_idx;
@@ -146,6 +165,7 @@ typedef struct moe_verify_aux {
   float* moe_out;
   void* hidden_out;
   int32_t* tstar;
+  void* attn_out;
 } moe_verify_aux;
 
 /*
@@ -169,12 +189,45 @@ int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* weig
  *   committed device out, int32 [B][K+1]: accepted picks, then -1 padding
  *   counts    device out, int32 [B]: tokens committed, 1..K+1 (K+1 means all
  *             drafts matched and the last token is the bonus)
- * Requires has_lm_head; 1 <= B; 0 <= K <= k_max; B*(K+1) <= max_tokens.
- * Asynchronous; allocates nothing.
+ * Requires has_lm_head and n_heads == 0; 1 <= B; 0 <= K <= k_max;
+ * B*(K+1) <= max_tokens.  Asynchronous; allocates nothing.
  */
 int moe_verify_step(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
                     int32_t B, int32_t K, int32_t* committed, int32_t* counts,
                     void* hip_stream);
+
+/*
+ * The verify step of a context with attention (n_heads > 0): every layer is
+ * x <- x + W_o Attn(RMSNorm(x; attn_gamma)) then the MoE block.  Attention is
+ * multi-head (heads of 128) with the rotary embedding of dimension pairs
+ * (2i, 2i+1) by pos * rope_theta^(-2i/128) and a KV cache: sequence b uses
+ * cache slot b; its K+1 positions sit at positions[b] .. positions[b]+K, their
+ * keys and values are written there, and position j attends to cache entries
+ * 0 .. positions[b]+j (scores q.k / sqrt(128), softmax in float32).  After
+ * the step the caller advances positions[b] by counts[b]: the entries of the
+ * accepted tokens stay valid and those of rejected drafts are overwritten by
+ * the next step.  The pages give no attention internals; this is the
+ * library's reading of the decoder on the page "Jina AI releases lightweight
+ * OCR model with built-in speculative decoding", section "Lean architecture
+ * with a compressed encoder" (12 layers, 32,768 positions).
+ *   positions device, int32 [B]: 0 <= positions[b] <= max_positions - (K+1)
+ *             (other values give unspecified results, never an access
+ *             outside the cache)
+ * Other arguments as moe_verify_step_ex; requires B <= max_seqs and
+ * K+1 <= max_positions.  Asynchronous; allocates nothing.
+ */
+int moe_verify_step_kv(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
+                       const int32_t* positions, int32_t B, int32_t K, int32_t* committed,
+                       int32_t* counts, const moe_verify_aux* aux, void* hip_stream);
+
+/*
+ * The context's KV cache (n_heads > 0): *k_cache and *v_cache receive device
+ * pointers to bfloat16 [L][max_seqs][n_heads][max_positions][128] arrays
+ * (rotated keys; values), zero after init.  The caller may write the entries
+ * of earlier positions (a prompt's keys and values) with ordinary copies on
+ * the context's stream.  Errors: MOE_EINVAL (NULL arguments, no attention).
+ */
+int moe_verify_kv_cache(moe_verify_ctx* ctx, void** k_cache, void** v_cache);
 
 /* moe_verify_step plus the optional outputs in `aux` (aux may be NULL). */
 int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,

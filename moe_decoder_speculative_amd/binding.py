@@ -16,7 +16,8 @@ LIB_PATH = os.path.join(_HERE, "lib", "libmoeverify.so")
 
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
-EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_block_forward",
+EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_verify_step_kv",
+            "moe_verify_kv_cache", "moe_block_forward",
             "moe_verify_graph_create", "moe_verify_graph_launch", "moe_verify_graph_destroy",
             "moe_verify_set_stage_events", "moe_verify_destroy", "moe_verify_last_error",
             "moe_draft_init", "moe_draft_step", "moe_draft_graph_create", "moe_draft_set_stage_events",
@@ -36,17 +37,20 @@ class MoeVerifyConfig(ctypes.Structure):
                 ("n_shared", ctypes.c_int32), ("inter", ctypes.c_int32), ("vocab", ctypes.c_int32),
                 ("n_layers", ctypes.c_int32), ("max_tokens", ctypes.c_int32),
                 ("max_prefill_tokens", ctypes.c_int32), ("k_max", ctypes.c_int32),
-                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("has_lm_head", ctypes.c_int32)]
+                ("rms_eps", ctypes.c_float), ("dtype", ctypes.c_int32), ("has_lm_head", ctypes.c_int32),
+                ("n_heads", ctypes.c_int32), ("max_positions", ctypes.c_int32), ("max_seqs", ctypes.c_int32),
+                ("rope_theta", ctypes.c_float)]
 
 
 class MoeVerifyWeights(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("router", "w_gate", "w_up", "w_down", "s_gate", "s_up",
-                                                "s_down", "norm_gamma", "final_gamma", "lm_head")]
+                                                "s_down", "norm_gamma", "final_gamma", "lm_head", "attn_gamma",
+                                                "w_q", "w_k", "w_v", "w_o")]
 
 
 class MoeVerifyAux(ctypes.Structure):
     _fields_ = [(n, ctypes.c_void_p) for n in ("topk_idx", "topk_w", "expert_count", "expert_offset",
-                                                "perm", "moe_out", "hidden_out", "tstar")]
+                                                "perm", "moe_out", "hidden_out", "tstar", "attn_out")]
 
 
 class MoeDraftConfig(ctypes.Structure):
@@ -79,6 +83,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_step.restype = ctypes.c_int
     lib.moe_verify_step_ex.argtypes = [vp, vp, vp, i32, i32, vp, vp, ctypes.POINTER(MoeVerifyAux), vp]
     lib.moe_verify_step_ex.restype = ctypes.c_int
+    lib.moe_verify_step_kv.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, ctypes.POINTER(MoeVerifyAux), vp]
+    lib.moe_verify_step_kv.restype = ctypes.c_int
+    lib.moe_verify_kv_cache.argtypes = [vp, ctypes.POINTER(vp), ctypes.POINTER(vp)]
+    lib.moe_verify_kv_cache.restype = ctypes.c_int
     lib.moe_block_forward.argtypes = [vp, i32, vp, i32, vp, ctypes.POINTER(MoeVerifyAux), vp]
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_verify_graph_create.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, ctypes.POINTER(vp)]
@@ -163,6 +171,20 @@ def moe_verify_step_ex(ctx: int, hidden, drafts, B: int, K: int, committed, coun
     _check(load_library().moe_verify_step_ex(ctx, _ptr(hidden), _ptr(drafts), B, K, _ptr(committed),
                                              _ptr(counts), ctypes.byref(aux) if aux is not None else None,
                                              _stream(stream)))
+
+
+def moe_verify_step_kv(ctx: int, hidden, drafts, positions, B: int, K: int, committed, counts,
+                       aux: MoeVerifyAux | None = None, stream=None) -> None:
+    _check(load_library().moe_verify_step_kv(ctx, _ptr(hidden), _ptr(drafts), _ptr(positions), B, K,
+                                             _ptr(committed), _ptr(counts),
+                                             ctypes.byref(aux) if aux is not None else None, _stream(stream)))
+
+
+def moe_verify_kv_cache(ctx: int) -> tuple[int, int]:
+    """Device addresses of the key and value caches ([L][seqs][heads][P][128] bf16)."""
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    _check(load_library().moe_verify_kv_cache(ctx, ctypes.byref(k), ctypes.byref(v)))
+    return k.value, v.value
 
 
 def moe_block_forward(ctx: int, layer: int, x, T: int, y, aux: MoeVerifyAux | None = None, stream=None) -> None:

@@ -135,6 +135,14 @@ int validate_config(const moe_verify_config& c) {
   if (!(c.rms_eps > 0.0f) || !std::isfinite(c.rms_eps)) return bad("rms_eps must be a positive finite number");
   if (c.has_lm_head != 0 && c.has_lm_head != 1) return bad("has_lm_head must be 0 or 1");
   if (c.has_lm_head && (c.vocab < 1 || c.vocab > (1 << 24))) return bad("vocab must be in [1, 2^24]");
+  if (c.n_heads < 0) return bad("n_heads must be >= 0");
+  if (c.n_heads > 0) {
+    if (c.dtype != MOE_DTYPE_BF16) return fail(MOE_EUNSUPPORTED, "config: attention needs bfloat16 storage");
+    if (c.hidden != c.n_heads * moe::kHeadDim) return bad("hidden must be 128 * n_heads");
+    if (c.max_positions < 8 || c.max_positions > 32768) return bad("max_positions must be in [8, 32768]");
+    if (c.max_seqs < 1 || c.max_seqs > 1024) return bad("max_seqs must be in [1, 1024]");
+    if (!(c.rope_theta > 0.0f) || !std::isfinite(c.rope_theta)) return bad("rope_theta must be a positive finite number");
+  }
   return MOE_OK;
 }
 
@@ -146,6 +154,8 @@ int validate_weights(const moe_verify_config& c, const moe_verify_weights& w) {
       {w.s_up, "s_up", c.n_shared > 0}, {w.s_down, "s_down", c.n_shared > 0},
       {w.norm_gamma, "norm_gamma", true}, {w.final_gamma, "final_gamma", c.has_lm_head != 0},
       {w.lm_head, "lm_head", c.has_lm_head != 0},
+      {w.attn_gamma, "attn_gamma", c.n_heads > 0}, {w.w_q, "w_q", c.n_heads > 0},
+      {w.w_k, "w_k", c.n_heads > 0},   {w.w_v, "w_v", c.n_heads > 0}, {w.w_o, "w_o", c.n_heads > 0},
   };
   for (const Item& it : items) {
     if (!it.required) continue;
@@ -166,6 +176,7 @@ int check_aux(const moe_verify_aux* a) {
   if ((r = check_ptr(a->moe_out, "aux.moe_out", false))) return r;
   if ((r = check_ptr(a->hidden_out, "aux.hidden_out", false))) return r;
   if ((r = check_ptr(a->tstar, "aux.tstar", false))) return r;
+  if ((r = check_ptr(a->attn_out, "aux.attn_out", false))) return r;
   return MOE_OK;
 }
 
@@ -229,6 +240,23 @@ int repack(moe_verify_ctx* c, const moe_verify_weights& w, hipStream_t s) {
   }
   MOE_HIP(hipMemcpyAsync(c->gamma, w.norm_gamma, L * H * es, hipMemcpyDeviceToDevice, s));
   if (g.has_lm_head) MOE_HIP(hipMemcpyAsync(c->final_gamma, w.final_gamma, H * es, hipMemcpyDeviceToDevice, s));
+  if (g.n_heads > 0) {
+    MOE_HIP(hipMemcpyAsync(c->attn_gamma, w.attn_gamma, L * H * es, hipMemcpyDeviceToDevice, s));
+    const void* qkv[3] = {w.w_q, w.w_k, w.w_v};
+    for (int64_t l = 0; l < L; ++l) {
+      for (int m = 0; m < 3; ++m)
+        MOE_HIP(moe::launch_tile_bf16(static_cast<const bf16_t*>(qkv[m]) + l * H * H, 0,
+                                      reinterpret_cast<bf16_t*>(c->wqkv) + (l * 3 + m) * H * H, 1, (int)H, (int)H,
+                                      (int)H, s));
+      MOE_HIP(moe::launch_tile_bf16(static_cast<const bf16_t*>(w.w_o) + l * H * H, 0,
+                                    reinterpret_cast<bf16_t*>(c->wo) + l * H * H, 1, (int)H, (int)H, (int)H, s));
+    }
+    float inv[moe::kHeadDim / 2];
+    for (int i = 0; i < moe::kHeadDim / 2; ++i)
+      inv[i] = static_cast<float>(std::pow(static_cast<double>(g.rope_theta), -2.0 * i / moe::kHeadDim));
+    MOE_HIP(hipMemcpyAsync(c->inv_freq, inv, sizeof(inv), hipMemcpyHostToDevice, s));
+    MOE_HIP(hipStreamSynchronize(s));  // `inv` is a host stack array
+  }
   return MOE_OK;
 }
 
@@ -292,6 +320,33 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
     return r;
   if ((r = ctx_alloc_t(c, 16, &c->n_tiles))) return r;
 
+  if (g.n_heads > 0) {
+    d.L = g.n_layers;
+    c->dq = d;
+    c->dq.E = 0;
+    c->dq.k = 0;
+    c->dq.S = 3;
+    c->dq.I = g.hidden;
+    c->dout = c->dq;
+    c->dout.S = 1;
+    const size_t cache = static_cast<size_t>(L) * g.max_seqs * g.n_heads * g.max_positions * moe::kHeadDim * 2;
+    const int G = 64;
+    if ((r = ctx_alloc(c, L * H * es, &c->attn_gamma))) return r;
+    if ((r = ctx_alloc(c, L * 3 * H * H * es, &c->wqkv))) return r;
+    if ((r = ctx_alloc(c, L * H * H * es, &c->wo))) return r;
+    if ((r = ctx_alloc_t(c, 64 * sizeof(float), &c->inv_freq))) return r;
+    if ((r = ctx_alloc(c, cache, &c->kcache))) return r;
+    if ((r = ctx_alloc(c, cache, &c->vcache))) return r;
+    MOE_HIP(hipMemsetAsync(c->kcache, 0, cache, s));
+    MOE_HIP(hipMemsetAsync(c->vcache, 0, cache, s));
+    if ((r = ctx_alloc(c, g.max_tokens * H * es, &c->xattn))) return r;
+    if ((r = ctx_alloc(c, g.max_tokens * H * es, &c->qbuf))) return r;
+    if ((r = ctx_alloc(c, g.max_tokens * H * es, &c->actx))) return r;
+    if ((r = ctx_alloc_t(c, moe::attn_part_floats(g.max_tokens, g.n_heads, G) * sizeof(float), &c->apart))) return r;
+    if ((r = ctx_alloc_t(c, 16, &c->zero))) return r;
+    MOE_HIP(hipMemsetAsync(c->zero, 0, 16, s));
+  }
+
   // arg-max keys are zero between steps (the acceptance clears them after use)
   MOE_HIP(hipMemsetAsync(c->keys, 0, moe::kKeySlots * tw * sizeof(unsigned long long), s));
 
@@ -302,18 +357,101 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
 
 // The blocks of a step: for layer l, norm+router (with the combine of layer
 // l-1 when l > 0), permutation, expert up, expert down.
+// The attention sublayer of layer l (verify steps of a context with
+// attention): pre-attention RMSNorm (after the combine of the previous
+// layer's MoE block when li > 0), q/k/v projection with the rotary embedding
+// and the cache writes, decode attention, output projection with the
+// residual add into xattn.
+int run_attention(moe_verify_ctx* c, const void* x_prev, int li, int l, int T, int B, int K1, const int* positions,
+                  const moe_verify_aux* aux, hipStream_t s) {
+  const moe::Dims& d = c->d;
+  const moe_verify_config& g = c->cfg;
+  const int64_t H = g.hidden, k = g.top_k;
+  const size_t es = c->esize;
+  moe::NormRouterParams an{};
+  an.x_in = x_prev;
+  if (li > 0) {  // finish the previous layer's MoE block into xres
+    an.x_out = c->xres;
+    an.y = c->y;
+    an.prev_idx = aux && aux->topk_idx ? aux->topk_idx + (li - 1) * T * k : c->idx[(li - 1) & 1];
+    an.prev_w = aux && aux->topk_w ? aux->topk_w + (li - 1) * T * k : c->w[(li - 1) & 1];
+    an.m_out = aux && aux->moe_out ? aux->moe_out + (li - 1) * T * H : nullptr;
+    an.combine = 1;
+  }
+  an.gamma = c->attn_gamma + l * H * es;
+  an.xhat = c->xhat;
+  an.T = T;
+  an.norm = 1;
+  an.route = 0;
+  MOE_HIP(moe::launch_norm_router(d, an, s));
+  const void* x_res = li > 0 ? c->xres : x_prev;
+
+  const size_t cache_layer = static_cast<size_t>(g.max_seqs) * g.n_heads * g.max_positions * moe::kHeadDim;
+  bf16_t* kc = reinterpret_cast<bf16_t*>(c->kcache) + l * cache_layer;
+  bf16_t* vc = reinterpret_cast<bf16_t*>(c->vcache) + l * cache_layer;
+  moe::ExpertParams qe{};
+  qe.n_active = c->zero;
+  qe.w_down = c->wqkv + l * 3 * H * H * es;
+  qe.act = c->xhat;
+  qe.T = T;
+  moe::EpiParams qp{};
+  qp.positions = positions;
+  qp.K1 = K1;
+  qp.P = g.max_positions;
+  qp.nh = g.n_heads;
+  qp.inv_freq = c->inv_freq;
+  qp.q = reinterpret_cast<bf16_t*>(c->qbuf);
+  qp.kc = kc;
+  qp.vc = vc;
+  MOE_HIP(moe::launch_linear_qkv(c->dq, qe, qp, s));
+
+  moe::AttnParams ap{};
+  ap.q = reinterpret_cast<const bf16_t*>(c->qbuf);
+  ap.kc = kc;
+  ap.vc = vc;
+  ap.positions = positions;
+  ap.B = B;
+  ap.K1 = K1;
+  ap.nh = g.n_heads;
+  ap.P = g.max_positions;
+  ap.G = moe::attn_groups(d, B, g.n_heads);
+  ap.part = c->apart;
+  ap.ctx = reinterpret_cast<bf16_t*>(c->actx);
+  MOE_HIP(moe::launch_attention(d, ap, s));
+
+  moe::ExpertParams oe{};
+  oe.n_active = c->zero;
+  oe.w_down = c->wo + l * H * H * es;
+  oe.act = c->actx;
+  oe.T = T;
+  moe::EpiParams op{};
+  op.x_in = static_cast<const bf16_t*>(x_res);
+  op.x_out = aux && aux->attn_out ? static_cast<bf16_t*>(aux->attn_out) + li * T * H
+                                  : reinterpret_cast<bf16_t*>(c->xattn);
+  MOE_HIP(moe::launch_linear_resid(c->dout, oe, op, s));
+  return MOE_OK;
+}
+
 int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_aux* aux, int layer0, int nlayers,
-               hipStream_t s, const void** x_last) {
+               hipStream_t s, const void** x_last, const int* positions = nullptr, int B = 0, int K1 = 0) {
   const moe::Dims& d = c->d;
   const moe_verify_config& g = c->cfg;
   const int64_t H = g.hidden, k = g.top_k, E = g.n_routed;
+  const bool attn = positions != nullptr;
   const void* x_prev = hidden;  // residual stream entering the previous block
   for (int li = 0; li < nlayers; ++li) {
     const int l = layer0 + li;
     int* idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
     float* wg = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
     moe::NormRouterParams nr{};
-    if (li == 0) {
+    if (attn) {
+      int r;
+      if ((r = run_attention(c, x_prev, li, l, T, B, K1, positions, aux, s))) return r;
+      // the MoE block takes the attention sublayer's output
+      x_prev = aux && aux->attn_out ? static_cast<const char*>(aux->attn_out) + li * T * H * c->esize
+                                    : static_cast<const char*>(c->xattn);
+      nr.x_in = x_prev;
+    } else if (li == 0) {
       nr.x_in = hidden;
     } else {
       nr.x_in = x_prev;
@@ -398,16 +536,21 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
   return MOE_OK;
 }
 
-int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
-              int32_t* committed, int32_t* counts, const moe_verify_aux* aux, void* stream) {
+int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, const int32_t* positions, int32_t B,
+              int32_t K, int32_t* committed, int32_t* counts, const moe_verify_aux* aux, void* stream) {
   if (!c) return fail(MOE_EINVAL, "ctx is NULL");
   const moe_verify_config& g = c->cfg;
   if (!g.has_lm_head) return fail(MOE_EINVAL, "context was created without an LM head");
+  if (g.n_heads > 0 && !positions) return fail(MOE_EINVAL, "context has attention: use moe_verify_step_kv");
+  if (g.n_heads == 0 && positions) return fail(MOE_EINVAL, "context has no attention: use moe_verify_step");
   if (B < 1) return fail(MOE_EINVAL, "B must be >= 1");
   if (K < 0 || K > g.k_max) return fail(MOE_EINVAL, "K must be in [0, k_max]");
   const int64_t T64 = static_cast<int64_t>(B) * (K + 1);
   if (T64 > g.max_tokens) return fail(MOE_EINVAL, "B*(K+1) exceeds max_tokens");
+  if (positions && B > g.max_seqs) return fail(MOE_EINVAL, "B exceeds max_seqs");
+  if (positions && K + 1 > g.max_positions) return fail(MOE_EINVAL, "K+1 exceeds max_positions");
   int r;
+  if ((r = check_ptr(positions, "positions", false))) return r;
   if ((r = check_ptr(hidden, "hidden", true))) return r;
   if ((r = check_ptr(drafts, "drafts", K > 0))) return r;
   if ((r = check_ptr(committed, "committed", true))) return r;
@@ -419,7 +562,7 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, int3
 
   const void* x_last = nullptr;
   MOE_HIP(mark(c->ev_before[MOE_STAGE_ALL], s));
-  if ((r = run_blocks(c, hidden, T, aux, 0, g.n_layers, s, &x_last))) return r;
+  if ((r = run_blocks(c, hidden, T, aux, 0, g.n_layers, s, &x_last, positions, B, K + 1))) return r;
 
   const int64_t H = g.hidden, k = g.top_k;
   const int li = g.n_layers - 1;
@@ -501,16 +644,36 @@ int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* weig
 
 int moe_verify_step(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
                     int32_t* committed, int32_t* counts, void* hip_stream) {
-  const int r = step_impl(ctx, hidden, drafts, B, K, committed, counts, nullptr, hip_stream);
+  const int r = step_impl(ctx, hidden, drafts, nullptr, B, K, committed, counts, nullptr, hip_stream);
   if (ctx) clear_hooks(ctx);
   return r;
 }
 
 int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
                        int32_t* committed, int32_t* counts, const moe_verify_aux* aux, void* hip_stream) {
-  const int r = step_impl(ctx, hidden, drafts, B, K, committed, counts, aux, hip_stream);
+  const int r = step_impl(ctx, hidden, drafts, nullptr, B, K, committed, counts, aux, hip_stream);
   if (ctx) clear_hooks(ctx);
   return r;
+}
+
+int moe_verify_step_kv(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, const int32_t* positions,
+                       int32_t B, int32_t K, int32_t* committed, int32_t* counts, const moe_verify_aux* aux,
+                       void* hip_stream) {
+  if (!positions) {
+    if (ctx) clear_hooks(ctx);
+    return fail(MOE_EINVAL, "positions is NULL");
+  }
+  const int r = step_impl(ctx, hidden, drafts, positions, B, K, committed, counts, aux, hip_stream);
+  if (ctx) clear_hooks(ctx);
+  return r;
+}
+
+int moe_verify_kv_cache(moe_verify_ctx* ctx, void** k_cache, void** v_cache) {
+  if (!ctx || !k_cache || !v_cache) return fail(MOE_EINVAL, "ctx, k_cache and v_cache must be non-NULL");
+  if (ctx->cfg.n_heads == 0) return fail(MOE_EINVAL, "context has no attention");
+  *k_cache = ctx->kcache;
+  *v_cache = ctx->vcache;
+  return MOE_OK;
 }
 
 int moe_verify_graph_create(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B,
@@ -522,7 +685,8 @@ int moe_verify_graph_create(moe_verify_ctx* ctx, const void* hidden, const int32
   for (int i = 0; i < MOE_STAGE_COUNT; ++i)
     if (ctx->ev_before[i] || ctx->ev_after[i]) return fail(MOE_EINVAL, "a timing hook is set; clear it first");
   return moe::api::capture_graph(
-      hip_stream, [&]() { return step_impl(ctx, hidden, drafts, B, K, committed, counts, nullptr, hip_stream); },
+      hip_stream,
+      [&]() { return step_impl(ctx, hidden, drafts, nullptr, B, K, committed, counts, nullptr, hip_stream); },
       out);
 }
 

@@ -44,6 +44,20 @@ struct moe_verify_ctx {
   float* y = nullptr;       // [tw*(k+S)][H]
   unsigned long long* keys = nullptr;  // [kKeySlots][tw]
 
+  // attention (cfg.n_heads > 0)
+  moe::Dims dq{}, dout{};              // q/k/v projection (3 slots), output projection (1 slot)
+  char* attn_gamma = nullptr;          // [L][H]
+  char* wqkv = nullptr;                // tiled [L][3][H/16][H/32][512]
+  char* wo = nullptr;                  // tiled [L][1][H/16][H/32][512]
+  float* inv_freq = nullptr;           // [64]
+  char* kcache = nullptr;              // [L][max_seqs][nh][P][128]
+  char* vcache = nullptr;
+  char* xattn = nullptr;               // [tw][H] attention sublayer output
+  char* qbuf = nullptr;                // [tw][H] rotated queries
+  char* actx = nullptr;                // [tw][H] attention output before W_o
+  float* apart = nullptr;              // attention partials
+  int* zero = nullptr;                 // a device 0 (no routed experts in the projections)
+
   int4* tiles = nullptr;               // grouped-GEMM tile table
   int* n_tiles = nullptr;
   bool gemm_ok = false;                // LDS allows the prefill grouped GEMM

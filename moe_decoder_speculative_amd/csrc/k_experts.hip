@@ -172,8 +172,44 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
   }
 }
 
-template <int KW, int RPW>  // KW: k-steps per wavefront (I/32/4); RPW: row tiles per workgroup
-__global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, int split) {
+// Epilogue of the down kernel when it serves as a plain linear layer over
+// shared-slot rows (EPI 1: the attention's q/k/v projection, slots 0, 1, 2
+// reading the same rows; EPI 2: the attention's output projection with the
+// residual add).  Adjacent output features (2i, 2i+1) sit in one lane, which
+// is the pair the rotary embedding turns.
+template <int EPI>
+__device__ __forceinline__ void linear_epilogue(const Dims& d, const ExpertParams& p, const EpiParams& e, int slot,
+                                                int n, int f, float v0, float v1) {
+  if constexpr (EPI == 1) {
+    const int b = n / e.K1, j = n % e.K1;
+    const int pos = e.positions[b] + j;
+    const int h = f / kHeadDim, dd = f % kHeadDim;
+    if (slot < 2) {  // rotate q and k by pos * inv_freq of the pair
+      float sn, cs;
+      sincosf(static_cast<float>(pos) * e.inv_freq[dd / 2], &sn, &cs);
+      const float r0 = __fsub_rn(__fmul_rn(v0, cs), __fmul_rn(v1, sn));
+      const float r1 = __fadd_rn(__fmul_rn(v0, sn), __fmul_rn(v1, cs));
+      v0 = r0;
+      v1 = r1;
+    }
+    const uint32_t packed = pack_bf16x2(v0, v1);
+    if (slot == 0) {
+      *reinterpret_cast<uint32_t*>(e.q + static_cast<int64_t>(n) * d.H + f) = packed;
+    } else if (pos >= 0 && pos < e.P) {
+      bf16_t* cache = slot == 1 ? e.kc : e.vc;
+      *reinterpret_cast<uint32_t*>(cache + ((static_cast<int64_t>(b) * e.nh + h) * e.P + pos) * kHeadDim + dd) =
+          packed;
+    }
+  } else {
+    const uint32_t x = *reinterpret_cast<const uint32_t*>(e.x_in + static_cast<int64_t>(n) * d.H + f);
+    const float x0 = __uint_as_float(x << 16), x1 = __uint_as_float(x & 0xffff0000u);
+    *reinterpret_cast<uint32_t*>(e.x_out + static_cast<int64_t>(n) * d.H + f) =
+        pack_bf16x2(__fadd_rn(x0, v0), __fadd_rn(x1, v1));
+  }
+}
+
+template <int KW, int RPW, int EPI = 0>  // KW: k-steps per wavefront (I/32/4); RPW: row tiles per workgroup
+__global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, int split, EpiParams e) {
   __shared__ float red[4][RPW][kWave][4];
   __shared__ int pairs[kTile];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
@@ -202,7 +238,9 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
     const int n = tile0 + lane % kTile;
     const int pr = slot_pair(d, p, si, min(n, si.ntok - 1));
     pair = n < si.ntok ? pr : -1;
-    const bf16_t* ar = act + static_cast<int64_t>(pr) * d.I + kt0 * kKStep + (lane / kTile) * 8;
+    // a linear layer's slots all read the token's own row
+    const int arow = EPI == 0 ? pr : min(n, si.ntok - 1);
+    const bf16_t* ar = act + static_cast<int64_t>(arow) * d.I + kt0 * kKStep + (lane / kTile) * 8;
 #pragma unroll
     for (int i = 0; i < KW; ++i) b[i] = load_frag(ar + i * kKStep);
   };
@@ -218,13 +256,28 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
     }
     if (wave == 0 && lane < kTile) pairs[lane] = pair;
     __syncthreads();
-    for (int q = threadIdx.x; q < RPW * kWave * 4; q += kBlock) {
-      const int r = q / (kWave * 4), L = (q / 4) % kWave, i = q % 4;
-      const int col = L % kTile, row = 4 * (L / kTile) + i;
-      const int pr = pairs[col];
-      if (pr >= 0) {
-        const float v = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
-        p.y[static_cast<int64_t>(pr) * d.H + (rb * RPW + r) * kTile + row] = v;
+    if constexpr (EPI == 0) {
+      for (int q = threadIdx.x; q < RPW * kWave * 4; q += kBlock) {
+        const int r = q / (kWave * 4), L = (q / 4) % kWave, i = q % 4;
+        const int col = L % kTile, row = 4 * (L / kTile) + i;
+        const int pr = pairs[col];
+        if (pr >= 0) {
+          const float v = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
+          p.y[static_cast<int64_t>(pr) * d.H + (rb * RPW + r) * kTile + row] = v;
+        }
+      }
+    } else {
+      // feature pairs (row, row + 1) of one token per thread
+      for (int q = threadIdx.x; q < RPW * kWave * 2; q += kBlock) {
+        const int r = q / (kWave * 2), L = (q / 2) % kWave, i = 2 * (q % 2);
+        const int col = L % kTile, row = 4 * (L / kTile) + i;
+        const int pr = pairs[col];
+        if (pr >= 0) {
+          const float v0 = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
+          const float v1 = ((red[0][r][L][i + 1] + red[1][r][L][i + 1]) + red[2][r][L][i + 1]) + red[3][r][L][i + 1];
+          const int n = pr - si.shared * p.T;  // token of the shared-slot row (no routed slots)
+          linear_epilogue<EPI>(d, p, e, si.shared, n, (rb * RPW + r) * kTile + row, v0, v1);
+        }
       }
     }
     __syncthreads();
@@ -312,10 +365,29 @@ hipError_t down_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
   const int split = token_split(p.T);
   if ((d.H / kTile) % RPW == 0) {
     const int grid = split_grid(d, d.H / (kTile * RPW), split);
-    hipLaunchKernelGGL((k_down_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p, split);
+    hipLaunchKernelGGL((k_down_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p, split, EpiParams{});
   } else {
     const int grid = split_grid(d, d.H / kTile, split);
-    hipLaunchKernelGGL((k_down_mfma<KW, 1>), dim3(grid), dim3(kBlock), 0, s, d, p, split);
+    hipLaunchKernelGGL((k_down_mfma<KW, 1>), dim3(grid), dim3(kBlock), 0, s, d, p, split, EpiParams{});
+  }
+  return hipGetLastError();
+}
+
+// A linear layer (H x H per slot) on the down kernel: the slots are shared
+// expert slots over T token rows, the epilogue writes q/k/v or x + W x.
+template <int EPI>
+hipError_t linear_launch(const Dims& d, const ExpertParams& p, const EpiParams& e, hipStream_t s) {
+  constexpr int RPW = 2;
+  if (d.E != 0 || d.k != 0 || d.I != d.H || d.H % (kTile * RPW) != 0 || d.H % kHeadDim != 0) return hipErrorInvalidValue;
+  const int split = token_split(p.T);
+  const int grid = split_grid(d, d.H / (kTile * RPW), split);
+  switch (d.I / (kKStep * 4)) {
+    case 2: hipLaunchKernelGGL((k_down_mfma<2, RPW, EPI>), dim3(grid), dim3(kBlock), 0, s, d, p, split, e); break;
+    case 4: hipLaunchKernelGGL((k_down_mfma<4, RPW, EPI>), dim3(grid), dim3(kBlock), 0, s, d, p, split, e); break;
+    case 8: hipLaunchKernelGGL((k_down_mfma<8, RPW, EPI>), dim3(grid), dim3(kBlock), 0, s, d, p, split, e); break;
+    case 10: hipLaunchKernelGGL((k_down_mfma<10, RPW, EPI>), dim3(grid), dim3(kBlock), 0, s, d, p, split, e); break;
+    case 12: hipLaunchKernelGGL((k_down_mfma<12, RPW, EPI>), dim3(grid), dim3(kBlock), 0, s, d, p, split, e); break;
+    default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
@@ -343,6 +415,16 @@ hipError_t launch_expert_up(const Dims& d, const ExpertParams& p, hipStream_t s)
   }
   const int kw = d.H / (kKStep * 4);
   MOE_KW_CASES(up_kw)
+}
+
+hipError_t launch_linear_qkv(const Dims& d, const ExpertParams& p, const EpiParams& e, hipStream_t s) {
+  if (!d.bf16 || d.S != 3) return hipErrorInvalidValue;
+  return linear_launch<1>(d, p, e, s);
+}
+
+hipError_t launch_linear_resid(const Dims& d, const ExpertParams& p, const EpiParams& e, hipStream_t s) {
+  if (!d.bf16 || d.S != 1) return hipErrorInvalidValue;
+  return linear_launch<2>(d, p, e, s);
 }
 
 hipError_t launch_expert_down(const Dims& d, const ExpertParams& p, hipStream_t s) {

@@ -82,6 +82,39 @@ struct ExpertParams {
 hipError_t launch_expert_up(const Dims& d, const ExpertParams& p, hipStream_t s);
 hipError_t launch_expert_down(const Dims& d, const ExpertParams& p, hipStream_t s);
 
+// Attention projections on the down kernel (d: E = 0, k = 0, I = H; bf16).
+constexpr int kHeadDim = 128;
+struct EpiParams {
+  // q/k/v (d.S = 3: slot 0 q, 1 k, 2 v, all reading act rows 0..T-1; token
+  // n = b*K1 + j sits at position positions[b] + j)
+  const int* positions;   // [B]
+  int K1, P, nh;
+  const float* inv_freq;  // [kHeadDim / 2] rotary inverse frequencies
+  bf16_t* q;              // [T][H] rotated queries
+  bf16_t* kc;             // this layer's key cache [seqs][nh][P][kHeadDim]
+  bf16_t* vc;             // value cache, same layout
+  // residual (d.S = 1): x_out = round(x_in + W act)
+  const bf16_t* x_in;     // [T][H]
+  bf16_t* x_out;          // [T][H]
+};
+hipError_t launch_linear_qkv(const Dims& d, const ExpertParams& p, const EpiParams& e, hipStream_t s);
+hipError_t launch_linear_resid(const Dims& d, const ExpertParams& p, const EpiParams& e, hipStream_t s);
+
+// Decode attention of the verify step: K1 query rows per sequence against
+// positions 0..positions[b]+j of the cache (keys / values [seqs][nh][P][128]).
+struct AttnParams {
+  const bf16_t* q;        // [T][H], T = B*K1
+  const bf16_t* kc;
+  const bf16_t* vc;
+  const int* positions;   // [B]
+  int B, K1, nh, P, G;    // G position groups per (sequence, head)
+  float* part;            // [B][nh][G][K1][2 + kHeadDim]: running max, sum, weighted values
+  bf16_t* ctx;            // [T][H] attention output (combine)
+};
+int attn_groups(const Dims& d, int B, int nh);
+size_t attn_part_floats(int T, int nh, int G);
+hipError_t launch_attention(const Dims& d, const AttnParams& p, hipStream_t s);
+
 // Grouped GEMM for prefill-sized token counts (MFMA, LDS-staged tiles).
 struct GemmTileParams {
   const int* cnt;        // [E]

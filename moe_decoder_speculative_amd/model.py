@@ -23,6 +23,22 @@ def to_device(a: np.ndarray, device="cuda"):
     return torch.from_numpy(a).to(device)
 
 
+_hip = None
+
+
+def hip_memcpy(dst: int, src: int, nbytes: int, kind: int):
+    """Synchronous hipMemcpy between raw addresses (kind 1: host to device,
+    2: device to host), for filling or reading a context's KV cache."""
+    import ctypes
+    global _hip
+    if _hip is None:
+        _hip = ctypes.CDLL("libamdhip64.so")
+        _hip.hipMemcpy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_size_t, ctypes.c_int]
+    rc = _hip.hipMemcpy(dst, src, nbytes, kind)
+    if rc != 0:
+        raise RuntimeError(f"hipMemcpy failed ({rc})")
+
+
 def _stacked(weights: dict, key: str, device):
     """Per-layer arrays stacked into one [L, ...] device tensor, one layer at a time."""
     torch = _torch()
@@ -43,7 +59,8 @@ class VerifyModel:
     """
 
     def __init__(self, w: Workload, weights: dict, max_tokens: int | None = None,
-                 max_prefill_tokens: int = 0, k_max: int = 7, device="cuda", stream=None, copies: int = 1):
+                 max_prefill_tokens: int = 0, k_max: int = 7, device="cuda", stream=None, copies: int = 1,
+                 max_seqs: int | None = None):
         torch = _torch()
         self.w = w
         self.device = device
@@ -52,10 +69,14 @@ class VerifyModel:
             hidden=w.H, n_routed=w.E, top_k=w.k, n_shared=w.S, inter=w.I, vocab=w.V if w.has_lm_head else 0,
             n_layers=len(weights["layers"]), max_tokens=self.max_tokens, max_prefill_tokens=max_prefill_tokens,
             k_max=k_max, rms_eps=w.eps, dtype=B_.MOE_DTYPE_BF16 if w.dtype == "bf16" else B_.MOE_DTYPE_F32,
-            has_lm_head=1 if w.has_lm_head else 0)
+            has_lm_head=1 if w.has_lm_head else 0, n_heads=w.n_heads,
+            max_positions=w.P if w.n_heads else 0, max_seqs=(max_seqs or max(w.B, 1)) if w.n_heads else 0,
+            rope_theta=w.rope_theta if w.n_heads else 0.0)
         self.cfg = cfg
-        t = {k: _stacked(weights, k, device) for k in ("router", "gate", "up", "down", "s_gate", "s_up",
-                                                       "s_down", "gamma")}
+        names = ["router", "gate", "up", "down", "s_gate", "s_up", "s_down", "gamma"]
+        if w.n_heads:
+            names += ["attn_gamma", "w_q", "w_k", "w_v", "w_o"]
+        t = {k: _stacked(weights, k, device) for k in names}
         fg = to_device(weights["final_gamma"], device) if w.has_lm_head else None
         lm = to_device(weights["lm_head"], device) if w.has_lm_head else None
         wts = B_.MoeVerifyWeights(
@@ -63,7 +84,8 @@ class VerifyModel:
             w_down=t["down"].data_ptr(),
             s_gate=t["s_gate"].data_ptr() if w.S else None, s_up=t["s_up"].data_ptr() if w.S else None,
             s_down=t["s_down"].data_ptr() if w.S else None, norm_gamma=t["gamma"].data_ptr(),
-            final_gamma=fg.data_ptr() if fg is not None else None, lm_head=lm.data_ptr() if lm is not None else None)
+            final_gamma=fg.data_ptr() if fg is not None else None, lm_head=lm.data_ptr() if lm is not None else None,
+            **({k: t[k].data_ptr() for k in ("attn_gamma", "w_q", "w_k", "w_v", "w_o")} if w.n_heads else {}))
         torch.cuda.synchronize()
         # `copies` independent contexts (separate repacked weights) let a
         # benchmark rotate among them so no weight byte is served from the
@@ -81,6 +103,39 @@ class VerifyModel:
         self.store_dtype = torch.bfloat16 if w.dtype == "bf16" else torch.float32
 
     # ------------------------------------------------------------------
+    def kv_slab_elems(self) -> int:
+        """bf16 elements of one (layer, sequence) slab of the cache: [heads][P][128]."""
+        return self.cfg.n_heads * self.cfg.max_positions * 128
+
+    def kv_write(self, l: int, b: int, k: np.ndarray, v: np.ndarray, copy: int = 0):
+        """Cache entries 0..n-1 of layer l, sequence b from uint16 (bf16 bits)
+        arrays [heads, n, 128]; the rest of the slab is zeroed."""
+        P = self.cfg.max_positions
+        kptr, vptr = B_.moe_verify_kv_cache(self.ctxs[copy])
+        off = (l * self.cfg.max_seqs + b) * self.kv_slab_elems() * 2
+        for src, base in ((k, kptr), (v, vptr)):
+            slab = np.zeros((self.cfg.n_heads, P, 128), np.uint16)
+            slab[:, :src.shape[1]] = src
+            hip_memcpy(base + off, slab.ctypes.data, slab.nbytes, 1)
+
+    def kv_read(self, l: int, b: int, copy: int = 0):
+        """(k, v) slabs of layer l, sequence b as uint16 arrays [heads, P, 128]."""
+        _torch().cuda.synchronize()
+        P = self.cfg.max_positions
+        kptr, vptr = B_.moe_verify_kv_cache(self.ctxs[copy])
+        off = (l * self.cfg.max_seqs + b) * self.kv_slab_elems() * 2
+        out = []
+        for base in (kptr, vptr):
+            slab = np.empty((self.cfg.n_heads, P, 128), np.uint16)
+            hip_memcpy(slab.ctypes.data, base + off, slab.nbytes, 2)
+            out.append(slab)
+        return out
+
+    def step_kv(self, hidden, drafts, positions, B: int, K: int, committed, counts, aux: dict | None = None,
+                stream=None, copy: int = 0):
+        B_.moe_verify_step_kv(self.ctxs[copy], hidden, drafts if K > 0 else None, positions, B, K, committed, counts,
+                              B_.make_aux(**aux) if aux else None, stream)
+
     def alloc_outputs(self, B: int, K: int):
         torch = _torch()
         committed = torch.empty((B, K + 1), dtype=torch.int32, device=self.device)
@@ -102,6 +157,8 @@ class VerifyModel:
         )
         if with_hidden:
             aux["hidden_out"] = torch.empty((T, w.H), dtype=self.store_dtype, device=self.device)
+        if w.n_heads:
+            aux["attn_out"] = torch.empty((L, T, w.H), dtype=self.store_dtype, device=self.device)
         return aux
 
     def step(self, hidden, drafts, B: int, K: int, committed, counts, aux: dict | None = None, stream=None,

@@ -57,6 +57,9 @@ class Workload:
     seed_id: int
     eps: float = 1e-6
     accept_p: float = DRAFT_ACCEPT_P
+    n_heads: int = 0        # attention heads of 128 (0: MoE-only blocks)
+    P: int = 0              # KV-cache positions per sequence
+    rope_theta: float = 10000.0
 
     @property
     def weight_seed(self) -> int:
@@ -72,6 +75,12 @@ class Workload:
 
     def with_(self, **kw) -> "Workload":
         return replace(self, **kw)
+
+
+PAGE_PROMPT = 1156 + 64     # visual tokens of a page at most, plus the prompt
+PAGE_OUTPUT = 1085          # output tokens per page
+ATTN_P = 2368               # >= PAGE_PROMPT + PAGE_OUTPUT + 8, a multiple of 64
+KV_STD = 0.7                # cached keys / values ~ the scale of W x at N(0, 0.02^2) weights
 
 
 def _verify(name, seed_id, B, **kw):
@@ -100,6 +109,12 @@ WORKLOADS = {
     "stack12_b32_zipf": _verify("stack12_b32_zipf", 5, B=32, L=12, routing="zipf"),
     # batch 1 through the 12 blocks + LM head (the decode-loop cost model's verifier)
     "stack12_b1": _verify("stack12_b1", 7, B=1, L=12),
+    # attention + MoE layers with a KV cache: each sequence part-way through
+    # one page (1,156 visual + 64 prompt tokens, then up to 1,085 generated)
+    "attn_b1": _verify("attn_b1", 8, B=1, n_heads=10, P=ATTN_P),
+    "attn_b32_zipf": _verify("attn_b32_zipf", 9, B=32, routing="zipf", n_heads=10, P=ATTN_P),
+    "attn_stack12_b1": _verify("attn_stack12_b1", 10, B=1, L=12, n_heads=10, P=ATTN_P),
+    "attn_stack12_b32_zipf": _verify("attn_stack12_b32_zipf", 11, B=32, L=12, routing="zipf", n_heads=10, P=ATTN_P),
     # the 8-page prefill through the same 12-block stack (no LM head)
     "prefill_8pages_stack12": Workload("prefill_8pages_stack12", H=1280, E=64, k=6, S=2, I=896,
                                        V=129280, L=12, B=0, K=0, T=8 * (1156 + 64),
@@ -190,7 +205,47 @@ def gen_weights(w: Workload, layers=None, threads: int | None = None) -> dict:
             res["lm_head"] = arr
         else:
             res["layers"][pos[l]][name] = arr
+    if w.n_heads > 0:
+        for l, lw in zip(layer_ids, res["layers"]):
+            lw.update(gen_attn_layer(w, l))
     return res
+
+
+def gen_attn_layer(w: Workload, l: int) -> dict:
+    """Layer l's attention weights from their own seed (SeedSequence(7000+id),
+    one child per layer): attn_gamma = 1 + U(-0.1, 0.1), w_q, w_k, w_v, w_o
+    N(0, 0.02^2)."""
+    ch = np.random.SeedSequence(7000 + w.seed_id).spawn(w.L)[l].spawn(5)
+    out = {"attn_gamma": to_storage((1.0 + 0.1 * _rng(ch[0]).uniform(-1, 1, w.H)).astype(np.float32), w.dtype)}
+    for c, name in zip(ch[1:], ("w_q", "w_k", "w_v", "w_o")):
+        vals = _rng(c).standard_normal(w.H * w.H, dtype=np.float32)
+        vals *= np.float32(WEIGHT_STD)
+        out[name] = to_storage(vals.reshape(w.H, w.H), w.dtype)
+    return out
+
+
+def kv_positions(w: Workload, B: int | None = None) -> np.ndarray:
+    """Cache length of each sequence before the step: part-way through one
+    page, PAGE_PROMPT + U{0 .. PAGE_OUTPUT - 1}, capped so the step fits; a
+    workload whose cache is shorter than a page draws uniformly over what fits."""
+    B = w.B if B is None else B
+    g = _rng(np.random.SeedSequence(8000 + w.seed_id).spawn(1)[0])
+    top = w.P - (w.K + 1)
+    if top >= PAGE_PROMPT + PAGE_OUTPUT:
+        return (PAGE_PROMPT + g.integers(0, PAGE_OUTPUT, size=B)).astype(np.int32)
+    return g.integers(0, top + 1, size=B).astype(np.int32)
+
+
+def kv_prefix(w: Workload, l: int, b: int, n: int):
+    """Cached keys and values of layer l, sequence b at positions 0..n-1:
+    N(0, KV_STD^2) in the storage type, [n_heads, n, 128] each, from child
+    (l, b) of SeedSequence(9000+id) (so any one sequence is reproducible)."""
+    ss = np.random.SeedSequence([9000 + w.seed_id, l, b])
+    g = _rng(ss)
+    shape = (w.n_heads, n, 128)
+    k = g.standard_normal(shape, dtype=np.float32) * np.float32(KV_STD)
+    v = g.standard_normal(shape, dtype=np.float32) * np.float32(KV_STD)
+    return to_storage(k, w.dtype), to_storage(v, w.dtype)
 
 
 # --------------------------------------------------------------------------

@@ -234,3 +234,77 @@ def check_draft_teacher_forced(drafts, states, hidden, committed, counts, R: int
         h, t = states[j], tok
     return (f"{K} steps x {B} rows: state rel err {worst:.2e}; states equal to the oracle's bit for bit "
             f"{equal_traj}/{K * B}; undecided picks {undecided}")
+
+
+def check_attn_step_teacher_forced(out: dict, gpu_kv: list, hidden, drafts, positions, kv0: list, weights: dict,
+                                   shp, ash, margin: float = 1e-3, slack: float = 2e-3) -> str:
+    """A verify step with attention, layer by layer on the GPU's own residual
+    stream, for B' sequences (any subset of a step: sequences do not interact).
+
+    out: the GPU's rows of those sequences -- attn_out [L][T'][H], moe_out,
+    topk_idx, topk_w [L][T'][k], hidden_out [T'][H], tstar [T'], counts [B'],
+    committed [B'][K+1]; gpu_kv[l] = (k, v) float32 [B', nh, P, d] the GPU's
+    caches after the step; kv0[l] = (k, v) the caches before it.  Per layer
+    the oracle runs the attention sublayer from the GPU's layer input on the
+    caches as they were: its output within the storage tolerance, the cache
+    rows it writes equal to the GPU's within the tolerance (bit for bit for
+    all other rows); then the MoE block from the GPU's attention output as in
+    check_rows_teacher_forced, and the next layer's input rebuilt exactly from
+    the GPU's attention output and MoE output.  Finally the greedy picks from
+    the GPU's last residual (exact where decided) and the acceptance of the
+    GPU's own picks."""
+    from oracle import attn_oracle as A
+    from oracle import moe_oracle as O
+    store = O.storage_round(shp.dtype)
+    Bs, K1 = len(positions), out["tstar"].shape[0] // len(positions)
+    K = K1 - 1
+    x = O.as_f32(hidden)
+    worst_a = worst_m = worst_kv = 0.0
+    undecided = 0
+    for l in range(shp.L):
+        lw = weights["layers"][l]
+        kc, vc = kv0[l][0].copy(), kv0[l][1].copy()
+        ra = A.attn_sublayer(x, positions, Bs, K, kc, vc, lw, ash)
+        xa = out["attn_out"][l]
+        err = rowwise_rel_err(xa, ra.x_out)
+        assert err.max() <= REL_TOL[shp.dtype], f"layer {l}: attention output rel err {err.max():.3e}"
+        worst_a = max(worst_a, float(err.max()))
+        gk, gv = gpu_kv[l]
+        for b in range(Bs):
+            p0 = int(positions[b])
+            new = slice(p0, p0 + K1)
+            for cache, ref in ((gk, kc), (gv, vc)):
+                e = rowwise_rel_err(cache[b][:, new].reshape(-1, ash.d_head), ref[b][:, new].reshape(-1, ash.d_head))
+                assert e.max() <= REL_TOL[shp.dtype], f"layer {l} seq {b}: new cache rows rel err {e.max():.3e}"
+                worst_kv = max(worst_kv, float(e.max()))
+                keep = np.ones(ash.P, bool)
+                keep[new] = False
+                assert np.array_equal(cache[b][:, keep], kv0[l][0 if cache is gk else 1][b][:, keep]), \
+                    f"layer {l} seq {b}: cache rows outside the step changed"
+        ref = O.moe_block(xa, lw, shp)
+        idx = out["topk_idx"][l]
+        mg = O.topk_margin(ref.z, shp.k)
+        same = np.all(np.sort(idx, 1) == np.sort(ref.idx, 1), axis=1)
+        decided = mg >= margin
+        assert np.all(same[decided]), f"layer {l}: expert sets differ on rows {np.where(decided & ~same)[0]}"
+        for t in np.where(~decided)[0]:
+            sel = np.zeros(shp.E, bool)
+            sel[idx[t]] = True
+            assert ref.z[t, sel].min() >= ref.z[t, ~sel].max() - slack, f"layer {l} row {t}: invalid top-k"
+        undecided += int((~decided).sum())
+        e = rowwise_rel_err(out["moe_out"][l][same], ref.m[same])
+        assert e.max() <= REL_TOL[shp.dtype], f"layer {l}: moe_out rel err {e.max():.3e}"
+        worst_m = max(worst_m, float(e.max()))
+        x = store((xa + out["moe_out"][l]).astype(np.float32))
+    assert np.array_equal(x, out["hidden_out"]), "rebuilt residual differs from the GPU's hidden_out"
+    lg = O.lm_head_logits(x, weights["final_gamma"], weights["lm_head"], shp.eps, store)
+    ts = out["tstar"]
+    am = O.argmax_margin(lg)
+    dec = am >= margin
+    assert np.array_equal(ts[dec], O.greedy_pick(lg)[dec]), "greedy picks differ on decided rows"
+    assert np.all(lg[np.arange(len(ts)), ts] >= lg.max(1) - slack), "a pick is not within slack of the maximum"
+    committed, counts = O.accept_prefix(ts.reshape(Bs, K1), np.asarray(drafts).reshape(Bs, K))
+    assert np.array_equal(out["counts"], counts) and np.array_equal(out["committed"], committed), \
+        "acceptance of the GPU's own picks differs"
+    return (f"attention out rel err {worst_a:.2e}, new cache rows {worst_kv:.2e}, moe_out {worst_m:.2e}; "
+            f"undecided top-k rows {undecided}, undecided picks {int((~dec).sum())}; counts {counts.tolist()}")

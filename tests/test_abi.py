@@ -145,3 +145,47 @@ def test_draft_calls_reject_null_arguments():
     assert g.value is None
     assert lib.moe_draft_set_stage_events(None, 0, None, None) == B.MOE_EINVAL
     lib.moe_draft_destroy(None)
+
+
+def _attn_cfg(**kw):
+    base = dict(n_heads=2, max_positions=64, max_seqs=4, rope_theta=10000.0)
+    base.update(kw)
+    return _cfg(**base)
+
+
+@pytest.mark.parametrize("bad", [
+    dict(n_heads=-1), dict(n_heads=3), dict(max_positions=4), dict(max_positions=40000), dict(max_seqs=0),
+    dict(max_seqs=2000), dict(rope_theta=0.0), dict(rope_theta=float("inf")),
+])
+def test_init_rejects_bad_attention_config(bad):
+    rc, out = _init_rc(_attn_cfg(**bad), _weights())
+    assert rc == B.MOE_EINVAL and out is None
+    assert B.moe_verify_last_error().startswith("config:")
+
+
+def test_attention_needs_bf16():
+    rc, out = _init_rc(_attn_cfg(dtype=B.MOE_DTYPE_F32), _weights())
+    assert rc == B.MOE_EUNSUPPORTED and out is None
+
+
+@pytest.mark.parametrize("field", ["attn_gamma", "w_q", "w_k", "w_v", "w_o"])
+def test_attention_weights_required(field):
+    rc, _ = _init_rc(_attn_cfg(), _weights(**{field: None}))
+    assert rc == B.MOE_EINVAL and field in B.moe_verify_last_error()
+    # without attention they may be NULL (init then stops at the injected allocation failure)
+    os.environ["MOE_VERIFY_FAULT"] = "alloc"
+    try:
+        rc, _ = _init_rc(_cfg(), _weights(**{field: None}))
+    finally:
+        del os.environ["MOE_VERIFY_FAULT"]
+    assert rc in (B.MOE_ENOMEM, B.MOE_EHIP)
+
+
+def test_step_kv_and_cache_reject_null_arguments():
+    lib = B.load_library()
+    rc = lib.moe_verify_step_kv(None, FAKE, FAKE, FAKE, 1, 3, FAKE, FAKE, None, None)
+    assert rc == B.MOE_EINVAL and "ctx" in B.moe_verify_last_error()
+    rc = lib.moe_verify_step_kv(None, FAKE, FAKE, None, 1, 3, FAKE, FAKE, None, None)
+    assert rc == B.MOE_EINVAL and "positions" in B.moe_verify_last_error()
+    k, v = ctypes.c_void_p(), ctypes.c_void_p()
+    assert lib.moe_verify_kv_cache(None, ctypes.byref(k), ctypes.byref(v)) == B.MOE_EINVAL

@@ -108,3 +108,64 @@ def test_draft_checker_rejects(plant):
     with pytest.raises(AssertionError):
         parity.check_draft_teacher_forced(drafts, states, c["hidden"], c["committed"], counts, c["R"], c["dw"],
                                           c["dshp"])
+
+
+# ------------------------------------------------------------- attention ----
+
+def _attn_case(B=4, K=3, L=2, P=48, seed=93):
+    from oracle import attn_oracle as A
+    w = workloads.small_bf16(B=B, K=K, L=L, seed_id=seed).with_(n_heads=2, P=P)
+    shp = workloads.shape_of(w)
+    ash = A.AttnShape(H=w.H, n_heads=2, d_head=128, P=P, dtype=w.dtype)
+    weights = synth.gen_weights(w)
+    noise = synth.HiddenNoise(w)
+    hidden = synth.to_storage(noise.draw(w.T), w.dtype)
+    positions = synth.kv_positions(w)
+    kv0 = []
+    for l in range(L):
+        kc = np.zeros((B, 2, P, 128), np.float32)
+        vc = np.zeros((B, 2, P, 128), np.float32)
+        for b in range(B):
+            k, v = synth.kv_prefix(w, l, b, int(positions[b]))
+            kc[b, :, :positions[b]] = O.as_f32(k)
+            vc[b, :, :positions[b]] = O.as_f32(v)
+        kv0.append((kc, vc))
+    caches = [(k.copy(), v.copy()) for k, v in kv0]
+    drafts = np.zeros((B, K), np.int32)
+    r = A.verify_step_attn(shp, ash, weights, hidden, drafts, positions, caches, B, K)
+    drafts = synth.make_drafts(w, r.tstar.reshape(B, K + 1))
+    caches = [(k.copy(), v.copy()) for k, v in kv0]
+    r = A.verify_step_attn(shp, ash, weights, hidden, drafts, positions, caches, B, K)
+    out = dict(attn_out=np.stack([a.x_out for a in r.attn]), moe_out=np.stack([b.m for b in r.blocks]),
+               topk_idx=np.stack([b.idx for b in r.blocks]), topk_w=np.stack([b.w for b in r.blocks]),
+               hidden_out=r.hidden_out, tstar=r.tstar, counts=r.counts, committed=r.committed)
+    return dict(out=out, kv=caches, kv0=kv0, hidden=hidden, drafts=drafts, positions=positions, weights=weights,
+                shp=shp, ash=ash)
+
+
+def _check_attn(c):
+    return parity.check_attn_step_teacher_forced(c["out"], c["kv"], c["hidden"], c["drafts"], c["positions"],
+                                                 c["kv0"], c["weights"], c["shp"], c["ash"])
+
+
+def test_attn_checker_accepts_the_oracle():
+    assert "counts" in _check_attn(_attn_case())
+
+
+@pytest.mark.parametrize("plant", ["old_row", "shifted_row", "attn_out", "counts"])
+def test_attn_checker_rejects(plant):
+    c = _attn_case()
+    pos = c["positions"]
+    if plant == "old_row":
+        c["kv"][0][0][1, 0, max(int(pos[1]) - 1, 0)] += 1.0       # an earlier cache row changed
+    elif plant == "shifted_row":
+        k = c["kv"][1][0][2]
+        p0 = int(pos[2])
+        k[:, p0 + 1:p0 + 5] = k[:, p0:p0 + 4].copy()              # keys written one position late
+        k[:, p0] = c["kv0"][1][0][2][:, p0]
+    elif plant == "attn_out":
+        c["out"]["attn_out"][1][3] *= 1.05
+    else:
+        c["out"]["counts"] = c["out"]["counts"] % 4 + 1
+    with pytest.raises(AssertionError):
+        _check_attn(c)

@@ -1,0 +1,190 @@
+"""Parity of the verify step with attention and a KV cache (moe_verify_step_kv)
+with the CPU oracle, through the C ABI.
+
+Small shapes (two heads of 128) over several layers with ragged batches,
+K = 0, 3 and 7, cache positions from empty to the last that fits, two steps
+in a row continuing the cache (positions advanced by the committed counts);
+the full-size one-layer workloads; and sampled sequences of the 12-layer
+batch-32 step with attention (a complete verify forward of the pages'
+decoder shape).  Bar: tests/parity.py, check_attn_step_teacher_forced.
+"""
+import numpy as np
+import pytest
+
+from oracle import attn_oracle as A
+from oracle import moe_oracle as O
+from moe_decoder_speculative_amd import synth
+from moe_decoder_speculative_amd.model import VerifyModel, to_device
+import parity
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    return torch
+
+
+def _prefix(w, positions, seqs=None):
+    """kv0[l] = (k, v) float32 [B', nh, P, 128] for sequences `seqs`, and the
+    bf16 bits of every (l, b) prefix for the upload."""
+    seqs = range(len(positions)) if seqs is None else seqs
+    bits = {}
+    kv0 = []
+    for l in range(w.L):
+        kc = np.zeros((len(seqs), w.n_heads, w.P, 128), np.float32)
+        vc = np.zeros_like(kc)
+        for i, b in enumerate(seqs):
+            k, v = synth.kv_prefix(w, l, b, int(positions[b]))
+            bits[(l, b)] = (k, v)
+            kc[i, :, :positions[b]] = O.as_f32(k)
+            vc[i, :, :positions[b]] = O.as_f32(v)
+        kv0.append((kc, vc))
+    return kv0, bits
+
+
+def _ash(w):
+    return A.AttnShape(H=w.H, n_heads=w.n_heads, d_head=128, P=w.P, theta=w.rope_theta, eps=w.eps, dtype=w.dtype)
+
+
+def _drafts(w, weights, hidden, positions, kv0):
+    """Drafts from the oracle's own greedy picks (kept with probability p)."""
+    caches = [(k.copy(), v.copy()) for k, v in kv0]
+    r = A.verify_step_attn(workloads.shape_of(w), _ash(w), weights, hidden, np.zeros((w.B, w.K), np.int32),
+                           positions, caches, w.B, w.K)
+    return synth.make_drafts(w, r.tstar.reshape(w.B, w.K + 1))
+
+
+def _gpu_step(vm, w, hidden, drafts, positions, B, K):
+    torch = _torch()
+    T = B * (K + 1)
+    aux = vm.alloc_aux(T)
+    committed, counts = vm.alloc_outputs(B, K)
+    vm.step_kv(to_device(hidden), to_device(np.asarray(drafts, np.int32)) if K else None,
+               to_device(np.asarray(positions, np.int32)), B, K, committed, counts, aux)
+    torch.cuda.synchronize()
+    out = {k: (parity.storage_to_f32(t) if k in ("hidden_out", "attn_out") else t.cpu().numpy())
+           for k, t in aux.items()}
+    out["committed"], out["counts"] = committed.cpu().numpy(), counts.cpu().numpy()
+    return out
+
+
+def _gpu_kv(vm, w, seqs):
+    kv = []
+    for l in range(w.L):
+        ks, vs = zip(*(vm.kv_read(l, b) for b in seqs))
+        kv.append((O.as_f32(np.stack(ks)), O.as_f32(np.stack(vs))))
+    return kv
+
+
+def _rows(out, seqs, K1):
+    """The rows of sequences `seqs` from a whole step's outputs."""
+    rows = np.concatenate([np.arange(b * K1, (b + 1) * K1) for b in seqs])
+    sub = {k: out[k][:, rows] for k in ("attn_out", "moe_out", "topk_idx", "topk_w")}
+    sub.update(hidden_out=out["hidden_out"][rows], tstar=out["tstar"][rows], counts=out["counts"][list(seqs)],
+               committed=out["committed"][list(seqs)])
+    return sub
+
+
+def _small_case(B, K, L, P, seed, edge=True):
+    w = workloads.small_bf16(name="attn_small", B=B, K=K, L=L, seed_id=seed).with_(n_heads=2, P=P)
+    positions = synth.kv_positions(w)
+    if edge and B >= 2:
+        positions[0], positions[-1] = 0, P - (K + 1)     # an empty cache and a full one
+    return w, positions
+
+
+@pytest.mark.parametrize("B,K,L,P", [(5, 3, 2, 64), (3, 0, 1, 64), (2, 7, 1, 80), (33, 3, 1, 128), (1, 3, 3, 256)])
+def test_attention_step_small(B, K, L, P):
+    w, positions = _small_case(B, K, L, P, seed=500 + B + 10 * K + 100 * L)
+    parity.say(f"[attn small] B={B} K={K} L={L} P={P} H={w.H} heads={w.n_heads} positions={positions.tolist()[:6]} "
+               f"entry=moe_verify_step_kv")
+    weights = synth.gen_weights(w)
+    hidden = synth.to_storage(synth.HiddenNoise(w).draw(w.T), w.dtype)
+    kv0, bits = _prefix(w, positions)
+    drafts = _drafts(w, weights, hidden, positions, kv0) if K else np.zeros((B, 0), np.int32)
+    vm = VerifyModel(w, weights, max_tokens=w.T, max_seqs=B)
+    try:
+        for (l, b), (k, v) in bits.items():
+            vm.kv_write(l, b, k, v)
+        out = _gpu_step(vm, w, hidden, drafts, positions, B, K)
+        msg = parity.check_attn_step_teacher_forced(out, _gpu_kv(vm, w, range(B)), hidden, drafts, positions, kv0,
+                                                    weights, workloads.shape_of(w), _ash(w))
+        parity.say(f"[attn small] ok: {msg}")
+    finally:
+        vm.close()
+
+
+def test_attention_two_steps_continue_the_cache():
+    """Step 1, then step 2 at positions + counts on the same cache (rejected
+    drafts' rows are overwritten); the oracle checks step 2 from the GPU's
+    cache after step 1."""
+    B, K, L, P = 4, 3, 2, 96
+    w, positions = _small_case(B, K, L, P, seed=611, edge=False)
+    positions = np.minimum(positions, P - 2 * (K + 1))
+    weights = synth.gen_weights(w)
+    noise = synth.HiddenNoise(w)
+    kv0, bits = _prefix(w, positions)
+    vm = VerifyModel(w, weights, max_tokens=w.T, max_seqs=B)
+    try:
+        for (l, b), (k, v) in bits.items():
+            vm.kv_write(l, b, k, v)
+        for step in range(2):
+            hidden = synth.to_storage(noise.draw(w.T), w.dtype)
+            drafts = _drafts(w, weights, hidden, positions, kv0)
+            parity.say(f"[attn two steps] step {step} positions {positions.tolist()}")
+            out = _gpu_step(vm, w, hidden, drafts, positions, B, K)
+            kv_after = _gpu_kv(vm, w, range(B))
+            msg = parity.check_attn_step_teacher_forced(out, kv_after, hidden, drafts, positions, kv0, weights,
+                                                        workloads.shape_of(w), _ash(w))
+            parity.say(f"[attn two steps] ok: {msg}")
+            positions = positions + out["counts"]
+            kv0 = kv_after
+    finally:
+        vm.close()
+
+
+@pytest.mark.parametrize("name,sample", [("attn_b1", None), ("attn_b32_zipf", [0, 7, 19, 31])])
+def test_attention_full_size_one_layer(name, sample):
+    w = synth.WORKLOADS[name]
+    _full(w, sample)
+
+
+@pytest.mark.slow
+def test_attention_stack12_b32_sampled():
+    """The 12-layer batch-32 step with attention as the benchmark runs it;
+    sequences 0 and 21 followed by the oracle layer by layer."""
+    _full(synth.WORKLOADS["attn_stack12_b32_zipf"], [0, 21])
+
+
+def _full(w, sample):
+    positions = synth.kv_positions(w)
+    seqs = list(range(w.B)) if sample is None else sample
+    parity.say(f"[attn full] {w.name}: B={w.B} K={w.K} L={w.L} P={w.P} sampled sequences {seqs} "
+               f"positions {positions[seqs].tolist()}")
+    weights = synth.gen_weights(w)
+    noise = synth.HiddenNoise(w)
+    hidden = synth.to_storage(noise.draw(w.T) + synth.hidden_offset(w, weights, noise), w.dtype)
+    K1 = w.K + 1
+    rows = np.concatenate([np.arange(b * K1, (b + 1) * K1) for b in seqs])
+    # drafts: the sampled sequences' from the oracle's picks, the rest random
+    kv0, _ = _prefix(w, positions, seqs)
+    sub_w = w.with_(B=len(seqs), T=len(seqs) * K1)
+    d_sub = _drafts(sub_w, weights, hidden[rows], positions[seqs], kv0)
+    drafts = np.random.default_rng(5).integers(0, w.V, size=(w.B, w.K)).astype(np.int32)
+    drafts[seqs] = d_sub
+    vm = VerifyModel(w, weights, max_tokens=w.T, max_seqs=w.B)
+    try:
+        for l in range(w.L):
+            for b in range(w.B):
+                k, v = synth.kv_prefix(w, l, b, int(positions[b]))
+                vm.kv_write(l, b, k, v)
+        out = _gpu_step(vm, w, hidden, drafts, positions, w.B, w.K)
+        msg = parity.check_attn_step_teacher_forced(_rows(out, seqs, K1), _gpu_kv(vm, w, seqs), hidden[rows],
+                                                    drafts[seqs], positions[seqs], kv0, weights,
+                                                    workloads.shape_of(w), _ash(w))
+        parity.say(f"[attn full] {w.name} ok: {msg}")
+    finally:
+        vm.close()
