@@ -98,6 +98,20 @@ def step_bytes(w, touched_per_layer) -> int:
     return int(sum(per) + lm)
 
 
+def attn_kv_bytes(w, positions) -> int:
+    """Keys and values the step's queries read: per sequence and head the
+    cache rows 0..p_b+K (256 B each for keys and for values)."""
+    return int(sum(w.n_heads * (int(p) + w.K + 1) * 512 for p in positions))
+
+
+def attn_step_bytes(w, positions) -> int:
+    """Attention's share of a step: per layer the four projections, the cache
+    rows read, the step's own keys and values written."""
+    if not w.n_heads:
+        return 0
+    return w.L * (4 * w.H * w.H * 2 + attn_kv_bytes(w, positions) + w.T * w.n_heads * 512)
+
+
 def step_flops(w) -> int:
     f = w.L * (w.T * (w.k + w.S) * 6 * w.H * w.I + 2 * w.T * w.E * w.H)
     if w.has_lm_head:
@@ -165,7 +179,29 @@ def cpu_baseline(w, weights, hidden_np, drafts_np, seconds: float):
     import oracle
     shp = oracle.Shape(H=w.H, E=w.E, k=w.k, S=w.S, I=w.I, V=w.V, L=w.L, eps=w.eps, dtype=w.dtype)
     # sample: whole steps when small, else one sequence (K+1 tokens) per call
-    if w.has_lm_head:
+    if w.has_lm_head and w.n_heads:
+        from oracle import attn_oracle as A
+        from moe_decoder_speculative_amd import synth
+        K = w.K
+        ash = A.AttnShape(H=w.H, n_heads=w.n_heads, d_head=128, P=w.P, theta=w.rope_theta, eps=w.eps,
+                          dtype=w.dtype)
+        pos = synth.kv_positions(w)[:1]
+        caches = []
+        for l in range(w.L):
+            k, v = synth.kv_prefix(w, l, 0, int(pos[0]))
+            kc = np.zeros((1, w.n_heads, w.P, 128), np.float32)
+            vc = np.zeros_like(kc)
+            kc[0, :, :pos[0]] = oracle.as_f32(k)
+            vc[0, :, :pos[0]] = oracle.as_f32(v)
+            caches.append((kc, vc))
+        h = hidden_np[: K + 1]
+        d = drafts_np[:1]
+        what = f"1 sequence x {K + 1} positions over a {int(pos[0])}-position cache per oracle step"
+        tokens_per_call = K + 1
+
+        def call():
+            A.verify_step_attn(shp, ash, weights, h, d, pos, caches, 1, K)
+    elif w.has_lm_head:
         seqs = w.B if w.T <= 8 else 1
         Bs, K = seqs, w.K
         h = hidden_np[: Bs * (K + 1)]
@@ -398,7 +434,8 @@ def bench_draft(args, name, torch, np, synth, binding, VerifyModel, to_device):
     gpu_ms_call = ev.elapsed_ms(g0, g1) / n
     kern_ms = sorted(ev.elapsed_ms(b, a) for b, a in zip(before, after))
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
-    for e in before + after + [g0, g1]:
+    attn_ms = sorted(ev.elapsed_ms(b, a) for b, a in zip(abefore, aafter))
+    for e in before + after + abefore + aafter + [g0, g1]:
         ev.destroy(e)
     kname = "k_lmhead_stream" if B <= 16 else ("k_lmhead_wide" if B <= 128 else "k_lmhead_mfma")
     kbytes = draft_head_bytes(H, Vd, B)
@@ -452,7 +489,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="decode_b1",
                     choices=["decode_b1", "decode_b32_zipf", "stack12_b32_zipf", "prefill_8pages",
-                             "prefill_8pages_stack12", "stack12_b1", "draft_b1", "draft_b32", "draft_b1_head32k"])
+                             "prefill_8pages_stack12", "stack12_b1", "draft_b1", "draft_b32", "draft_b1_head32k",
+                             "attn_b1", "attn_b32_zipf", "attn_stack12_b1", "attn_stack12_b32_zipf"])
     ap.add_argument("--draft", default=None, help="draft workload of the cost model (default: same B, whole head)")
     ap.add_argument("--copies", type=int, default=0, help="weight copies to rotate (0: enough for 1.5 GB)")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
@@ -510,8 +548,20 @@ def main():
         return
     prefill = not w.has_lm_head
     model = VerifyModel(w, weights, max_tokens=16 if prefill else w.T,
-                        max_prefill_tokens=w.T if prefill else 0, copies=copies)
+                        max_prefill_tokens=w.T if prefill else 0, copies=copies, max_seqs=max(w.B, 1))
     log(f"{copies} weight copies of {copy_bytes / 1e6:.0f} MB in HBM")
+    positions_np = None
+    if w.n_heads:
+        positions_np = synth.kv_positions(w)
+        t = time.time()
+        for l in range(w.L):
+            for b in range(w.B):
+                k, v = synth.kv_prefix(w, l, b, int(positions_np[b]))
+                for c in range(copies):
+                    model.kv_write(l, b, k, v, copy=c)
+        positions = to_device(positions_np)
+        log(f"KV caches filled ({w.n_heads} heads, positions {int(positions_np.min())}..{int(positions_np.max())}) "
+            f"in {time.time() - t:.1f}s")
 
     hidden = to_device(hidden_np)
     drafts_np = None
@@ -538,18 +588,25 @@ def main():
         # drafts: each correct with probability p against this step's own greedy picks
         committed, counts = model.alloc_outputs(w.B, w.K)
         aux = model.alloc_aux(w.T, with_hidden=False)
-        model.step(hidden, to_device(np.zeros((w.B, w.K), np.int32)), w.B, w.K, committed, counts, aux)
+
+        def one(d, c=0, a=None):
+            if w.n_heads:
+                model.step_kv(hidden, d, positions, w.B, w.K, committed, counts, a, copy=c)
+            else:
+                model.step(hidden, d, w.B, w.K, committed, counts, a, copy=c)
+
+        one(to_device(np.zeros((w.B, w.K), np.int32)), 0, aux)
         torch.cuda.synchronize()
         tstar = aux["tstar"].cpu().numpy()
         touched = [len(np.unique(aux["topk_idx"][l].cpu().numpy())) for l in range(w.L)]
         drafts_np = synth.make_drafts(w, tstar.reshape(w.B, w.K + 1))
         drafts = to_device(drafts_np)
-        model.step(hidden, drafts, w.B, w.K, committed, counts)
+        one(drafts)
         torch.cuda.synchronize()
         committed_per_step = int(counts.sum().item())
 
         def run(c):
-            model.step(hidden, drafts, w.B, w.K, committed, counts, copy=c)
+            one(drafts, c)
     del aux
 
     ev = HipEvents()
@@ -564,6 +621,8 @@ def main():
     sampled = list(range(0, K, EVERY))
     before = [ev.create() for _ in sampled]
     after = [ev.create() for _ in sampled]
+    abefore = [ev.create() for _ in sampled] if w.n_heads else []
+    aafter = [ev.create() for _ in sampled] if w.n_heads else []
     g0, g1 = ev.create(), ev.create()
     stage = binding.MOE_STAGE_LMHEAD if (w.L == 1 and not prefill) else binding.MOE_STAGE_EXPERT_UP
     torch.cuda.synchronize()
@@ -573,6 +632,9 @@ def main():
         c = i % copies
         if i % EVERY == 0:
             binding.moe_verify_set_stage_events(model.ctxs[c], stage, before[i // EVERY], after[i // EVERY])
+            if w.n_heads:
+                binding.moe_verify_set_stage_events(model.ctxs[c], binding.MOE_STAGE_ATTENTION,
+                                                    abefore[i // EVERY], aafter[i // EVERY])
         run(c)
     ev.record(g1, stream)
     torch.cuda.synchronize()
@@ -581,7 +643,8 @@ def main():
     gpu_ms_step = ev.elapsed_ms(g0, g1) / K
     kern_ms = sorted(ev.elapsed_ms(b, a) for b, a in zip(before, after))
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
-    for e in before + after + [g0, g1]:
+    attn_ms = sorted(ev.elapsed_ms(b, a) for b, a in zip(abefore, aafter))
+    for e in before + after + abefore + aafter + [g0, g1]:
         ev.destroy(e)
 
     if prefill:
@@ -604,8 +667,20 @@ def main():
                 "kernel": kname, "bytes_per_launch": kbytes}
     roof.update({"avg_us": kern_avg_ms * 1e3, "median_us": kern_ms[len(kern_ms) // 2] * 1e3,
                  "launches_timed": len(kern_ms)})
-    sbytes = step_bytes(w, touched)
+    attn_roof = None
+    if w.n_heads:
+        abytes = attn_kv_bytes(w, positions_np) + w.T * w.H * 2
+        aavg = sum(attn_ms) / len(attn_ms)
+        aach = abytes / (aavg * 1e-3) / 1e9
+        attn_roof = {"bound": "hbm", "achieved": aach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": aach / HBM_PEAK_GBS, "kernel": "k_attn_split", "bytes_per_launch": abytes,
+                     "avg_us": aavg * 1e3, "median_us": attn_ms[len(attn_ms) // 2] * 1e3,
+                     "launches_timed": len(attn_ms), "traffic": traffic_from_profiles("k_attention.hip", w.name)}
+    sbytes = step_bytes(w, touched) + attn_step_bytes(w, positions_np)
     sflops = step_flops(w)
+    if w.n_heads:  # projections and the q.k / p.v products over the cached rows
+        sflops += w.L * (8 * w.T * w.H * w.H + 4 * 128 * w.n_heads * sum(
+            (w.K + 1) * (int(p) + w.K + 1) for p in positions_np))
     step = {"gpu_ms_per_step": gpu_ms_step, "algorithmic_bytes": sbytes,
             "hbm_frac": sbytes / (ms_step * 1e-3) / (HBM_PEAK_GBS * 1e9), "flops": sflops,
             "mfma_frac": sflops / (ms_step * 1e-3) / (MFMA_BF16_PEAK_TFLOPS * 1e12),
@@ -634,6 +709,10 @@ def main():
         "roofline": roof,
         "step": step,
     }
+    if attn_roof:
+        res["attention"] = attn_roof
+        res["config"].update(heads=w.n_heads, kv_positions=[int(positions_np.min()), int(positions_np.max())],
+                             kv_capacity=w.P)
     model.close()
     torch.cuda.synchronize()
     if not args.no_cpu_baseline:

@@ -276,7 +276,8 @@ void moe_verify_graph_destroy(moe_verify_graph* graph);
 #define MOE_STAGE_EXPERT_UP 1   /* expert gate/up kernel of the first block of a call        */
 #define MOE_STAGE_EXPERT_DOWN 2 /* expert down kernel of the first block of a call           */
 #define MOE_STAGE_ALL 3         /* the whole call, first kernel to last                      */
-#define MOE_STAGE_COUNT 4
+#define MOE_STAGE_ATTENTION 4   /* decode-attention kernel of the first layer (step_kv)      */
+#define MOE_STAGE_COUNT 5
 
 /*
  * Timing hook for profiling.  `before` and `after` are hipEvent_t handles

@@ -22,7 +22,7 @@ EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_ver
             "moe_verify_set_stage_events", "moe_verify_destroy", "moe_verify_last_error",
             "moe_draft_init", "moe_draft_step", "moe_draft_graph_create", "moe_draft_set_stage_events",
             "moe_draft_destroy")
-MOE_STAGE_LMHEAD, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_ALL = 0, 1, 2, 3
+MOE_STAGE_LMHEAD, MOE_STAGE_EXPERT_UP, MOE_STAGE_EXPERT_DOWN, MOE_STAGE_ALL, MOE_STAGE_ATTENTION = 0, 1, 2, 3, 4
 
 
 class MoeVerifyError(RuntimeError):

@@ -417,7 +417,10 @@ int run_attention(moe_verify_ctx* c, const void* x_prev, int li, int l, int T, i
   ap.G = moe::attn_groups(d, B, g.n_heads);
   ap.part = c->apart;
   ap.ctx = reinterpret_cast<bf16_t*>(c->actx);
-  MOE_HIP(moe::launch_attention(d, ap, s));
+  if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_ATTENTION], s));
+  MOE_HIP(moe::launch_attention_split(d, ap, s));
+  if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_ATTENTION], s));
+  MOE_HIP(moe::launch_attention_combine(ap, s));
 
   moe::ExpertParams oe{};
   oe.n_active = c->zero;

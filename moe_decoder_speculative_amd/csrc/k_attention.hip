@@ -5,14 +5,15 @@
 // At decode sizes attention is a stream over the KV cache (512 B per position
 // and head), so the work is split over positions: workgroup (g, h, b) takes
 // the 64-position tiles g*4 + w, g*4 + w + 4G, ... of sequence b and head h,
-// one tile per wavefront at a time, in float32 on the vector ALUs:
-//   scores: lane = position, the lane streams its 256-byte key row and dots
-//           it with the K1 queries held in LDS (broadcast reads);
-//   softmax: per query the tile's maximum and sum across the wavefront, folded
-//           into a running (max, sum) with the usual rescaling;
-//   values:  lane = two head dimensions, each position's value row is one
-//           coalesced 256-byte read, its weights broadcast from the lane that
-//           scored it (readlane).
+// one tile per wavefront at a time, every load of a tile issued first:
+//   scores: 16 MFMAs 16x16x32 per tile with the keys as the A operand (bf16
+//           rows as cached, 16 B a lane) and the bf16 queries as B (columns
+//           >= K1 zero), float32 accumulation;
+//   softmax: per query the tile's maximum and sum (16 values in a lane, then
+//           across the four lane groups), folded into a running (max, sum)
+//           with the usual rescaling;
+//   values:  float32, lane = two head dimensions, each position's value row is
+//           one coalesced 256-byte read, its weights broadcast through LDS.
 // The four wavefronts' states meet in LDS and the workgroup writes one
 // partial (max, sum, weighted values) per query; k_attn_combine merges the G
 // partials of every (row, head) and rounds the result to bfloat16.  Reading of
@@ -35,106 +36,135 @@ constexpr int kPartStride = 2 + kHeadDim;
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kNegBig = -1.0e30f;
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, kWave));
-  return v;
-}
-
 __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(x * kLog2e); }
+
+// position groups of a sequence that hold cache rows (the others exit)
+__device__ __forceinline__ int used_groups(int len, int G) { return min(G, (len + 4 * kPosTile - 1) / (4 * kPosTile)); }
+
+__device__ __forceinline__ int clamped_pos(const AttnParams& p, int b, int K1) {
+  return min(max(p.positions[b], 0), p.P - K1);
+}
 
 template <int K1>
 __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
-  __shared__ __align__(16) float qs[K1][kHeadDim];
+  __shared__ __align__(16) bf16_t qb[16][kHeadDim];       // queries, rows >= K1 zero (MFMA B operand)
+  __shared__ __align__(16) float wsm[4][K1][kPosTile];     // a wavefront's softmax weights of one tile
   __shared__ float wm[4][K1], wl[4][K1];
   __shared__ float wacc[4][K1][kHeadDim];
   const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   const int H = p.nh * kHeadDim;
   // positions are clamped so every access stays inside the cache
-  const int pos0 = min(max(p.positions[b], 0), p.P - K1);
+  const int pos0 = clamped_pos(p, b, K1);
   const int len = pos0 + K1;
-  for (int i = threadIdx.x; i < K1 * kHeadDim; i += kBlock) {
-    const int j = i / kHeadDim, dd = i % kHeadDim;
-    qs[j][dd] = bf16_to_f32(p.q[static_cast<int64_t>(b * K1 + j) * H + h * kHeadDim + dd]);
+  if (g >= used_groups(len, p.G)) return;
+  for (int i = threadIdx.x; i < 16 * kHeadDim / 8; i += kBlock) {
+    const int j = i / (kHeadDim / 8), c = i % (kHeadDim / 8);
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (j < K1) v = *reinterpret_cast<const uint4*>(p.q + static_cast<int64_t>(b * K1 + j) * H + h * kHeadDim + 8 * c);
+    *reinterpret_cast<uint4*>(&qb[j][8 * c]) = v;
   }
   __syncthreads();
+  // query fragments of the four k-steps: column lane % 16, dimensions (lane / 16) * 8 + 32 ks
+  bf16x8_t qf[4];
+#pragma unroll
+  for (int ks = 0; ks < 4; ++ks)
+    qf[ks] = *reinterpret_cast<const bf16x8_t*>(&qb[lane % 16][ks * 32 + (lane / 16) * 8]);
   const int64_t base = (static_cast<int64_t>(b) * p.nh + h) * p.P;
   const bf16_t* kc = p.kc + base * kHeadDim;
   const bf16_t* vc = p.vc + base * kHeadDim;
   const float scale = 0.08838834764831845f;  // 1 / sqrt(128)
+  const int jq = lane % 16;                    // the query this lane's scores belong to
 
-  float m[K1], l[K1], acc[K1][2];
+  float m = kNegBig, l = 0.0f;  // running max and sum of query jq
+  float acc[K1][2];
 #pragma unroll
-  for (int j = 0; j < K1; ++j) {
-    m[j] = kNegBig;
-    l[j] = 0.0f;
-    acc[j][0] = acc[j][1] = 0.0f;
-  }
+  for (int j = 0; j < K1; ++j) acc[j][0] = acc[j][1] = 0.0f;
   for (int tile = g * 4 + wave; tile * kPosTile < len; tile += p.G * 4) {
-    const int pp = tile * kPosTile + lane;
-    const bool valid = pp < len;
-    const bf16_t* krow = kc + static_cast<int64_t>(min(pp, len - 1)) * kHeadDim;
-    float s[K1];
+    const int t0 = tile * kPosTile;
+    // every load of the tile first: key fragments (A operand: row = position
+    // t0 + 16 pt + lane % 16, dimensions (lane / 16) * 8 + 32 ks) and the 64
+    // value-row words of this lane's two dimensions; rows past the cache length
+    // repeat the last row and get weight zero
+    uint4 kf[4][4];
 #pragma unroll
-    for (int j = 0; j < K1; ++j) s[j] = 0.0f;
-#pragma unroll 4
-    for (int c = 0; c < kHeadDim / 8; ++c) {
-      const uint4 kv = *reinterpret_cast<const uint4*>(krow + c * 8);
-      const float kf[8] = {__uint_as_float(kv.x << 16), __uint_as_float(kv.x & 0xffff0000u),
-                           __uint_as_float(kv.y << 16), __uint_as_float(kv.y & 0xffff0000u),
-                           __uint_as_float(kv.z << 16), __uint_as_float(kv.z & 0xffff0000u),
-                           __uint_as_float(kv.w << 16), __uint_as_float(kv.w & 0xffff0000u)};
+    for (int pt = 0; pt < 4; ++pt) {
+      const bf16_t* krow = kc + static_cast<int64_t>(min(t0 + pt * 16 + lane % 16, len - 1)) * kHeadDim;
 #pragma unroll
-      for (int j = 0; j < K1; ++j) {
-        const float4 qa = *reinterpret_cast<const float4*>(&qs[j][c * 8]);
-        const float4 qb = *reinterpret_cast<const float4*>(&qs[j][c * 8 + 4]);
-        s[j] = fmaf(kf[0], qa.x, s[j]);
-        s[j] = fmaf(kf[1], qa.y, s[j]);
-        s[j] = fmaf(kf[2], qa.z, s[j]);
-        s[j] = fmaf(kf[3], qa.w, s[j]);
-        s[j] = fmaf(kf[4], qb.x, s[j]);
-        s[j] = fmaf(kf[5], qb.y, s[j]);
-        s[j] = fmaf(kf[6], qb.z, s[j]);
-        s[j] = fmaf(kf[7], qb.w, s[j]);
-      }
+      for (int ks = 0; ks < 4; ++ks) kf[pt][ks] = *reinterpret_cast<const uint4*>(krow + ks * 32 + (lane / 16) * 8);
     }
-    float w[K1];
+    uint32_t vv[kPosTile];
+#pragma unroll
+    for (int q = 0; q < kPosTile; ++q)
+      vv[q] = *reinterpret_cast<const uint32_t*>(vc + static_cast<int64_t>(min(t0 + q, len - 1)) * kHeadDim + 2 * lane);
+    // scores: sc[pt][i] = q_jq . k at position t0 + 16 pt + 4 (lane / 16) + i
+    f32x4_t sc[4];
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt) {
+      sc[pt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) sc[pt] = mfma16(__builtin_bit_cast(bf16x8_t, kf[pt][ks]), qf[ks], sc[pt]);
+    }
+    float M = kNegBig;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int pp = t0 + pt * 16 + 4 * (lane / 16) + i;
+        const bool ok = jq < K1 && pp < len && pp <= pos0 + jq;  // causal: query j sees up to pos0 + j
+        sc[pt][i] = ok ? sc[pt][i] * scale : kNegBig;
+        M = fmaxf(M, sc[pt][i]);
+      }
+    M = fmaxf(M, __shfl_xor(M, 16, kWave));
+    M = fmaxf(M, __shfl_xor(M, 32, kWave));
+    float L = 0.0f;
+#pragma unroll
+    for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = sc[pt][i] > 0.5f * kNegBig ? exp_f(sc[pt][i] - M) : 0.0f;
+        sc[pt][i] = e;
+        L += e;
+      }
+    L += __shfl_xor(L, 16, kWave);
+    L += __shfl_xor(L, 32, kWave);
+    const float mn = fmaxf(m, M);
+    const float a = exp_f(m - mn), c = exp_f(M - mn);
+    l = l * a + L * c;
+    m = mn;
+    if (jq < K1) {
+#pragma unroll
+      for (int pt = 0; pt < 4; ++pt)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) wsm[wave][jq][pt * 16 + 4 * (lane / 16) + i] = sc[pt][i] * c;
+    }
+    // values: every lane rescales its accumulators by query j's factor (held
+    // by lane j) and adds the tile's weighted value rows
 #pragma unroll
     for (int j = 0; j < K1; ++j) {
-      const bool ok = valid && pp <= pos0 + j;  // causal: query j sees positions up to pos0 + j
-      const float sj = ok ? s[j] * scale : kNegBig;
-      const float M = wave_max(sj);
-      const float e = ok ? exp_f(sj - M) : 0.0f;
-      const float L = wave_sum(e);
-      const float mn = fmaxf(m[j], M);
-      const float a = exp_f(m[j] - mn), c = exp_f(M - mn);
-      l[j] = l[j] * a + L * c;
-      acc[j][0] *= a;
-      acc[j][1] *= a;
-      m[j] = mn;
-      w[j] = e * c;
+      const float aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), j));
+      acc[j][0] *= aj;
+      acc[j][1] *= aj;
     }
-    const int n = min(kPosTile, len - tile * kPosTile);
-    const bf16_t* vrow = vc + static_cast<int64_t>(tile * kPosTile) * kHeadDim + 2 * lane;
-    for (int q = 0; q < n; ++q) {
-      const uint32_t vv = *reinterpret_cast<const uint32_t*>(vrow + static_cast<int64_t>(q) * kHeadDim);
-      const float v0 = __uint_as_float(vv << 16), v1 = __uint_as_float(vv & 0xffff0000u);
+#pragma unroll
+    for (int q4 = 0; q4 < kPosTile; q4 += 4) {
 #pragma unroll
       for (int j = 0; j < K1; ++j) {
-        const float wq = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(w[j]), q));
-        acc[j][0] = fmaf(wq, v0, acc[j][0]);
-        acc[j][1] = fmaf(wq, v1, acc[j][1]);
+        const float4 wq = *reinterpret_cast<const float4*>(&wsm[wave][j][q4]);
+        const float ws[4] = {wq.x, wq.y, wq.z, wq.w};
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          const uint32_t v = vv[q4 + r];
+          acc[j][0] = fmaf(ws[r], __uint_as_float(v << 16), acc[j][0]);
+          acc[j][1] = fmaf(ws[r], __uint_as_float(v & 0xffff0000u), acc[j][1]);
+        }
       }
     }
   }
   // the four wavefronts' states -> one partial per query
-  if (lane == 0) {
-#pragma unroll
-    for (int j = 0; j < K1; ++j) {
-      wm[wave][j] = m[j];
-      wl[wave][j] = l[j];
-    }
+  if (lane < K1) {
+    wm[wave][lane] = m;
+    wl[wave][lane] = l;
   }
 #pragma unroll
   for (int j = 0; j < K1; ++j) {
@@ -145,41 +175,45 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
   float* out = p.part + ((static_cast<int64_t>(b) * p.nh + h) * p.G + g) * K1 * kPartStride;
   for (int i = threadIdx.x; i < K1 * kHeadDim; i += kBlock) {
     const int j = i / kHeadDim, dd = i % kHeadDim;
-    const float M = fmaxf(fmaxf(wm[0][j], wm[1][j]), fmaxf(wm[2][j], wm[3][j]));
-    float L = 0.0f, A = 0.0f;
+    const float Mx = fmaxf(fmaxf(wm[0][j], wm[1][j]), fmaxf(wm[2][j], wm[3][j]));
+    float Ls = 0.0f, A = 0.0f;
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
-      const float f = exp_f(wm[q][j] - M);
-      L += f * wl[q][j];
+      const float f = exp_f(wm[q][j] - Mx);
+      Ls += f * wl[q][j];
       A += f * wacc[q][j][dd];
     }
     out[j * kPartStride + 2 + dd] = A;
     if (dd == 0) {
-      out[j * kPartStride] = M;
-      out[j * kPartStride + 1] = L;
+      out[j * kPartStride] = Mx;
+      out[j * kPartStride + 1] = Ls;
     }
   }
 }
 
-// One workgroup per query row: merge the G partials of each head, divide,
-// round to bfloat16.
-__global__ __launch_bounds__(kBlock) void k_attn_combine(AttnParams p) {
-  const int t = blockIdx.x, b = t / p.K1, j = t % p.K1;
-  const int H = p.nh * kHeadDim;
-  for (int i = threadIdx.x; i < H; i += kBlock) {
-    const int h = i / kHeadDim, dd = i % kHeadDim;
-    const float* part = p.part + ((static_cast<int64_t>(b) * p.nh + h) * p.G) * p.K1 * kPartStride + j * kPartStride;
-    float M = kNegBig;
-    for (int g = 0; g < p.G; ++g) M = fmaxf(M, part[static_cast<int64_t>(g) * p.K1 * kPartStride]);
-    float L = 0.0f, A = 0.0f;
-    for (int g = 0; g < p.G; ++g) {
-      const float* pg = part + static_cast<int64_t>(g) * p.K1 * kPartStride;
-      const float f = exp_f(pg[0] - M);
-      L += f * pg[1];
-      A += f * pg[2 + dd];
-    }
-    p.ctx[static_cast<int64_t>(t) * H + i] = f32_to_bf16(A / L);
+// One 128-thread workgroup per (query row, head), a thread per dimension:
+// merge the partials of the groups that hold positions, divide, round.
+__global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnParams p) {
+  __shared__ float sm[64], sf[64];
+  const int t = blockIdx.x, h = blockIdx.y, b = t / p.K1, j = t % p.K1;
+  const int dd = threadIdx.x;
+  const int len = clamped_pos(p, b, p.K1) + p.K1;
+  const int ng = used_groups(len, p.G);
+  const float* part = p.part + ((static_cast<int64_t>(b) * p.nh + h) * p.G) * p.K1 * kPartStride + j * kPartStride;
+  const int64_t gs = static_cast<int64_t>(p.K1) * kPartStride;
+  if (dd < ng) sm[dd] = part[dd * gs];
+  __syncthreads();
+  float M = kNegBig;
+  for (int g = 0; g < ng; ++g) M = fmaxf(M, sm[g]);
+  if (dd < ng) sf[dd] = exp_f(sm[dd] - M);
+  __syncthreads();
+  float L = 0.0f, A = 0.0f;
+#pragma unroll 8
+  for (int g = 0; g < ng; ++g) {
+    L = fmaf(sf[g], part[g * gs + 1], L);
+    A = fmaf(sf[g], part[g * gs + 2 + dd], A);
   }
+  p.ctx[static_cast<int64_t>(t) * (p.nh * kHeadDim) + h * kHeadDim + dd] = f32_to_bf16(A / L);
 }
 
 }  // namespace
@@ -192,6 +226,17 @@ int attn_groups(const Dims& d, int B, int nh) {
 size_t attn_part_floats(int T, int nh, int G) { return static_cast<size_t>(T) * nh * G * kPartStride; }
 
 hipError_t launch_attention(const Dims& d, const AttnParams& p, hipStream_t s) {
+  const hipError_t e = launch_attention_split(d, p, s);
+  return e != hipSuccess ? e : launch_attention_combine(p, s);
+}
+
+hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s) {
+  if (p.G > 64) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_attn_combine, dim3(p.B * p.K1, p.nh), dim3(kHeadDim), 0, s, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_attention_split(const Dims& d, const AttnParams& p, hipStream_t s) {
   if (p.K1 < 1 || p.K1 > kMaxK1 || p.B < 1 || p.G < 1 || p.P < p.K1 || d.H != p.nh * kHeadDim)
     return hipErrorInvalidValue;
   const dim3 grid(p.G, p.nh, p.B);
@@ -206,9 +251,6 @@ hipError_t launch_attention(const Dims& d, const AttnParams& p, hipStream_t s) {
     case 8: hipLaunchKernelGGL(k_attn_split<8>, grid, dim3(kBlock), 0, s, p); break;
     default: return hipErrorInvalidValue;
   }
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(k_attn_combine, dim3(p.B * p.K1), dim3(kBlock), 0, s, p);
   return hipGetLastError();
 }
 

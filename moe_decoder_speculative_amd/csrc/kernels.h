@@ -113,7 +113,9 @@ struct AttnParams {
 };
 int attn_groups(const Dims& d, int B, int nh);
 size_t attn_part_floats(int T, int nh, int G);
-hipError_t launch_attention(const Dims& d, const AttnParams& p, hipStream_t s);
+hipError_t launch_attention(const Dims& d, const AttnParams& p, hipStream_t s);          // split + combine
+hipError_t launch_attention_split(const Dims& d, const AttnParams& p, hipStream_t s);
+hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s);
 
 // Grouped GEMM for prefill-sized token counts (MFMA, LDS-staged tiles).
 struct GemmTileParams {
