@@ -434,8 +434,7 @@ def bench_draft(args, name, torch, np, synth, binding, VerifyModel, to_device):
     gpu_ms_call = ev.elapsed_ms(g0, g1) / n
     kern_ms = sorted(ev.elapsed_ms(b, a) for b, a in zip(before, after))
     kern_avg_ms = sum(kern_ms) / len(kern_ms)
-    attn_ms = sorted(ev.elapsed_ms(b, a) for b, a in zip(abefore, aafter))
-    for e in before + after + abefore + aafter + [g0, g1]:
+    for e in before + after + [g0, g1]:
         ev.destroy(e)
     kname = "k_lmhead_stream" if B <= 16 else ("k_lmhead_wide" if B <= 128 else "k_lmhead_mfma")
     kbytes = draft_head_bytes(H, Vd, B)
@@ -675,7 +674,8 @@ def main():
         attn_roof = {"bound": "hbm", "achieved": aach, "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": aach / HBM_PEAK_GBS, "kernel": "k_attn_split", "bytes_per_launch": abytes,
                      "avg_us": aavg * 1e3, "median_us": attn_ms[len(attn_ms) // 2] * 1e3,
-                     "launches_timed": len(attn_ms), "traffic": traffic_from_profiles("k_attention.hip", w.name)}
+                     "launches_timed": len(attn_ms),
+                     "traffic": traffic_from_profiles("k_attention.hip", f"{w.name}:k_attn_split")}
     sbytes = step_bytes(w, touched) + attn_step_bytes(w, positions_np)
     sflops = step_flops(w)
     if w.n_heads:  # projections and the q.k / p.v products over the cached rows
