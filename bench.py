@@ -256,9 +256,32 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
     (their c includes the draft head).  The drafts of random weights are never
     accepted, so tau_K is the expected count at acceptance p, not this run's."""
     from moe_decoder_speculative_amd.model import DraftModel
+    stream = torch.cuda.Stream()
+    sh = stream.cuda_stream
     B = w0.B
     p = w0.accept_p
-    model = VerifyModel(w0, weights, max_tokens=B * 4, copies=copies)
+    model = VerifyModel(w0, weights, max_tokens=B * 4, copies=copies, max_seqs=B)
+    positions = None
+    if w0.n_heads:  # every copy's caches hold the same prompt rows
+        pos_np = synth.kv_positions(w0)
+        for l in range(w0.L):
+            for b in range(B):
+                k, v = synth.kv_prefix(w0, l, b, int(pos_np[b]))
+                for c in range(copies):
+                    model.kv_write(l, b, k, v, copy=c)
+        positions = to_device(pos_np)
+
+    def vstep(hidden, drafts, K, committed, counts, aux=None, c=0):
+        if positions is not None:
+            model.step_kv(hidden, drafts, positions, B, K, committed, counts, aux, stream=sh, copy=c)
+        else:
+            model.step(hidden, drafts, B, K, committed, counts, aux, stream=sh, copy=c)
+
+    def vgraph(c, hidden, drafts, K, committed, counts):
+        if positions is not None:
+            return binding.moe_verify_graph_create_kv(model.ctxs[c], hidden, drafts, positions, B, K, committed,
+                                                      counts, sh)
+        return binding.moe_verify_graph_create(model.ctxs[c], hidden, drafts, B, K, committed, counts, sh)
     # the draft workload of the same batch and shapes (whole-vocabulary head unless --draft names one)
     dname = args.draft or next((n for n, d in synth.DRAFT_WORKLOADS.items()
                                 if d.B == B and d.head_rows == 0 and synth.WORKLOADS[d.base].H == w0.H
@@ -269,8 +292,6 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
         dw = synth.gen_draft_weights(dwl, w0, weights["lm_head"])
         dms = [DraftModel(model, dwl.Id, dw, max_batch=B, k_max=3, copy=c) for c in range(copies)]
         del dw
-    stream = torch.cuda.Stream()
-    sh = stream.cuda_stream
     ev = HipEvents()
     rows = []
     for K in range(4):
@@ -278,7 +299,7 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
         hidden = to_device(hidden_np[:T])
         committed, counts = model.alloc_outputs(B, K)
         aux = model.alloc_aux(T, with_hidden=False)
-        model.step(hidden, to_device(np.zeros((B, K), np.int32)) if K else None, B, K, committed, counts, aux)
+        vstep(hidden, to_device(np.zeros((B, K), np.int32)) if K else None, K, committed, counts, aux)
         torch.cuda.synchronize()
         wk = w0.with_(K=K, T=T)
         drafts = to_device(synth.make_drafts(wk, aux["tstar"].cpu().numpy().reshape(B, K + 1))) if K else None
@@ -299,10 +320,8 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
             ev.destroy(b)
             return ms * 1e3
 
-        eager_us = timed(lambda c: model.step(hidden, drafts, B, K, committed, counts, stream=sh, copy=c),
-                         args.steps)
-        graphs = [binding.moe_verify_graph_create(model.ctxs[c], hidden, drafts, B, K, committed, counts, sh)
-                  for c in range(copies)]
+        eager_us = timed(lambda c: vstep(hidden, drafts, K, committed, counts, c=c), args.steps)
+        graphs = [vgraph(c, hidden, drafts, K, committed, counts) for c in range(copies)]
         try:
             graph_us = timed(lambda c: binding.moe_verify_graph_launch(graphs[c], sh), args.steps)
         finally:
@@ -314,8 +333,7 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
         if dms and K > 0:
             row["draft_eager_us"] = round(timed(lambda c: dms[c].step(hidden, committed, counts, K + 1, B, K, drafts,
                                                                       stream=sh), args.steps), 2)
-            graphs = [binding.moe_verify_graph_create(model.ctxs[c], hidden, drafts, B, K, committed, counts, sh)
-                      for c in range(copies)]
+            graphs = [vgraph(c, hidden, drafts, K, committed, counts) for c in range(copies)]
             dgraphs = [binding.moe_draft_graph_create(dms[c].ctx, hidden, committed, counts, K + 1, B, K, drafts,
                                                       None, sh) for c in range(copies)]
             try:
@@ -323,7 +341,7 @@ def cost_model(args, w0, weights, hidden_np, copies, torch, np, synth, binding, 
                                                     args.steps), 2)
 
                 def loop_eager(c):
-                    model.step(hidden, drafts, B, K, committed, counts, stream=sh, copy=c)
+                    vstep(hidden, drafts, K, committed, counts, c=c)
                     dms[c].step(hidden, committed, counts, K + 1, B, K, drafts, stream=sh)
 
                 def loop_graph(c):

@@ -268,6 +268,12 @@ typedef struct moe_verify_graph moe_verify_graph;
 int moe_verify_graph_create(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
                             int32_t B, int32_t K, int32_t* committed, int32_t* counts,
                             void* hip_stream, moe_verify_graph** out);
+/* The same for moe_verify_step_kv (a context with attention): the captured
+ * step reads `positions` at every launch, so the caller may advance them
+ * between launches. */
+int moe_verify_graph_create_kv(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
+                               const int32_t* positions, int32_t B, int32_t K, int32_t* committed,
+                               int32_t* counts, void* hip_stream, moe_verify_graph** out);
 int moe_verify_graph_launch(moe_verify_graph* graph, void* hip_stream);
 void moe_verify_graph_destroy(moe_verify_graph* graph);
 

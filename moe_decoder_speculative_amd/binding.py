@@ -18,7 +18,8 @@ MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_verify_step_kv",
             "moe_verify_kv_cache", "moe_block_forward",
-            "moe_verify_graph_create", "moe_verify_graph_launch", "moe_verify_graph_destroy",
+            "moe_verify_graph_create", "moe_verify_graph_create_kv", "moe_verify_graph_launch",
+            "moe_verify_graph_destroy",
             "moe_verify_set_stage_events", "moe_verify_destroy", "moe_verify_last_error",
             "moe_draft_init", "moe_draft_step", "moe_draft_graph_create", "moe_draft_set_stage_events",
             "moe_draft_destroy")
@@ -91,6 +92,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_block_forward.restype = ctypes.c_int
     lib.moe_verify_graph_create.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp, ctypes.POINTER(vp)]
     lib.moe_verify_graph_create.restype = ctypes.c_int
+    lib.moe_verify_graph_create_kv.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, vp, ctypes.POINTER(vp)]
+    lib.moe_verify_graph_create_kv.restype = ctypes.c_int
     lib.moe_verify_graph_launch.argtypes = [vp, vp]
     lib.moe_verify_graph_launch.restype = ctypes.c_int
     lib.moe_verify_graph_destroy.argtypes = [vp]
@@ -197,6 +200,16 @@ def moe_verify_graph_create(ctx: int, hidden, drafts, B: int, K: int, committed,
     out = ctypes.c_void_p()
     _check(load_library().moe_verify_graph_create(ctx, _ptr(hidden), _ptr(drafts), B, K, _ptr(committed),
                                                   _ptr(counts), _stream(stream), ctypes.byref(out)))
+    return out.value
+
+
+def moe_verify_graph_create_kv(ctx: int, hidden, drafts, positions, B: int, K: int, committed, counts,
+                               stream) -> int:
+    """Capture one moe_verify_step_kv on `stream` into a graph handle."""
+    out = ctypes.c_void_p()
+    _check(load_library().moe_verify_graph_create_kv(ctx, _ptr(hidden), _ptr(drafts), _ptr(positions), B, K,
+                                                     _ptr(committed), _ptr(counts), _stream(stream),
+                                                     ctypes.byref(out)))
     return out.value
 
 

@@ -693,6 +693,21 @@ int moe_verify_graph_create(moe_verify_ctx* ctx, const void* hidden, const int32
       out);
 }
 
+int moe_verify_graph_create_kv(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
+                               const int32_t* positions, int32_t B, int32_t K, int32_t* committed, int32_t* counts,
+                               void* hip_stream, moe_verify_graph** out) {
+  if (!out) return fail(MOE_EINVAL, "out is NULL");
+  *out = nullptr;
+  if (!ctx) return fail(MOE_EINVAL, "ctx is NULL");
+  if (!positions) return fail(MOE_EINVAL, "positions is NULL");
+  for (int i = 0; i < MOE_STAGE_COUNT; ++i)
+    if (ctx->ev_before[i] || ctx->ev_after[i]) return fail(MOE_EINVAL, "a timing hook is set; clear it first");
+  return moe::api::capture_graph(
+      hip_stream,
+      [&]() { return step_impl(ctx, hidden, drafts, positions, B, K, committed, counts, nullptr, hip_stream); },
+      out);
+}
+
 int moe_verify_graph_launch(moe_verify_graph* graph, void* hip_stream) {
   if (!graph) return fail(MOE_EINVAL, "graph is NULL");
   MOE_HIP(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(hip_stream)));

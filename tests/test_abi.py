@@ -189,3 +189,13 @@ def test_step_kv_and_cache_reject_null_arguments():
     assert rc == B.MOE_EINVAL and "positions" in B.moe_verify_last_error()
     k, v = ctypes.c_void_p(), ctypes.c_void_p()
     assert lib.moe_verify_kv_cache(None, ctypes.byref(k), ctypes.byref(v)) == B.MOE_EINVAL
+
+
+def test_graph_kv_rejects_null_arguments():
+    lib = B.load_library()
+    out = ctypes.c_void_p(1)
+    rc = lib.moe_verify_graph_create_kv(None, FAKE, FAKE, FAKE, 1, 3, FAKE, FAKE, FAKE, ctypes.byref(out))
+    assert rc == B.MOE_EINVAL and out.value is None
+    rc = lib.moe_verify_graph_create_kv(ctypes.c_void_p(8), FAKE, FAKE, None, 1, 3, FAKE, FAKE, FAKE,
+                                        ctypes.byref(out))
+    assert rc == B.MOE_EINVAL and "positions" in B.moe_verify_last_error()

@@ -188,3 +188,52 @@ def _full(w, sample):
         parity.say(f"[attn full] {w.name} ok: {msg}")
     finally:
         vm.close()
+
+
+def test_attention_graph_replay_matches_eager():
+    """moe_verify_graph_create_kv: a captured step with attention replayed four
+    times, eager steps of the same context between the replays; committed
+    tokens, counts and every cache row equal the eager step's, bit for bit."""
+    torch = _torch()
+    from moe_decoder_speculative_amd import binding
+    B, K, L, P = 4, 3, 2, 64
+    w, positions = _small_case(B, K, L, P, seed=707)
+    parity.say(f"[attn graph] B={B} K={K} L={L} P={P} entry=moe_verify_graph_create_kv/moe_verify_graph_launch")
+    weights = synth.gen_weights(w)
+    hidden_np = synth.to_storage(synth.HiddenNoise(w).draw(w.T), w.dtype)
+    kv0, bits = _prefix(w, positions)
+    drafts_np = _drafts(w, weights, hidden_np, positions, kv0)
+    vm = VerifyModel(w, weights, max_tokens=w.T, max_seqs=B)
+    g = None
+    try:
+        for (l, b), (k, v) in bits.items():
+            vm.kv_write(l, b, k, v)
+        hidden, drafts, pos = to_device(hidden_np), to_device(drafts_np), to_device(np.asarray(positions, np.int32))
+        c_ref, n_ref = vm.alloc_outputs(B, K)
+        vm.step_kv(hidden, drafts, pos, B, K, c_ref, n_ref)
+        torch.cuda.synchronize()
+        kv_ref = _gpu_kv(vm, w, range(B))
+        stream = torch.cuda.Stream()
+        c_g, n_g = vm.alloc_outputs(B, K)
+        torch.cuda.synchronize()
+        g = binding.moe_verify_graph_create_kv(vm.ctx, hidden, drafts, pos, B, K, c_g, n_g, stream)
+        c_e, n_e = vm.alloc_outputs(B, K)
+        for rep in range(4):
+            c_g.fill_(-5)
+            n_g.fill_(-5)
+            torch.cuda.synchronize()
+            binding.moe_verify_graph_launch(g, stream)
+            stream.synchronize()
+            assert torch.equal(c_g, c_ref) and torch.equal(n_g, n_ref), f"replay {rep}: outputs differ"
+            kv = _gpu_kv(vm, w, range(B))
+            for l in range(L):
+                assert np.array_equal(kv[l][0], kv_ref[l][0]) and np.array_equal(kv[l][1], kv_ref[l][1]), \
+                    f"replay {rep}: layer {l} cache differs"
+            vm.step_kv(hidden, drafts, pos, B, K, c_e, n_e)
+            torch.cuda.synchronize()
+            assert torch.equal(c_e, c_ref)
+        parity.say(f"[attn graph] ok: 4 replays equal to eager, counts {n_ref.cpu().tolist()}")
+    finally:
+        if g:
+            binding.moe_verify_graph_destroy(g)
+        vm.close()
