@@ -120,7 +120,12 @@ __device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, i
   }
 }
 
-template <typename ST, int KQ>  // KQ = H / 128: router k-steps per wavefront (bf16)
+// EARLY: no combine in this launch (the first block of a step, or the MoE
+// block after an attention sublayer), so phase 1 is light and the router
+// fragments are requested at kernel start, their latency overlapping the row
+// loads; with a combine they are requested after phase 1 (to keep phase 1
+// within 128 registers).
+template <typename ST, int KQ, bool EARLY>  // KQ = H / 128: router k-steps per wavefront (bf16)
 __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterParams p, int rows) {
   // dynamic LDS: [0, 16 KiB) router partials zp[4][16][64] (reused by the sort);
   // then bf16 xh operand tiles [H/32][64 lanes][8] or f32 xh rows [16][H]
@@ -155,6 +160,8 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
     }
   };
 
+  if constexpr (EARLY) load_router();
+
   // ------------------------------------------------------------ phase 1
   if (has_row) {
     float x[CPL][4];
@@ -169,7 +176,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
         if (p.norm) gg[c] = *reinterpret_cast<const Vec4<ST>*>(gam + 4 * ch);
       }
     }
-    if (p.combine) {
+    if (!EARLY && p.combine) {
       // rows to add, in order: shared experts, then routed by ascending expert
       const int nrows = d.S + k;
       int ids[kMaxTopK];
@@ -286,7 +293,7 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
     }
   }
   if (!p.route) return;
-  load_router();
+  if constexpr (!EARLY) load_router();
   const int nrows = min(rows, T - t0);
   if constexpr (sizeof(ST) == 2) {
     // rows of this workgroup past T: zero operand lanes so MFMA reads defined values
@@ -386,7 +393,10 @@ hipError_t launch_kq(const Dims& d, const NormRouterParams& p, hipStream_t s) {
   const dim3 grid((p.T + rows - 1) / rows);
   const size_t xs = p.route ? (sizeof(ST) == 2 ? static_cast<size_t>(d.H) * 32 : static_cast<size_t>(d.H) * kRows * 4) : 0;
   const size_t smem = 4 * kRows * 64 * sizeof(float) + xs;
-  hipLaunchKernelGGL((k_norm_router<ST, KQ>), grid, dim3(kThreads), smem, s, d, p, rows);
+  if (!p.combine && p.route && sizeof(ST) == 2)
+    hipLaunchKernelGGL((k_norm_router<ST, KQ, true>), grid, dim3(kThreads), smem, s, d, p, rows);
+  else
+    hipLaunchKernelGGL((k_norm_router<ST, KQ, false>), grid, dim3(kThreads), smem, s, d, p, rows);
   return hipGetLastError();
 }
 
