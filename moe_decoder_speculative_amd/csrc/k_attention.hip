@@ -12,8 +12,10 @@
 //   softmax: per query the tile's maximum and sum (16 values in a lane, then
 //           across the four lane groups), folded into a running (max, sum)
 //           with the usual rescaling;
-//   values:  float32, lane = two head dimensions, each position's value row is
-//           one coalesced 256-byte read, its weights broadcast through LDS.
+//   values:  float32; a lane reads 16 bytes (eight dimensions) of every fourth
+//           value row, so a tile is 16 loads and all 32 of a tile's loads fit
+//           in flight at once; weights come from LDS, and the four lane
+//           groups' partial sums are added once at the end.
 // The four wavefronts' states meet in LDS and the workgroup writes one
 // partial (max, sum, weighted values) per query; k_attn_combine merges the G
 // partials of every (row, head) and rounds the result to bfloat16.  Reading of
@@ -77,9 +79,13 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
   const int jq = lane % 16;                    // the query this lane's scores belong to
 
   float m = kNegBig, l = 0.0f;  // running max and sum of query jq
-  float acc[K1][2];
+  // weighted values: lane sums dimensions 8 (lane % 16) .. + 8 over the rows
+  // 4 i + lane / 16 of each tile; the four lane groups are added at the end
+  float acc[K1][8];
 #pragma unroll
-  for (int j = 0; j < K1; ++j) acc[j][0] = acc[j][1] = 0.0f;
+  for (int j = 0; j < K1; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[j][e] = 0.0f;
   for (int tile = g * 4 + wave; tile * kPosTile < len; tile += p.G * 4) {
     const int t0 = tile * kPosTile;
     // every load of the tile first: key fragments (A operand: row = position
@@ -93,10 +99,13 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
 #pragma unroll
       for (int ks = 0; ks < 4; ++ks) kf[pt][ks] = *reinterpret_cast<const uint4*>(krow + ks * 32 + (lane / 16) * 8);
     }
-    uint32_t vv[kPosTile];
+    // value rows 4 i + lane / 16, 16 bytes a lane: 16 loads cover the tile, so
+    // a tile's 32 loads stay under the per-wavefront limit of loads in flight
+    uint4 vv[kPosTile / 4];
 #pragma unroll
-    for (int q = 0; q < kPosTile; ++q)
-      vv[q] = *reinterpret_cast<const uint32_t*>(vc + static_cast<int64_t>(min(t0 + q, len - 1)) * kHeadDim + 2 * lane);
+    for (int i = 0; i < kPosTile / 4; ++i)
+      vv[i] = *reinterpret_cast<const uint4*>(
+          vc + static_cast<int64_t>(min(t0 + 4 * i + lane / 16, len - 1)) * kHeadDim + 8 * (lane % 16));
     // scores: sc[pt][i] = q_jq . k at position t0 + 16 pt + 4 (lane / 16) + i
     f32x4_t sc[4];
 #pragma unroll
@@ -143,33 +152,41 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
 #pragma unroll
     for (int j = 0; j < K1; ++j) {
       const float aj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(a), j));
-      acc[j][0] *= aj;
-      acc[j][1] *= aj;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[j][e] *= aj;
     }
 #pragma unroll
-    for (int q4 = 0; q4 < kPosTile; q4 += 4) {
+    for (int i = 0; i < kPosTile / 4; ++i) {
+      const float vf[8] = {__uint_as_float(vv[i].x << 16), __uint_as_float(vv[i].x & 0xffff0000u),
+                           __uint_as_float(vv[i].y << 16), __uint_as_float(vv[i].y & 0xffff0000u),
+                           __uint_as_float(vv[i].z << 16), __uint_as_float(vv[i].z & 0xffff0000u),
+                           __uint_as_float(vv[i].w << 16), __uint_as_float(vv[i].w & 0xffff0000u)};
 #pragma unroll
       for (int j = 0; j < K1; ++j) {
-        const float4 wq = *reinterpret_cast<const float4*>(&wsm[wave][j][q4]);
-        const float ws[4] = {wq.x, wq.y, wq.z, wq.w};
+        const float wq = wsm[wave][j][4 * i + lane / 16];
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-          const uint32_t v = vv[q4 + r];
-          acc[j][0] = fmaf(ws[r], __uint_as_float(v << 16), acc[j][0]);
-          acc[j][1] = fmaf(ws[r], __uint_as_float(v & 0xffff0000u), acc[j][1]);
-        }
+        for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(wq, vf[e], acc[j][e]);
       }
     }
   }
+  // the four lane groups' partial sums of every dimension
+#pragma unroll
+  for (int j = 0; j < K1; ++j)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      acc[j][e] += __shfl_xor(acc[j][e], 16, kWave);
+      acc[j][e] += __shfl_xor(acc[j][e], 32, kWave);
+    }
   // the four wavefronts' states -> one partial per query
   if (lane < K1) {
     wm[wave][lane] = m;
     wl[wave][lane] = l;
   }
+  if (lane < 16) {
 #pragma unroll
-  for (int j = 0; j < K1; ++j) {
-    wacc[wave][j][2 * lane] = acc[j][0];
-    wacc[wave][j][2 * lane + 1] = acc[j][1];
+    for (int j = 0; j < K1; ++j)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) wacc[wave][j][8 * lane + e] = acc[j][e];
   }
   __syncthreads();
   float* out = p.part + ((static_cast<int64_t>(b) * p.nh + h) * p.G + g) * K1 * kPartStride;
