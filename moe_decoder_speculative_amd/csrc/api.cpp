@@ -312,6 +312,7 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->perm))) return r;
   if ((r = ctx_alloc_t(c, E * sizeof(int), &c->active))) return r;
   if ((r = ctx_alloc_t(c, 16, &c->n_active))) return r;
+  if ((r = ctx_alloc_t(c, E * sizeof(int4), &c->desc))) return r;
   if ((r = ctx_alloc(c, (rows + 1) * I * es, &c->act))) return r;
   MOE_HIP(hipMemsetAsync(c->act + rows * I * es, 0, I * es, s));
   if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->y))) return r;
@@ -482,10 +483,11 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     pp.perm = aux && aux->perm ? aux->perm + li * T * k : c->perm;
     pp.active = c->active;
     pp.n_active = c->n_active;
+    pp.desc = c->desc;
     const bool fused_sort = T <= moe::norm_router_sort_limit();
     if (fused_sort) {
       // the (single) norm/router workgroup sorts the pairs
-      nr.sort = moe::SortParams{idx, pp.cnt, pp.off, pp.perm, pp.active, pp.n_active, 1};
+      nr.sort = moe::SortParams{idx, pp.cnt, pp.off, pp.perm, pp.active, pp.n_active, pp.desc, 1};
     }
     MOE_HIP(moe::launch_norm_router(d, nr, s));
     if (!fused_sort) MOE_HIP(moe::launch_permute(d, pp, s));
@@ -497,6 +499,7 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     ep.perm = pp.perm;
     ep.active = c->active;
     ep.n_active = c->n_active;
+    ep.desc = c->desc;
     ep.w_gate = c->gate + l * c->gate_layer;
     ep.w_up = c->up + l * c->gate_layer;
     ep.w_down = c->down + l * c->down_layer;

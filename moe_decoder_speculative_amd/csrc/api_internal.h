@@ -40,6 +40,7 @@ struct moe_verify_ctx {
   int* perm = nullptr;      // [tw*k]
   int* active = nullptr;    // [E]
   int* n_active = nullptr;  // [1]
+  int4* desc = nullptr;     // [E] routed slot descriptors
   char* act = nullptr;      // [tw*(k+S)][I] storage
   float* y = nullptr;       // [tw*(k+S)][H]
   unsigned long long* keys = nullptr;  // [kKeySlots][tw]

@@ -36,21 +36,23 @@ struct SlotInfo {
   int shared;    // shared slot index or -1
 };
 
+// A shared slot needs no lookup; a routed slot reads its one descriptor
+// (expert, tokens, first pair), written by the sort.
 __device__ __forceinline__ bool slot_info(const Dims& d, const ExpertParams& p, int slot, SlotInfo& si) {
-  const int nact = *p.n_active;
-  if (slot >= d.S + nact) return false;
   if (slot < d.S) {
     si.expert = d.E + slot;
     si.ntok = p.T;
     si.base = 0;
     si.shared = slot;
-  } else {
-    const int e = p.active[slot - d.S];
-    si.expert = e;
-    si.ntok = p.cnt[e];
-    si.base = p.off[e];
-    si.shared = -1;
+    return true;
   }
+  if (slot >= d.S + d.E) return false;
+  const int4 ds = p.desc[slot - d.S];
+  if (ds.x < 0) return false;
+  si.expert = ds.x;
+  si.ntok = ds.y;
+  si.base = ds.z;
+  si.shared = -1;
   return true;
 }
 
@@ -348,13 +350,18 @@ __global__ __launch_bounds__(kBlock) void k_down_f32(Dims d, ExpertParams p) {
 // token tiles per workgroup, at most four ways.
 int token_split(int T) { return std::min(4, std::max(1, (T + 2 * kTile - 1) / (2 * kTile))); }
 // grid for R row tiles: the shared part (whole groups of 8 pairs, `split`
-// ways), then one workgroup per routed (slot, row tile)
-int split_grid(const Dims& d, int R, int split) { return (d.S * R + 7) / 8 * 8 * split + d.E * R; }
+// ways), then one workgroup per routed (slot, row tile) -- for at most T*k
+// routed slots, as many as T tokens can activate (the rest would only read
+// the active count and exit, holding a CU slot for a memory round trip)
+int split_grid(const Dims& d, int R, int split, int T) {
+  const int routed = std::min(d.E, std::max(0, T) * d.k);
+  return (d.S * R + 7) / 8 * 8 * split + routed * R;
+}
 
 template <int KW>
 hipError_t up_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
   const int split = token_split(p.T);
-  const int grid = split_grid(d, d.I / kTile, split);
+  const int grid = split_grid(d, d.I / kTile, split, p.T);
   hipLaunchKernelGGL(k_up_mfma<KW>, dim3(grid), dim3(kBlock), 0, s, d, p, split);
   return hipGetLastError();
 }
@@ -364,10 +371,10 @@ hipError_t down_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
   constexpr int RPW = 2;
   const int split = token_split(p.T);
   if ((d.H / kTile) % RPW == 0) {
-    const int grid = split_grid(d, d.H / (kTile * RPW), split);
+    const int grid = split_grid(d, d.H / (kTile * RPW), split, p.T);
     hipLaunchKernelGGL((k_down_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p, split, EpiParams{});
   } else {
-    const int grid = split_grid(d, d.H / kTile, split);
+    const int grid = split_grid(d, d.H / kTile, split, p.T);
     hipLaunchKernelGGL((k_down_mfma<KW, 1>), dim3(grid), dim3(kBlock), 0, s, d, p, split, EpiParams{});
   }
   return hipGetLastError();
@@ -380,7 +387,7 @@ hipError_t linear_launch(const Dims& d, const ExpertParams& p, const EpiParams& 
   constexpr int RPW = 2;
   if (d.E != 0 || d.k != 0 || d.I != d.H || d.H % (kTile * RPW) != 0 || d.H % kHeadDim != 0) return hipErrorInvalidValue;
   const int split = token_split(p.T);
-  const int grid = split_grid(d, d.H / (kTile * RPW), split);
+  const int grid = split_grid(d, d.H / (kTile * RPW), split, p.T);
   switch (d.I / (kKStep * 4)) {
     case 2: hipLaunchKernelGGL((k_down_mfma<2, RPW, EPI>), dim3(grid), dim3(kBlock), 0, s, d, p, split, e); break;
     case 4: hipLaunchKernelGGL((k_down_mfma<4, RPW, EPI>), dim3(grid), dim3(kBlock), 0, s, d, p, split, e); break;

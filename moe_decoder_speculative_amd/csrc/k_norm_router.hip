@@ -82,7 +82,15 @@ __device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, i
     if (lane < E) {
       s.cnt[lane] = c;
       s.off[lane] = incl - c;
-      if (c > 0) s.active[__popcll(act & ((1ull << lane) - 1ull))] = lane;
+      const unsigned long long below = (1ull << lane) - 1ull;
+      const unsigned long long inact = ~act & (E == 64 ? ~0ull : ((1ull << E) - 1ull));
+      if (c > 0) {
+        const int r = __popcll(act & below);
+        s.active[r] = lane;
+        s.desc[r] = make_int4(lane, c, incl - c, 0);
+      } else {
+        s.desc[__popcll(act) + __popcll(inact & below)] = make_int4(-1, 0, 0, 0);
+      }
     }
     if (lane == kWave - 1) {
       s.off[E] = incl;

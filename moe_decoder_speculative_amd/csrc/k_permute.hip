@@ -75,6 +75,8 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(int E, PermuteParams p
       p.cnt[e] = c;
       p.off[e] = incl - c;
       if (c > 0) p.active[rank] = e;
+      // every rank gets a descriptor: inactive experts rank last
+      p.desc[rank] = c > 0 ? make_int4(e, c, incl - c, 0) : make_int4(-1, 0, 0, 0);
     }
     if (e == E - 1 && lane == E - 1) {
       p.off[E] = incl;

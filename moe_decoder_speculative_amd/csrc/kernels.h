@@ -25,6 +25,7 @@ struct SortParams {
   int* perm;             // [P]
   int* active;           // [E] experts with cnt > 0, ascending
   int* n_active;         // [1]
+  int4* desc;            // [E] slot descriptors (see PermuteParams)
   int fused;             // 1: the (single) norm/router workgroup sorts in LDS
 };
 
@@ -58,6 +59,8 @@ struct PermuteParams {
   int* perm;       // [P]
   int* active;     // [E] experts with cnt > 0, busiest first; entries past n_active unused
   int* n_active;   // [1]
+  int4* desc;      // [E] routed slot i: (expert, tokens, first pair in perm, 0) of active[i];
+                   //     (-1, 0, 0, 0) past n_active -- one read tells an expert workgroup its work
 };
 hipError_t launch_permute(const Dims& d, const PermuteParams& p, hipStream_t s);
 
@@ -72,6 +75,7 @@ struct ExpertParams {
   const int* perm;       // [T*k]
   const int* active;     // [E]
   const int* n_active;   // [1]
+  const int4* desc;      // [E] routed slot descriptors (null when there are no routed experts)
   const void* w_gate;    // this layer: bf16 tiled [E+S][I/16][H/32][512]; f32 [E+S][I][H]
   const void* w_up;      // same layout as w_gate
   const void* w_down;    // bf16 tiled [E+S][H/16][I/32][512]; f32 [E+S][H][I]
