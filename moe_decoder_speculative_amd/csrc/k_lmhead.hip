@@ -504,7 +504,6 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadP
   constexpr int kUnitTiles = kWideWaves * R;
   __shared__ __align__(16) unsigned char bring[2 * kWideStageBytes];
   __shared__ uint64_t wbest[kWideWaves][NT * kTile];
-  __shared__ uint64_t run_best[NT * kTile];
   // the wavefront index as a scalar: addresses and branches that depend only
   // on it stay scalar
   const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
@@ -551,56 +550,64 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadP
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[r][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // End of a unit: per-token best (logit, lowest row) over the unit's rows.
-  // Branch-free: rows past V get key 0, and after the two butterflies the
-  // four lanes l, l+16, l+32, l+48 hold the same value and all store it.
+  // End of a unit: each lane folds its R x 4 rows of every token tile into
+  // one candidate (largest logit; on equal logits the first, which is the
+  // lowest row) and merges its key into the lane's running best; lanes and
+  // wavefronts meet once, after the last unit.  In the unit holding the end
+  // of the vocabulary, rows past V take -inf and a lane whose candidate is
+  // such a row contributes no key.
+  uint64_t lbest[NT];
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) lbest[nt] = 0ull;
   int cur_u = blockIdx.x;  // unit being accumulated
-  auto unit_end = [&]() {
-    const int u = cur_u;
-    cur_u += gridDim.x;
+  auto fold_unit = [&](auto masked) {
+    constexpr bool kMasked = decltype(masked)::value;
+    const int row0 = (cur_u * kUnitTiles + wave * R) * kTile + 4 * (lane / kTile);
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) {
-      uint64_t best = 0ull;
+      float bv = acc[0][nt][0];
+      int bj = 0;
+      if (kMasked && row0 >= d.V) bv = -__builtin_inff();
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int row = (u * kUnitTiles + wave * R + r) * kTile + 4 * (lane / kTile) + i;
-          const uint64_t valid = 0ull - static_cast<uint64_t>(row < d.V);
-          const uint64_t key = argmax_key(acc[r][nt][i], static_cast<uint32_t>(row)) & valid;
-          best = key > best ? key : best;
-          acc[r][nt][i] = 0.f;
+          if (r == 0 && i == 0) continue;
+          const int j = r * kTile + i;
+          float v = acc[r][nt][i];
+          if (kMasked && row0 + j >= d.V) v = -__builtin_inff();
+          bj = v > bv ? j : bj;
+          bv = v > bv ? v : bv;
         }
-      uint64_t o = __shfl_xor(best, 16, kWave);
-      best = o > best ? o : best;
-      o = __shfl_xor(best, 32, kWave);
-      best = o > best ? o : best;
-      wbest[wave][nt * kTile + lane % kTile] = best;
-    }
-    lds_barrier();
-    if (wave < (NT * kTile + kWave - 1) / kWave) {
-      const int t = wave * kWave + lane;
-      uint64_t b = run_best[t % (NT * kTile)];
+      uint64_t key = argmax_key(bv, static_cast<uint32_t>(row0 + bj));
+      if (kMasked && row0 + bj >= d.V) key = 0ull;
+      lbest[nt] = key > lbest[nt] ? key : lbest[nt];
 #pragma unroll
-      for (int w = 0; w < kWideWaves; ++w) {
-        const uint64_t v = wbest[w][t % (NT * kTile)];
-        b = v > b ? v : b;
-      }
-      if (t < NT * kTile) run_best[t] = b;
+      for (int r = 0; r < R; ++r) acc[r][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
+  auto unit_end = [&]() {
+    if ((cur_u + 1) * kUnitTiles * kTile > d.V) {
+      fold_unit(std::true_type{});
+    } else {
+      fold_unit(std::false_type{});
+    }
+    cur_u += gridDim.x;
+  };
 
-  if (threadIdx.x < NT * kTile) run_best[threadIdx.x] = 0ull;
-  // weight ring primed (total >= KT >= 4)
-  bf16x8_t a[P][R];
-#pragma unroll
-  for (int j = 0; j < P; ++j)
-    if (j < total) load_a_next(a[j]);
-  // activation ring: slot j holds the fragment of a step g = j mod P
-  //    (loaded for every g < total + P: rows repeat, so reads stay in bounds)
+  // activation ring first: slot j holds the fragment of a step g = j mod P
+  //    (loaded for every g < total + P: rows repeat, so reads stay in bounds);
+  // the first step then waits for its own fragment, not for the weight ring
   bf16x8_t pb[P];
 #pragma unroll
   for (int j = 0; j < P; ++j) pb[j] = load_b_next();
+  // weight ring primed, unconditionally (a conditional load would make the
+  // compiler's wait before the first stage write drain the whole ring): steps
+  // past the workgroup's last read clamped rows and are never used, and the
+  // refills below only run for steps that exist
+  bf16x8_t a[P][R];
+#pragma unroll
+  for (int j = 0; j < P; ++j) load_a_next(a[j]);
   put_b(0, pb[0]);
   pb[0] = load_b_next();
   lds_barrier();
@@ -656,11 +663,27 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadP
 #undef MOE_WIDE_QUAD
 #undef MOE_WIDE_STEP
 
-  if (static_cast<int>(threadIdx.x) < NT * kTile && static_cast<int>(threadIdx.x) < p.T &&
-      run_best[threadIdx.x] != 0ull)
-    __hip_atomic_fetch_max(p.keys + static_cast<int64_t>(blockIdx.x % kKeySlots) * p.key_stride + threadIdx.x,
-                           static_cast<unsigned long long>(run_best[threadIdx.x]), __ATOMIC_RELAXED,
-                           __HIP_MEMORY_SCOPE_AGENT);
+  // lanes l, l + 16, l + 32, l + 48 hold token l % 16's candidates of the
+  // wavefront's rows; then the wavefronts' bests meet in LDS
+#pragma unroll
+  for (int nt = 0; nt < NT; ++nt) {
+    uint64_t best = lbest[nt];
+    uint64_t o = __shfl_xor(best, 16, kWave);
+    best = o > best ? o : best;
+    o = __shfl_xor(best, 32, kWave);
+    best = o > best ? o : best;
+    if (lane < kTile) wbest[wave][nt * kTile + lane] = best;
+  }
+  lds_barrier();
+  const int t = threadIdx.x;
+  if (t < NT * kTile && t < p.T) {
+    uint64_t b = 0ull;
+#pragma unroll
+    for (int w = 0; w < kWideWaves; ++w) b = wbest[w][t] > b ? wbest[w][t] : b;
+    if (b != 0ull)
+      __hip_atomic_fetch_max(p.keys + static_cast<int64_t>(blockIdx.x % kKeySlots) * p.key_stride + t,
+                             static_cast<unsigned long long>(b), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
 }
 
 template <int NT, int R, int P>
