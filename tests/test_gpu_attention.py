@@ -4,9 +4,9 @@ with the CPU oracle, through the C ABI.
 Small shapes (two heads of 128) over several layers with ragged batches,
 K = 0, 3 and 7, cache positions from empty to the last that fits, two steps
 in a row continuing the cache (positions advanced by the committed counts);
-the full-size one-layer workloads; and sampled sequences of the 12-layer
-batch-32 step with attention (a complete verify forward of the pages'
-decoder shape).  Bar: tests/parity.py, check_attn_step_teacher_forced.
+the full-size one-layer workloads; a cache of 32,768 positions (the largest
+accepted) at full width; and sampled sequences of the 12-layer batch-32 step
+with attention (a complete verify forward of the pages' decoder shape).  Bar: tests/parity.py, check_attn_step_teacher_forced.
 """
 import numpy as np
 import pytest
@@ -159,8 +159,18 @@ def test_attention_stack12_b32_sampled():
     _full(synth.WORKLOADS["attn_stack12_b32_zipf"], [0, 21])
 
 
-def _full(w, sample):
-    positions = synth.kv_positions(w)
+@pytest.mark.slow
+def test_attention_near_max_positions():
+    """The largest cache the library accepts -- 32,768 positions, the pages'
+    position limit -- at full width (10 heads of 128): one sequence whose
+    step ends on the last cache row and one in the middle (rotary angles up
+    to ~32,767 rad, 512 position tiles in 52 groups)."""
+    w = synth.WORKLOADS["attn_b1"].with_(name="attn_maxpos", B=2, T=8, P=32768)
+    _full(w, None, positions=np.array([w.P - (w.K + 1), 17001], np.int32))
+
+
+def _full(w, sample, positions=None):
+    positions = synth.kv_positions(w) if positions is None else positions
     seqs = list(range(w.B)) if sample is None else sample
     parity.say(f"[attn full] {w.name}: B={w.B} K={w.K} L={w.L} P={w.P} sampled sequences {seqs} "
                f"positions {positions[seqs].tolist()}")
