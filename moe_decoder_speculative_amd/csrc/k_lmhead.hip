@@ -31,8 +31,9 @@ namespace {
 // ------------------------------------------------------------ acceptance ----
 // One workgroup per kAcceptSeqs sequences: every key copy of its tokens is
 // read once (all loads in flight together) and cleared, the copies are folded
-// per token in LDS, then one thread per sequence runs the acceptance.
-constexpr int kAcceptSeqs = 32;
+// per token in LDS, then one thread per sequence runs the acceptance on its
+// drafts, which it loaded with the keys (not one dependent load per draft).
+constexpr int kAcceptSeqs = 8;
 constexpr int kAcceptTok = kAcceptSeqs * 8;  // K + 1 <= 8 tokens per sequence
 
 __global__ __launch_bounds__(kBlock) void k_accept(LmHeadParams p) {
@@ -41,6 +42,10 @@ __global__ __launch_bounds__(kBlock) void k_accept(LmHeadParams p) {
   const int b0 = blockIdx.x * kAcceptSeqs;
   const int nb = min(kAcceptSeqs, p.B - b0);
   const int t0 = b0 * K1, nt = nb * K1;
+  int dr[7];  // drafts of sequence b0 + threadIdx.x (K <= 7); -1 never matches a pick
+#pragma unroll
+  for (int j = 0; j < 7; ++j)
+    dr[j] = static_cast<int>(threadIdx.x) < nb && j < p.K ? p.drafts[(b0 + threadIdx.x) * p.K + j] : -1;
   for (int t = threadIdx.x; t < nt; t += kBlock) best[t] = 0ull;
   __syncthreads();
   constexpr int kPer = kKeySlots * kAcceptTok / kBlock;
@@ -65,7 +70,12 @@ __global__ __launch_bounds__(kBlock) void k_accept(LmHeadParams p) {
     const int b = b0 + threadIdx.x;
     const unsigned long long* pk = best + threadIdx.x * K1;
     int a = 0;
-    while (a < p.K && p.drafts[b * p.K + a] == static_cast<int>(argmax_key_index(pk[a]))) ++a;
+    bool run = true;
+#pragma unroll
+    for (int j = 0; j < 7; ++j) {
+      run = run && j < p.K && dr[j] == static_cast<int>(argmax_key_index(pk[j]));
+      a += run ? 1 : 0;
+    }
     for (int j = 0; j < K1; ++j)
       p.committed[b * K1 + j] = j <= a ? static_cast<int>(argmax_key_index(pk[j])) : -1;
     p.counts[b] = a + 1;
