@@ -14,9 +14,10 @@
 //       step's normalised state;
 //   the LM-head kernel (arg-max keys) and k_draft_pick: the draft token, and
 //       for the next step the normalised embedding of that token.
-// Each row kernel is one 256-thread workgroup per sequence: the row's loads
-// are all issued before the sum of squares is reduced, and H <= 2048 gives at
-// most two 4-element chunks per thread.  The block is the page "Jina AI
+// Each row kernel is one 256-thread workgroup per sequence: the row's loads,
+// and the gains its RMSNorm multiplies by, are all issued before the sum of
+// squares is reduced (a load after the reduction is one more memory round
+// trip), and H <= 2048 gives at most two 4-element chunks per thread.  The block is the page "Jina AI
 // releases lightweight OCR model with built-in speculative decoding", section
 // "Speculative decoding without accuracy loss" (one draft block applied K
 // times); its internals are this library's reading.
@@ -76,15 +77,30 @@ __device__ __forceinline__ void block_sum2(float& a, float& b, float (*red)[kBlo
   }
 }
 
+// A gain vector's chunks of this thread, loaded with the row.
+struct Gain {
+  uint2 g[kCPB];
+};
+
+__device__ __forceinline__ Gain load_gain(const bf16_t* gamma, int nchunks) {
+  Gain r;
+#pragma unroll
+  for (int c = 0; c < kCPB; ++c) {
+    const int ch = threadIdx.x + c * kBlock;
+    r.g[c] = ch < nchunks ? *reinterpret_cast<const uint2*>(gamma + 4 * ch) : make_uint2(0u, 0u);
+  }
+  return r;
+}
+
 // dst = round(r / rms * gamma), rms = sqrt(ss / H + eps)
-__device__ __forceinline__ void store_norm(const Row& r, int nchunks, float ss, const Dims& d, const bf16_t* gamma,
+__device__ __forceinline__ void store_norm(const Row& r, int nchunks, float ss, const Dims& d, const Gain& gamma,
                                            bf16_t* dst) {
   const float rms = sqrtf(ss / static_cast<float>(d.H) + d.eps);
 #pragma unroll
   for (int c = 0; c < kCPB; ++c) {
     const int ch = threadIdx.x + c * kBlock;
     if (ch < nchunks) {
-      const uint2 g = *reinterpret_cast<const uint2*>(gamma + 4 * ch);
+      const uint2 g = gamma.g[c];
       const float gg[4] = {__uint_as_float(g.x << 16), __uint_as_float(g.x & 0xffff0000u),
                            __uint_as_float(g.y << 16), __uint_as_float(g.y & 0xffff0000u)};
       uint2 o;
@@ -116,6 +132,7 @@ __device__ __forceinline__ const bf16_t* embed_row(const DraftParams& p, const D
 __global__ __launch_bounds__(kBlock) void k_draft_in(Dims d, DraftParams p) {
   __shared__ float red[2][kBlock / kWave];
   const int b = blockIdx.x, nchunks = d.H / 4;
+  const Gain gh = load_gain(p.gamma_h, nchunks), ge = load_gain(p.gamma_e, nchunks);
   const int j = p.counts ? min(max(p.counts[b] - 1, 0), p.R - 1) : p.R - 1;
   const int64_t row = static_cast<int64_t>(b) * p.R + j;
   const int tok = p.committed[row];
@@ -124,8 +141,8 @@ __global__ __launch_bounds__(kBlock) void k_draft_in(Dims d, DraftParams p) {
   load_bf16_row(embed_row(p, d, tok), nchunks, e);
   float sh = row_sumsq(h, nchunks), se = row_sumsq(e, nchunks);
   block_sum2(sh, se, red);
-  store_norm(h, nchunks, sh, d, p.gamma_h, p.x + static_cast<int64_t>(b) * d.H);
-  store_norm(e, nchunks, se, d, p.gamma_e, p.x + static_cast<int64_t>(p.B + b) * d.H);
+  store_norm(h, nchunks, sh, d, gh, p.x + static_cast<int64_t>(b) * d.H);
+  store_norm(e, nchunks, se, d, ge, p.x + static_cast<int64_t>(p.B + b) * d.H);
 }
 
 // u = round(y0 + y1); FFN input RMSNorm(u; gamma_f)
@@ -134,6 +151,7 @@ __global__ __launch_bounds__(kBlock) void k_draft_mid(Dims d, DraftParams p) {
   const int b = blockIdx.x, nchunks = d.H / 4;
   const float* y0 = p.yp + static_cast<int64_t>(b) * d.H;
   const float* y1 = p.yp + static_cast<int64_t>(p.B + b) * d.H;
+  const Gain gf = load_gain(p.gamma_f, nchunks);
   Row u;
 #pragma unroll
   for (int c = 0; c < kCPB; ++c) {
@@ -151,7 +169,7 @@ __global__ __launch_bounds__(kBlock) void k_draft_mid(Dims d, DraftParams p) {
   store_row(u, nchunks, p.u + static_cast<int64_t>(b) * d.H);
   float ss = row_sumsq(u, nchunks), unused = 0.0f;
   block_sum2(ss, unused, red);
-  store_norm(u, nchunks, ss, d, p.gamma_f, p.uh + static_cast<int64_t>(b) * d.H);
+  store_norm(u, nchunks, ss, d, gf, p.uh + static_cast<int64_t>(b) * d.H);
 }
 
 // v = round(u + sum_s y_s) (slots in ascending order); the step output, the
@@ -159,29 +177,46 @@ __global__ __launch_bounds__(kBlock) void k_draft_mid(Dims d, DraftParams p) {
 __global__ __launch_bounds__(kBlock) void k_draft_out(Dims d, DraftParams p) {
   __shared__ float red[2][kBlock / kWave];
   const int b = blockIdx.x, nchunks = d.H / 4;
+  const Gain go = load_gain(p.gamma_o, nchunks), gh = load_gain(p.gamma_h, nchunks);
   Row v;
   load_bf16_row(p.u + static_cast<int64_t>(b) * d.H, nchunks, v);
+  // the slots' outputs, added in ascending slot order; each group of eight
+  // slots has all its loads in flight before the first add
+  constexpr int kG = 8;
+  float m[kCPB][4] = {};
+  for (int s0 = 0; s0 < p.Sf; s0 += kG) {
+    float4 y[kG][kCPB];
 #pragma unroll
-  for (int c = 0; c < kCPB; ++c) {
-    const int ch = threadIdx.x + c * kBlock;
-    if (ch < nchunks) {
-      float m[4] = {0.f, 0.f, 0.f, 0.f};
-      for (int s = 0; s < p.Sf; ++s) {
-        const float4 y = *reinterpret_cast<const float4*>(p.y + (static_cast<int64_t>(s) * p.B + b) * d.H + 4 * ch);
-        m[0] = __fadd_rn(m[0], y.x);
-        m[1] = __fadd_rn(m[1], y.y);
-        m[2] = __fadd_rn(m[2], y.z);
-        m[3] = __fadd_rn(m[3], y.w);
+    for (int q = 0; q < kG; ++q)
+#pragma unroll
+      for (int c = 0; c < kCPB; ++c) {
+        const int ch = threadIdx.x + c * kBlock;
+        y[q][c] = s0 + q < p.Sf && ch < nchunks
+                      ? *reinterpret_cast<const float4*>(p.y + (static_cast<int64_t>(s0 + q) * p.B + b) * d.H + 4 * ch)
+                      : make_float4(0.f, 0.f, 0.f, 0.f);
       }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) v.v[c][i] = bf16_to_f32(f32_to_bf16(__fadd_rn(v.v[c][i], m[i])));
-    }
+    for (int q = 0; q < kG; ++q)
+#pragma unroll
+      for (int c = 0; c < kCPB; ++c)
+        if (s0 + q < p.Sf) {
+          m[c][0] = __fadd_rn(m[c][0], y[q][c].x);
+          m[c][1] = __fadd_rn(m[c][1], y[q][c].y);
+          m[c][2] = __fadd_rn(m[c][2], y[q][c].z);
+          m[c][3] = __fadd_rn(m[c][3], y[q][c].w);
+        }
   }
+#pragma unroll
+  for (int c = 0; c < kCPB; ++c)
+    if (static_cast<int>(threadIdx.x) + c * kBlock < nchunks) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v.v[c][i] = bf16_to_f32(f32_to_bf16(__fadd_rn(v.v[c][i], m[c][i])));
+    }
   if (p.states) store_row(v, nchunks, p.states + (static_cast<int64_t>(p.step) * p.B + b) * d.H);
   float ss = row_sumsq(v, nchunks), unused = 0.0f;
   block_sum2(ss, unused, red);
-  store_norm(v, nchunks, ss, d, p.gamma_o, p.xf + static_cast<int64_t>(b) * d.H);
-  if (!p.last) store_norm(v, nchunks, ss, d, p.gamma_h, p.x + static_cast<int64_t>(b) * d.H);
+  store_norm(v, nchunks, ss, d, go, p.xf + static_cast<int64_t>(b) * d.H);
+  if (!p.last) store_norm(v, nchunks, ss, d, gh, p.x + static_cast<int64_t>(b) * d.H);
 }
 
 // The draft token from the arg-max keys (which are cleared for the next use)
@@ -190,6 +225,7 @@ __global__ __launch_bounds__(kBlock) void k_draft_pick(Dims d, DraftParams p) {
   __shared__ float red[2][kBlock / kWave];
   __shared__ int tok_s;
   const int b = blockIdx.x, nchunks = d.H / 4;
+  const Gain ge = load_gain(p.gamma_e, nchunks);
   if (threadIdx.x < kWave) {
     unsigned long long key = 0ull;
     if (threadIdx.x < kKeySlots) {
@@ -211,7 +247,7 @@ __global__ __launch_bounds__(kBlock) void k_draft_pick(Dims d, DraftParams p) {
   load_bf16_row(embed_row(p, d, tok_s), nchunks, e);
   float ss = row_sumsq(e, nchunks), unused = 0.0f;
   block_sum2(ss, unused, red);
-  store_norm(e, nchunks, ss, d, p.gamma_e, p.x + static_cast<int64_t>(p.B + b) * d.H);
+  store_norm(e, nchunks, ss, d, ge, p.x + static_cast<int64_t>(p.B + b) * d.H);
 }
 
 }  // namespace
