@@ -35,6 +35,7 @@ namespace {
 constexpr int kMaxK1 = 8;
 constexpr int kPosTile = 64;
 constexpr int kPartStride = 2 + kHeadDim;
+constexpr int kMaxGroups = 64;  // position groups per (sequence, head), at most
 constexpr float kLog2e = 1.44269504088896341f;
 constexpr float kNegBig = -1.0e30f;
 
@@ -211,24 +212,34 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
 // One 128-thread workgroup per (query row, head), a thread per dimension:
 // merge the partials of the groups that hold positions, divide, round.
 __global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnParams p) {
-  __shared__ float sm[64], sf[64];
+  __shared__ float sm[kMaxGroups], sl[kMaxGroups], sf[kMaxGroups];
   const int t = blockIdx.x, h = blockIdx.y, b = t / p.K1, j = t % p.K1;
   const int dd = threadIdx.x;
   const int len = clamped_pos(p, b, p.K1) + p.K1;
   const int ng = used_groups(len, p.G);
   const float* part = p.part + ((static_cast<int64_t>(b) * p.nh + h) * p.G) * p.K1 * kPartStride + j * kPartStride;
   const int64_t gs = static_cast<int64_t>(p.K1) * kPartStride;
-  if (dd < ng) sm[dd] = part[dd * gs];
+  // every load first (one memory round trip): group dd's max and sum, and
+  // this dimension's weighted sum of every group
+  float av[kMaxGroups];
+#pragma unroll
+  for (int g = 0; g < kMaxGroups; ++g) av[g] = g < ng ? part[g * gs + 2 + dd] : 0.0f;
+  if (dd < ng) {
+    sm[dd] = part[dd * gs];
+    sl[dd] = part[dd * gs + 1];
+  }
   __syncthreads();
   float M = kNegBig;
   for (int g = 0; g < ng; ++g) M = fmaxf(M, sm[g]);
   if (dd < ng) sf[dd] = exp_f(sm[dd] - M);
   __syncthreads();
   float L = 0.0f, A = 0.0f;
-#pragma unroll 8
-  for (int g = 0; g < ng; ++g) {
-    L = fmaf(sf[g], part[g * gs + 1], L);
-    A = fmaf(sf[g], part[g * gs + 2 + dd], A);
+#pragma unroll
+  for (int g = 0; g < kMaxGroups; ++g) {
+    if (g < ng) {
+      L = fmaf(sf[g], sl[g], L);
+      A = fmaf(sf[g], av[g], A);
+    }
   }
   p.ctx[static_cast<int64_t>(t) * (p.nh * kHeadDim) + h * kHeadDim + dd] = f32_to_bf16(A / L);
 }
@@ -237,7 +248,7 @@ __global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnParams p) {
 
 int attn_groups(const Dims& d, int B, int nh) {
   const int target = 2 * d.n_cu;
-  return std::min(64, std::max(1, (target + B * nh - 1) / (B * nh)));
+  return std::min(kMaxGroups, std::max(1, (target + B * nh - 1) / (B * nh)));
 }
 
 size_t attn_part_floats(int T, int nh, int G) { return static_cast<size_t>(T) * nh * G * kPartStride; }
