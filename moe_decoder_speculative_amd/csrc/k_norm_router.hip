@@ -34,6 +34,7 @@ namespace {
 constexpr int kThreads = 1024;   // 16 wavefronts
 constexpr int kWaves = kThreads / kWave;
 constexpr int kRows = 16;        // token rows a workgroup can hold (MFMA tile columns)
+constexpr int kRouterHelpers = 64;  // workgroups that only bring the router matrix into L2
 constexpr int kGroup = 2;        // expert rows loaded together in the combine
 
 template <typename ST>
@@ -150,6 +151,29 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   constexpr int CPL = (KQ + 1) / 2;  // 4-element chunks per lane: ceil(H / 256)
 
   const int et = wave % 4, kq = wave / 4;
+
+  // Helper workgroups (after the rows' workgroups): one CU takes ~5 us to pull
+  // the 160 KiB router matrix (its misses in flight are few), so 64 helpers
+  // each load one eighth of it and exit.  Workgroups go to the eight XCDs in
+  // turn, so every XCD gets eight helpers covering the whole matrix, and the
+  // row workgroups' requests find it in their XCD's L2.
+  if (static_cast<int>(blockIdx.x) >= (T + rows - 1) / rows) {
+    if constexpr (sizeof(ST) == 2) {
+      const int h = static_cast<int>(blockIdx.x) - (T + rows - 1) / rows;
+      const int frags = 4 * (H / kKStep), per = (frags + 7) / 8;  // 1 KiB fragments: [64 / 16][H / 32]
+      const int f0 = ((h / 8) % 8) * per;
+      const bf16_t* wr = reinterpret_cast<const bf16_t*>(p.router);
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const int f = f0 + wave + q * kWaves;
+        if (wave + q * kWaves < per && f < frags) {
+          const bf16x8_t v = load_frag(wr + static_cast<int64_t>(f) * kFragElems + lane * 8);
+          asm volatile("" ::"v"(v));
+        }
+      }
+    }
+    return;
+  }
 
   // router fragments of this wavefront, requested after phase 1 (to keep
   // phase 1 within 128 registers)
@@ -398,7 +422,8 @@ hipError_t launch_kq(const Dims& d, const NormRouterParams& p, hipStream_t s) {
   // or the step is prefill-sized; 4 otherwise, so that a verify step of a few
   // hundred rows spreads its combine reads over more CUs
   const int rows = (p.T <= kRows || p.T > 256) ? kRows : 4;
-  const dim3 grid((p.T + rows - 1) / rows);
+  // the rows' workgroups, then the router-matrix helpers (bf16 routing only)
+  const dim3 grid((p.T + rows - 1) / rows + (p.route && sizeof(ST) == 2 ? kRouterHelpers : 0));
   const size_t xs = p.route ? (sizeof(ST) == 2 ? static_cast<size_t>(d.H) * 32 : static_cast<size_t>(d.H) * kRows * 4) : 0;
   const size_t smem = 4 * kRows * 64 * sizeof(float) + xs;
   if (!p.combine && p.route && sizeof(ST) == 2)
