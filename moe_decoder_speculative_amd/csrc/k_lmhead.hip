@@ -494,9 +494,11 @@ __global__ __launch_bounds__(kBlock, 2) void k_lmhead_stream(Dims d, LmHeadParam
 // w owns the unit's row tiles Rw..Rw+R-1 over the whole reduction, so its
 // accumulators (R row tiles x NT token tiles) never leave registers.  Per
 // 32-wide k-step g:
-//  * weight fragments go straight to registers from a ring of P steps in
-//    flight per wavefront (PR KiB: 16 KiB with P = 4, R = 4 and P = 8,
-//    R = 2), which keeps HBM busy through the barriers;
+//  * weight fragments go straight to registers from a ring of P = 4 steps in
+//    flight per wavefront (PR KiB: 16 KiB with R = 4, 8 KiB with R = 2),
+//    which keeps HBM busy through the barriers (at 8 token tiles a ring of
+//    8 steps, 128 KiB in flight per CU, only lengthened the queues: the
+//    head took 72.6 us at 128 tokens against 70.3 us with 4);
 //  * the activation fragments of all NT token tiles (NT KiB, shared by the 8
 //    wavefronts) come from a double-buffered LDS stage; wavefront w loads
 //    token tile w % NT of step g into a ring of P registers P steps ahead and
@@ -770,7 +772,7 @@ hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s) {
   const int nt = (p.T + kTile - 1) / kTile;
   if (nt <= 2) return lm_wide_nt<2, 4, 4>(d, p, s);
   if (nt <= 4) return lm_wide_nt<4, 4, 4>(d, p, s);
-  if (nt <= 8) return lm_wide_nt<8, 2, 8>(d, p, s);
+  if (nt <= 8) return lm_wide_nt<8, 2, 4>(d, p, s);
   return lm_nt<8, 4, 2>(d, p, s);
 }
 
