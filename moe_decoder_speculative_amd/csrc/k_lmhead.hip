@@ -489,14 +489,15 @@ __global__ __launch_bounds__(kBlock, 2) void k_lmhead_stream(Dims d, LmHeadParam
 
 // ------------------------------------------------- 17..128 tokens ----
 // One 512-thread workgroup per CU, persistent over units of 8R row tiles
-// (R = 4 up to 4 token tiles, 2 for 8, which keeps the accumulators plus the
-// load rings within the 256 registers of two wavefronts per SIMD); wavefront
+// (R = 2: with R = 4 the accumulators and rings of 8 token tiles spill, and
+// at 2 token tiles R = 4 -- 16 KiB in flight per wavefront -- was slower: a
+// draft call's head 64.5 -> 68.8 % of the HBM peak with R = 2); wavefront
 // w owns the unit's row tiles Rw..Rw+R-1 over the whole reduction, so its
 // accumulators (R row tiles x NT token tiles) never leave registers.  Per
 // 32-wide k-step g:
 //  * weight fragments go straight to registers from a ring of P = 4 steps in
-//    flight per wavefront (PR KiB: 16 KiB with R = 4, 8 KiB with R = 2),
-//    which keeps HBM busy through the barriers (at 8 token tiles a ring of
+//    flight per wavefront (PR = 8 KiB, 64 KiB per CU), which keeps HBM busy
+//    through the barriers (at 8 token tiles a ring of
 //    8 steps, 128 KiB in flight per CU, only lengthened the queues: the
 //    head took 72.6 us at 128 tokens against 70.3 us with 4);
 //  * the activation fragments of all NT token tiles (NT KiB, shared by the 8
@@ -770,8 +771,8 @@ hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s) {
     }
   }
   const int nt = (p.T + kTile - 1) / kTile;
-  if (nt <= 2) return lm_wide_nt<2, 4, 4>(d, p, s);
-  if (nt <= 4) return lm_wide_nt<4, 4, 4>(d, p, s);
+  if (nt <= 2) return lm_wide_nt<2, 2, 4>(d, p, s);
+  if (nt <= 4) return lm_wide_nt<4, 2, 4>(d, p, s);
   if (nt <= 8) return lm_wide_nt<8, 2, 4>(d, p, s);
   return lm_nt<8, 4, 2>(d, p, s);
 }
