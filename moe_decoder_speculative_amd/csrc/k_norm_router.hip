@@ -192,14 +192,12 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
     }
   };
 
-  if constexpr (EARLY) load_router();
-
   // ------------------------------------------------------------ phase 1
+  float x[CPL][4];
+  Vec4<ST> gg[CPL];  // the gain, loaded with the row, converted when used
+  const ST* xin = reinterpret_cast<const ST*>(p.x_in) + static_cast<int64_t>(t) * H;
+  const ST* gam = reinterpret_cast<const ST*>(p.gamma);
   if (has_row) {
-    float x[CPL][4];
-    Vec4<ST> gg[CPL];  // the gain, loaded with the row, converted when used
-    const ST* xin = reinterpret_cast<const ST*>(p.x_in) + static_cast<int64_t>(t) * H;
-    const ST* gam = reinterpret_cast<const ST*>(p.gamma);
 #pragma unroll
     for (int c = 0; c < CPL; ++c) {
       const int ch = lane + c * kWave;
@@ -208,6 +206,12 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
         if (p.norm) gg[c] = *reinterpret_cast<const Vec4<ST>*>(gam + 4 * ch);
       }
     }
+  }
+  // EARLY: the router fragments are requested right after the row loads (a
+  // wavefront's loads complete in order, so requested first they would hold
+  // up the rows by the whole matrix pull)
+  if constexpr (EARLY) load_router();
+  if (has_row) {
     if (!EARLY && p.combine) {
       // rows to add, in order: shared experts, then routed by ascending expert
       const int nrows = d.S + k;
