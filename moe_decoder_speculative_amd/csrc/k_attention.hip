@@ -247,8 +247,11 @@ __global__ __launch_bounds__(kHeadDim) void k_attn_combine(AttnParams p) {
 }  // namespace
 
 int attn_groups(const Dims& d, int B, int nh) {
-  const int target = 2 * d.n_cu;
-  return std::min(kMaxGroups, std::max(1, (target + B * nh - 1) / (B * nh)));
+  // about one workgroup per CU, at least two groups: at B = 1 (10 heads)
+  // twice that many groups (52) was 3 us slower -- more partials to combine
+  // -- and one group at B = 32 12 us slower
+  const int target = d.n_cu;
+  return std::min(kMaxGroups, std::max(2, (target + B * nh - 1) / (B * nh)));
 }
 
 size_t attn_part_floats(int T, int nh, int G) { return static_cast<size_t>(T) * nh * G * kPartStride; }
