@@ -285,6 +285,81 @@ def test_lm_head_argmax_first_occurrence_and_loop():
     assert O.greedy_pick(tie)[0] == 1
 
 
+def _torch_head_logits(x, gamma, W, eps, bf16):
+    """Final norm and logits with torch's CPU routines: F.rms_norm in float32,
+    the bf16 rounding of its output when the storage is bf16, then F.linear in
+    float64 on those values."""
+    import torch.nn.functional as F
+    xt = torch.from_numpy(np.ascontiguousarray(x, np.float32))
+    xf = F.rms_norm(xt, (xt.shape[1],), weight=torch.from_numpy(np.asarray(gamma, np.float32)), eps=eps)
+    if bf16:
+        xf = xf.to(torch.bfloat16).to(torch.float32)
+    return F.linear(xf.double(), torch.from_numpy(np.asarray(W, np.float64))).numpy()
+
+
+def _head_mismatch(got, ref):
+    """(fraction of logits off by more than 1e-5 of the logit scale, largest
+    difference over that scale).  Summation order alone stays far below the
+    first; a bf16 rounding that resolves the other way on one side moves a
+    few logits by about |W| * 2^-8 * |xf|, which stays below the second."""
+    scale = np.abs(ref).max()
+    d = np.abs(np.asarray(got, np.float64) - ref) / scale
+    return float(np.mean(d > 1e-5)), float(d.max())
+
+
+def _head_case(H, V, T, dtype, seed):
+    g = np.random.default_rng(seed)
+    # rows of very different scale (the norm matters) and a non-unit gain
+    x = (g.standard_normal((T, H)) * g.uniform(0.2, 5.0, (T, 1))).astype(np.float32)
+    gamma = g.uniform(0.5, 1.5, H).astype(np.float32)
+    W = (g.standard_normal((V, H)) * 0.02).astype(np.float32)
+    if dtype == "bf16":
+        x, gamma, W = _torch_bf16(x), _torch_bf16(gamma), _torch_bf16(W)
+    return x, gamma, W
+
+
+@pytest.mark.parametrize("H,V,T,dtype", [(256, 1024, 8, "f32"), (256, 1024, 8, "bf16"), (384, 777, 33, "bf16"),
+                                         (128, 300, 5, "f32")])
+def test_lm_head_logits_match_torch_rms_norm_and_linear(H, V, T, dtype):
+    """lm_head_logits (final RMSNorm with its gain, the R1 rounding for bf16,
+    then the vocabulary product) against torch's rms_norm and linear, at the
+    tiny workload's head shape and small bf16 shapes with ragged sizes."""
+    x, gamma, W = _head_case(H, V, T, dtype, seed=H + V + T)
+    eps = 1e-6
+    got = O.lm_head_logits(x, gamma, W, eps, O.storage_round(dtype))
+    ref = _torch_head_logits(x, gamma, W, eps, dtype == "bf16")
+    frac, worst = _head_mismatch(got, ref)
+    assert frac <= 0.01 and worst <= 2e-3, (frac, worst)
+    if dtype == "f32":
+        assert worst <= 1e-5
+    decided = O.argmax_margin(ref.astype(np.float32)) >= 1e-3 * np.abs(ref).max()
+    assert np.array_equal(O.greedy_pick(got)[decided], np.argmax(ref, 1)[decided])
+
+
+def test_lm_head_logits_pin_rejects_planted_mistakes():
+    """The head pin fails for a dropped final norm, a skipped R1 rounding and
+    an ignored gain, each planted in a copy of lm_head_logits."""
+    H, V, T, eps = 256, 1024, 16, 1e-6
+    x, gamma, W = _head_case(H, V, T, "bf16", seed=99)
+    ref = _torch_head_logits(x, gamma, W, eps, True)
+    bf = O.storage_round("bf16")
+
+    def no_norm(x, gamma_f, w_lm, eps, store):
+        return (store(O.as_f32(x) * gamma_f) @ O.as_f32(w_lm).T).astype(np.float32)
+
+    def no_r1(x, gamma_f, w_lm, eps, store):
+        return O.lm_head_logits(x, gamma_f, w_lm, eps, O.storage_round("f32"))
+
+    def no_gain(x, gamma_f, w_lm, eps, store):
+        return O.lm_head_logits(x, np.ones_like(gamma_f), w_lm, eps, store)
+
+    frac, worst = _head_mismatch(O.lm_head_logits(x, gamma, W, eps, bf), ref)
+    assert frac <= 0.01 and worst <= 2e-3
+    for bad in (no_norm, no_r1, no_gain):
+        frac, worst = _head_mismatch(bad(x, gamma, W, eps, bf), ref)
+        assert frac > 0.01 or worst > 2e-3, bad.__name__
+
+
 # ---------------------------------------------------------- acceptance ----
 
 @pytest.mark.parametrize("K", [0, 1, 2, 3, 4])
