@@ -24,7 +24,8 @@
  * The pages give no internals of the block; the projection of the normalised
  * state and token embedding, the dense SwiGLU FFN with residual, the output
  * norm and the shared LM head are this library's reading, and the block has
- * no attention (neither has the verify step in this library).
+ * no attention (the verify step has an attention variant, moe_verify_step_kv
+ * in moe_verify.h; the draft block does not).
  *
  * Numerics.  bfloat16 storage, float32 arithmetic; values are rounded to
  * bfloat16 (nearest, ties to even) at: every normalised activation (a, e,

@@ -169,6 +169,11 @@ typedef struct moe_verify_aux {
 } moe_verify_aux;
 
 /*
+ * The decoder whose blocks these are has 64 routed experts, two shared
+ * experts, top-6 routing and 12 layers (page "Jina AI releases lightweight OCR
+ * model with built-in speculative decoding", section "Lean architecture with a
+ * compressed encoder"); the config carries those counts, and the widths the
+ * pages leave open.
  * Validate `cfg`, allocate the context and repack the weights into it on
  * `hip_stream`, then synchronise that stream (so the caller may free its
  * weight tensors as soon as this returns).  On success *out receives the
@@ -235,7 +240,11 @@ int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* d
                        const moe_verify_aux* aux, void* hip_stream);
 
 /*
- * One MoE-FFN block of layer `layer` over T token rows (the prefill path):
+ * One MoE-FFN block of layer `layer` over T token rows (the prefill path: a
+ * page enters the decoder as at most 1,156 visual tokens, 256 global plus up
+ * to nine local tiles of 100, page "Jina AI releases lightweight OCR model
+ * with built-in speculative decoding", section "Lean architecture with a
+ * compressed encoder"; several pages and their prompts make thousands of rows):
  *   x  device, storage [T][H] in;  y  device, storage [T][H] out = x + MoE(RMSNorm(x)).
  * x and y may not overlap.  aux (may be NULL) receives layer-0-indexed
  * topk_idx/topk_w/expert_count/expert_offset/perm/moe_out for this block;
