@@ -23,6 +23,12 @@ from moe_decoder_speculative_amd.model import VerifyModel, to_device
 
 REL_TOL = {"bf16": 2e-2, "f32": 1e-4}
 W_TOL = 1e-3
+# The residual stream after the 12-block stack, compared end to end: two
+# float32 evaluations of the oracle itself (its own, and every sum
+# accumulated in float64) already differ by up to 2.1e-2 of a row's scale
+# there on the margin-selected rows (tests/test_margin_rows.py holds that
+# spread under 3e-2), so the end-to-end bar is twice the single-block one.
+STACK12_HIDDEN_TOL = 4e-2
 
 
 def rowwise_rel_err(got: np.ndarray, ref: np.ndarray) -> np.ndarray:
@@ -57,8 +63,11 @@ def run_step(model: VerifyModel, case, B: int, K: int, with_aux=True):
     return out
 
 
-def check_block(out: dict, l: int, blk, k: int, E: int, dtype: str, T: int, tag=""):
-    """Layer l of the step against the oracle's BlockResult."""
+def check_block(out: dict, l: int, blk, k: int, E: int, dtype: str, T: int, tag="", gates_rel: bool = False):
+    """Layer l of the step against the oracle's BlockResult.  Gate weights
+    within W_TOL absolute, or (gates_rel, for a multi-block step compared end
+    to end, where they inherit the drift of the two trajectories) within the
+    storage type's per-row relative bar like every other float output."""
     idx = out["topk_idx"][l]
     assert idx.shape == blk.idx.shape
     # the selected expert set is unique (margin >= 1e-3); order inside it may differ
@@ -69,7 +78,11 @@ def check_block(out: dict, l: int, blk, k: int, E: int, dtype: str, T: int, tag=
     r_sel = np.argsort(blk.idx, 1, kind="stable")
     gw = np.take_along_axis(w, o_sel, 1)
     rw = np.take_along_axis(blk.w, r_sel, 1)
-    assert np.abs(gw - rw).max() <= W_TOL, f"{tag} layer {l}: gate weights off by {np.abs(gw - rw).max()}"
+    if gates_rel:
+        gerr = rowwise_rel_err(gw, rw).max()
+        assert gerr <= REL_TOL[dtype], f"{tag} layer {l}: gate weights rel err {gerr:.3e}"
+    else:
+        assert np.abs(gw - rw).max() <= W_TOL, f"{tag} layer {l}: gate weights off by {np.abs(gw - rw).max()}"
     np.testing.assert_allclose(w.sum(1), 1.0, atol=1e-5)
     # counting sort: counts and offsets exact; within each expert the tokens in
     # ascending order (pair ids depend on the order inside a selection, so the
@@ -132,15 +145,18 @@ def check_rows_teacher_forced(per_layer: list, x0, weights: dict, shp, margin: f
             f"rows {undecided}, rows with another expert set {differing}")
 
 
-def check_step(out: dict, case, B: int, K: int, tag=""):
+def check_step(out: dict, case, B: int, K: int, tag="", gates_rel: bool = False, hidden_tol: float | None = None):
+    """The whole step against the oracle's.  hidden_tol overrides the bar of
+    the final residual stream (a deep stack compared end to end)."""
     ref = case.ref
     w = case.w
     T = B * (K + 1)
     errs = []
     for l, blk in enumerate(ref.blocks):
-        errs.append(check_block(out, l, blk, w.k, w.E, w.dtype, T, tag))
+        errs.append(check_block(out, l, blk, w.k, w.E, w.dtype, T, tag, gates_rel))
     herr = rowwise_rel_err(out["hidden_out"], ref.hidden_out).max()
-    assert herr <= REL_TOL[w.dtype], f"{tag}: hidden_out rel err {herr:.3e}"
+    htol = REL_TOL[w.dtype] if hidden_tol is None else hidden_tol
+    assert herr <= htol, f"{tag}: hidden_out rel err {herr:.3e}"
     assert np.array_equal(out["tstar"], ref.tstar), f"{tag}: greedy picks differ"
     assert np.array_equal(out["counts"], ref.counts), f"{tag}: counts differ"
     assert np.array_equal(out["committed"], ref.committed), f"{tag}: committed tokens differ"
@@ -158,9 +174,17 @@ def check_stack_teacher_forced(out: dict, case, margin: float = 1e-3, slack: flo
     undecided = 0
     exact_traj_rows = 0
     worst_m = 0.0
+    # drift: the oracle's logits along the GPU's trajectory against its own,
+    # on the rows whose expert sets have agreed with the oracle's own so far
+    agree = np.ones(x.shape[0], bool)
+    drift = []
     for l in range(shp.L):
         ref = O.moe_block(x, case.weights["layers"][l], shp)
         idx = out["topk_idx"][l]
+        own = case.ref.blocks[l]
+        dz = np.abs(ref.z - own.z).max(1)
+        drift.append(float(dz[agree].max()) if agree.any() else float("nan"))
+        agree &= np.all(np.sort(idx, 1) == np.sort(own.idx, 1), axis=1)
         mg = O.topk_margin(ref.z, shp.k)
         same = np.all(np.sort(idx, 1) == np.sort(ref.idx, 1), axis=1)
         decided = mg >= margin
@@ -188,9 +212,17 @@ def check_stack_teacher_forced(out: dict, case, margin: float = 1e-3, slack: flo
     assert np.array_equal(out["counts"], counts) and np.array_equal(out["committed"], committed)
     exact_traj_rows = int(np.sum(np.all(out["hidden_out"] == case.ref.hidden_out, axis=1)))
     same_tokens = int(np.sum(ts == case.ref.tstar))
+    lg_own = O.lm_head_logits(case.ref.hidden_out, case.weights["final_gamma"], case.weights["lm_head"],
+                              shp.eps, store)
+    dl = np.abs(lg - lg_own).max(1)
+    head_drift = float(dl[agree].max()) if agree.any() else float("nan")
+    drift_txt = " ".join(f"{d:.1e}" for d in drift)
     return (f"moe_out rel err {worst_m:.2e}; undecided top-k rows {undecided}, undecided picks "
             f"{int((~decided).sum())}; rows on the oracle's exact trajectory {exact_traj_rows}/{len(ts)}; "
-            f"picks equal to the oracle's own step {same_tokens}/{len(ts)}; committed {int(counts.sum())}")
+            f"picks equal to the oracle's own step {same_tokens}/{len(ts)}; committed {int(counts.sum())}; "
+            f"rows whose expert sets follow the oracle's own at every layer {int(agree.sum())}/{len(ts)}; "
+            f"drift of the router logits along the GPU's trajectory per layer (max over those rows) "
+            f"[{drift_txt}], of the head logits {head_drift:.1e}")
 
 
 def check_draft_teacher_forced(drafts, states, hidden, committed, counts, R: int, dw: dict, dshp,

@@ -8,6 +8,8 @@ the oracle's greedy picks.  Expected values therefore come from the oracle only.
 from __future__ import annotations
 
 import functools
+import json
+import os
 from dataclasses import dataclass
 
 import numpy as np
@@ -96,3 +98,38 @@ def small_bf16(name="small_bf16", B=5, K=3, H=256, E=16, k=4, S=2, I=128, V=1000
     return synth.Workload(name=name, H=H, E=E, k=k, S=S, I=I, V=V, L=L, B=B, K=K,
                           T=B * (K + 1), dtype="bf16", routing=routing,
                           drafts="independent", has_lm_head=True, seed_id=seed_id)
+
+
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+
+def margin_rows_case(name: str) -> Case:
+    """A stacked workload on rows whose top-k and arg-max gaps leave room for
+    the drift of a second float32 evaluation at every block: the stream
+    positions written by tests/golden/make_margin_rows.py (which uses only
+    the oracle and the seeded generator) select rows of the workload's own
+    hidden-noise stream; the expected outputs are the oracle's step on them."""
+    with open(os.path.join(GOLDEN, f"{name}_rows.json")) as f:
+        spec = json.load(f)
+    w = synth.WORKLOADS[name]
+    shp = shape_of(w)
+    weights = synth.gen_weights(w)
+    noise = synth.HiddenNoise(w)
+    offset = synth.hidden_offset(w, weights, noise)
+    rows = np.asarray(spec["rows"], dtype=np.int64)
+    assert rows.size == w.T
+    n = 0
+    chunks = []
+    while n <= rows.max():
+        chunks.append(noise.draw(spec["chunk"]))
+        n += spec["chunk"]
+    raw = np.concatenate(chunks)[rows]
+    hidden = synth.to_storage(raw + offset, w.dtype)
+    B, K = w.B, w.K
+    ref = oracle.verify_step(shp, weights, hidden, np.zeros((B, K), np.int32), B, K)
+    # the rows meet the stored schedule along the oracle's own trajectory
+    for l, blk in enumerate(ref.blocks):
+        assert oracle.topk_margin(blk.z, w.k).min() >= spec["router_margin"][l], f"block {l}: margin below schedule"
+    drafts = synth.make_drafts(w, ref.tstar.reshape(B, K + 1))
+    ref.committed, ref.counts = oracle.accept_prefix(ref.tstar.reshape(B, K + 1), drafts)
+    return Case(w, shp, weights, hidden, drafts, ref, 0)
