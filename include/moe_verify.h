@@ -305,6 +305,28 @@ void moe_verify_graph_destroy(moe_verify_graph* graph);
  */
 int moe_verify_set_stage_events(moe_verify_ctx* ctx, int32_t stage, void* before, void* after);
 
+/*
+ * For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the verify
+ * step of moe_verify_step with its workspace -- residual and normalised rows,
+ * selections, permutation, SwiGLU activations, expert outputs, arg-max keys
+ * -- in a file-scope device array of MOE_STATIC_SCRATCH_BYTES that the
+ * library holds on every GPU it runs on until the process ends, instead of
+ * the context's own workspace.  The call allocates nothing; the caller
+ * passes inputs and outputs exactly as for moe_verify_step, with the same
+ * results.  Limits: B*(K+1) <= MOE_STATIC_MAX_TOKENS (and <= max_tokens),
+ * a context without attention, the context's device current.  Every call on
+ * one GPU uses that GPU's one array: calls that overlap on one GPU (on
+ * different streams, or from several threads or contexts) race, and must be
+ * serialised by the caller.  Errors: those of moe_verify_step; MOE_EINVAL
+ * for a step larger than the limits or a workspace that would not fit.
+ */
+#define MOE_STATIC_SCRATCH_BYTES (16u << 20)
+#define MOE_STATIC_MAX_TOKENS 128
+int moe_verify_step_static(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts,
+                           int32_t B, int32_t K, int32_t* committed, int32_t* counts,
+                           void* hip_stream);
+
 /* Free everything the context owns.  NULL is accepted.  Synchronises the
  * device work the context may still have in flight. */
 void moe_verify_destroy(moe_verify_ctx* ctx);

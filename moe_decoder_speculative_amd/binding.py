@@ -17,6 +17,7 @@ LIB_PATH = os.path.join(_HERE, "lib", "libmoeverify.so")
 MOE_OK, MOE_EINVAL, MOE_EUNSUPPORTED, MOE_ENOMEM, MOE_EHIP = 0, -1, -2, -3, -4
 MOE_DTYPE_F32, MOE_DTYPE_BF16 = 0, 1
 EXPORTED = ("moe_verify_init", "moe_verify_step", "moe_verify_step_ex", "moe_verify_step_kv",
+            "moe_verify_step_static",
             "moe_verify_kv_cache", "moe_block_forward",
             "moe_verify_graph_create", "moe_verify_graph_create_kv", "moe_verify_graph_launch",
             "moe_verify_graph_destroy",
@@ -82,6 +83,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.moe_verify_init.restype = ctypes.c_int
     lib.moe_verify_step.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
     lib.moe_verify_step.restype = ctypes.c_int
+    lib.moe_verify_step_static.argtypes = [vp, vp, vp, i32, i32, vp, vp, vp]
+    lib.moe_verify_step_static.restype = ctypes.c_int
     lib.moe_verify_step_ex.argtypes = [vp, vp, vp, i32, i32, vp, vp, ctypes.POINTER(MoeVerifyAux), vp]
     lib.moe_verify_step_ex.restype = ctypes.c_int
     lib.moe_verify_step_kv.argtypes = [vp, vp, vp, vp, i32, i32, vp, vp, ctypes.POINTER(MoeVerifyAux), vp]
@@ -159,6 +162,12 @@ def moe_verify_init(cfg: MoeVerifyConfig, weights: MoeVerifyWeights, stream=None
 def moe_verify_step(ctx: int, hidden, drafts, B: int, K: int, committed, counts, stream=None) -> None:
     _check(load_library().moe_verify_step(ctx, _ptr(hidden), _ptr(drafts), B, K, _ptr(committed),
                                           _ptr(counts), _stream(stream)))
+
+
+def moe_verify_step_static(ctx: int, hidden, drafts, B: int, K: int, committed, counts, stream=None) -> None:
+    """moe_verify_step with the workspace in the library's static device scratch (allocates nothing)."""
+    _check(load_library().moe_verify_step_static(ctx, _ptr(hidden), _ptr(drafts), B, K, _ptr(committed),
+                                                 _ptr(counts), _stream(stream)))
 
 
 def make_aux(**tensors) -> MoeVerifyAux:

@@ -296,30 +296,30 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   }
 
   const int64_t tw = std::max<int64_t>(g.max_tokens, g.max_prefill_tokens);
-  c->tw = tw;
+  c->ws.tw = tw;
   const int64_t rows = tw * (g.top_k + S);
-  if ((r = ctx_alloc(c, tw * H * es, &c->xres))) return r;
+  if ((r = ctx_alloc(c, tw * H * es, &c->ws.xres))) return r;
   // one extra all-zero row past the end of xhat and act: padding lanes of the
   // grouped GEMM read it instead of branching
-  if ((r = ctx_alloc(c, (tw + 1) * H * es, &c->xhat))) return r;
-  MOE_HIP(hipMemsetAsync(c->xhat + tw * H * es, 0, H * es, s));
+  if ((r = ctx_alloc(c, (tw + 1) * H * es, &c->ws.xhat))) return r;
+  MOE_HIP(hipMemsetAsync(c->ws.xhat + tw * H * es, 0, H * es, s));
   for (int i = 0; i < 2; ++i) {
-    if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->idx[i]))) return r;
-    if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(float), &c->w[i]))) return r;
+    if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->ws.idx[i]))) return r;
+    if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(float), &c->ws.w[i]))) return r;
   }
-  if ((r = ctx_alloc_t(c, E * sizeof(int), &c->cnt))) return r;
-  if ((r = ctx_alloc_t(c, (E + 1) * sizeof(int), &c->off))) return r;
-  if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->perm))) return r;
-  if ((r = ctx_alloc_t(c, E * sizeof(int), &c->active))) return r;
-  if ((r = ctx_alloc_t(c, 16, &c->n_active))) return r;
-  if ((r = ctx_alloc_t(c, E * sizeof(int4), &c->desc))) return r;
-  if ((r = ctx_alloc(c, (rows + 1) * I * es, &c->act))) return r;
-  MOE_HIP(hipMemsetAsync(c->act + rows * I * es, 0, I * es, s));
-  if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->y))) return r;
-  if ((r = ctx_alloc_t(c, moe::kKeySlots * tw * sizeof(unsigned long long), &c->keys))) return r;
-  if ((r = ctx_alloc_t(c, static_cast<size_t>(moe::gemm_max_tiles(d, static_cast<int>(tw))) * sizeof(int4), &c->tiles)))
+  if ((r = ctx_alloc_t(c, E * sizeof(int), &c->ws.cnt))) return r;
+  if ((r = ctx_alloc_t(c, (E + 1) * sizeof(int), &c->ws.off))) return r;
+  if ((r = ctx_alloc_t(c, tw * g.top_k * sizeof(int), &c->ws.perm))) return r;
+  if ((r = ctx_alloc_t(c, E * sizeof(int), &c->ws.active))) return r;
+  if ((r = ctx_alloc_t(c, 16, &c->ws.n_active))) return r;
+  if ((r = ctx_alloc_t(c, E * sizeof(int4), &c->ws.desc))) return r;
+  if ((r = ctx_alloc(c, (rows + 1) * I * es, &c->ws.act))) return r;
+  MOE_HIP(hipMemsetAsync(c->ws.act + rows * I * es, 0, I * es, s));
+  if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->ws.y))) return r;
+  if ((r = ctx_alloc_t(c, moe::kKeySlots * tw * sizeof(unsigned long long), &c->ws.keys))) return r;
+  if ((r = ctx_alloc_t(c, static_cast<size_t>(moe::gemm_max_tiles(d, static_cast<int>(tw))) * sizeof(int4), &c->ws.tiles)))
     return r;
-  if ((r = ctx_alloc_t(c, 16, &c->n_tiles))) return r;
+  if ((r = ctx_alloc_t(c, 16, &c->ws.n_tiles))) return r;
 
   if (g.n_heads > 0) {
     d.L = g.n_layers;
@@ -349,7 +349,7 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   }
 
   // arg-max keys are zero between steps (the acceptance clears them after use)
-  MOE_HIP(hipMemsetAsync(c->keys, 0, moe::kKeySlots * tw * sizeof(unsigned long long), s));
+  MOE_HIP(hipMemsetAsync(c->ws.keys, 0, moe::kKeySlots * tw * sizeof(unsigned long long), s));
 
   if ((r = repack(c, w, s))) return r;
   MOE_HIP(hipStreamSynchronize(s));
@@ -363,7 +363,7 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
 // layer's MoE block when li > 0), q/k/v projection with the rotary embedding
 // and the cache writes, decode attention, output projection with the
 // residual add into xattn.
-int run_attention(moe_verify_ctx* c, const void* x_prev, int li, int l, int T, int B, int K1, const int* positions,
+int run_attention(moe_verify_ctx* c, const moe::api::Workspace& W, const void* x_prev, int li, int l, int T, int B, int K1, const int* positions,
                   const moe_verify_aux* aux, hipStream_t s) {
   const moe::Dims& d = c->d;
   const moe_verify_config& g = c->cfg;
@@ -372,20 +372,20 @@ int run_attention(moe_verify_ctx* c, const void* x_prev, int li, int l, int T, i
   moe::NormRouterParams an{};
   an.x_in = x_prev;
   if (li > 0) {  // finish the previous layer's MoE block into xres
-    an.x_out = c->xres;
-    an.y = c->y;
-    an.prev_idx = aux && aux->topk_idx ? aux->topk_idx + (li - 1) * T * k : c->idx[(li - 1) & 1];
-    an.prev_w = aux && aux->topk_w ? aux->topk_w + (li - 1) * T * k : c->w[(li - 1) & 1];
+    an.x_out = W.xres;
+    an.y = W.y;
+    an.prev_idx = aux && aux->topk_idx ? aux->topk_idx + (li - 1) * T * k : W.idx[(li - 1) & 1];
+    an.prev_w = aux && aux->topk_w ? aux->topk_w + (li - 1) * T * k : W.w[(li - 1) & 1];
     an.m_out = aux && aux->moe_out ? aux->moe_out + (li - 1) * T * H : nullptr;
     an.combine = 1;
   }
   an.gamma = c->attn_gamma + l * H * es;
-  an.xhat = c->xhat;
+  an.xhat = W.xhat;
   an.T = T;
   an.norm = 1;
   an.route = 0;
   MOE_HIP(moe::launch_norm_router(d, an, s));
-  const void* x_res = li > 0 ? c->xres : x_prev;
+  const void* x_res = li > 0 ? W.xres : x_prev;
 
   const size_t cache_layer = static_cast<size_t>(g.max_seqs) * g.n_heads * g.max_positions * moe::kHeadDim;
   bf16_t* kc = reinterpret_cast<bf16_t*>(c->kcache) + l * cache_layer;
@@ -393,7 +393,7 @@ int run_attention(moe_verify_ctx* c, const void* x_prev, int li, int l, int T, i
   moe::ExpertParams qe{};
   qe.n_active = c->zero;
   qe.w_down = c->wqkv + l * 3 * H * H * es;
-  qe.act = c->xhat;
+  qe.act = W.xhat;
   qe.T = T;
   moe::EpiParams qp{};
   qp.positions = positions;
@@ -436,7 +436,7 @@ int run_attention(moe_verify_ctx* c, const void* x_prev, int li, int l, int T, i
   return MOE_OK;
 }
 
-int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_aux* aux, int layer0, int nlayers,
+int run_blocks(moe_verify_ctx* c, const moe::api::Workspace& W, const void* hidden, int T, const moe_verify_aux* aux, int layer0, int nlayers,
                hipStream_t s, const void** x_last, const int* positions = nullptr, int B = 0, int K1 = 0) {
   const moe::Dims& d = c->d;
   const moe_verify_config& g = c->cfg;
@@ -445,12 +445,12 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
   const void* x_prev = hidden;  // residual stream entering the previous block
   for (int li = 0; li < nlayers; ++li) {
     const int l = layer0 + li;
-    int* idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
-    float* wg = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
+    int* idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : W.idx[li & 1];
+    float* wg = aux && aux->topk_w ? aux->topk_w + li * T * k : W.w[li & 1];
     moe::NormRouterParams nr{};
     if (attn) {
       int r;
-      if ((r = run_attention(c, x_prev, li, l, T, B, K1, positions, aux, s))) return r;
+      if ((r = run_attention(c, W, x_prev, li, l, T, B, K1, positions, aux, s))) return r;
       // the MoE block takes the attention sublayer's output
       x_prev = aux && aux->attn_out ? static_cast<const char*>(aux->attn_out) + li * T * H * c->esize
                                     : static_cast<const char*>(c->xattn);
@@ -459,17 +459,17 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
       nr.x_in = hidden;
     } else {
       nr.x_in = x_prev;
-      nr.x_out = c->xres;
-      nr.y = c->y;
-      nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx + (li - 1) * T * k : c->idx[(li - 1) & 1];
-      nr.prev_w = aux && aux->topk_w ? aux->topk_w + (li - 1) * T * k : c->w[(li - 1) & 1];
+      nr.x_out = W.xres;
+      nr.y = W.y;
+      nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx + (li - 1) * T * k : W.idx[(li - 1) & 1];
+      nr.prev_w = aux && aux->topk_w ? aux->topk_w + (li - 1) * T * k : W.w[(li - 1) & 1];
       nr.m_out = aux && aux->moe_out ? aux->moe_out + (li - 1) * T * H : nullptr;
       nr.combine = 1;
-      x_prev = c->xres;
+      x_prev = W.xres;
     }
     nr.gamma = c->gamma + l * H * c->esize;
     nr.router = c->router + l * c->router_layer;
-    nr.xhat = c->xhat;
+    nr.xhat = W.xhat;
     nr.idx_out = idx;
     nr.w_out = wg;
     nr.T = T;
@@ -478,12 +478,12 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     moe::PermuteParams pp{};
     pp.idx = idx;
     pp.P = T * static_cast<int>(k);
-    pp.cnt = aux && aux->expert_count ? aux->expert_count + li * E : c->cnt;
-    pp.off = aux && aux->expert_offset ? aux->expert_offset + li * (E + 1) : c->off;
-    pp.perm = aux && aux->perm ? aux->perm + li * T * k : c->perm;
-    pp.active = c->active;
-    pp.n_active = c->n_active;
-    pp.desc = c->desc;
+    pp.cnt = aux && aux->expert_count ? aux->expert_count + li * E : W.cnt;
+    pp.off = aux && aux->expert_offset ? aux->expert_offset + li * (E + 1) : W.off;
+    pp.perm = aux && aux->perm ? aux->perm + li * T * k : W.perm;
+    pp.active = W.active;
+    pp.n_active = W.n_active;
+    pp.desc = W.desc;
     const bool fused_sort = T <= moe::norm_router_sort_limit();
     if (fused_sort) {
       // the (single) norm/router workgroup sorts the pairs
@@ -493,36 +493,36 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
     if (!fused_sort) MOE_HIP(moe::launch_permute(d, pp, s));
 
     moe::ExpertParams ep{};
-    ep.xhat = c->xhat;
+    ep.xhat = W.xhat;
     ep.cnt = pp.cnt;
     ep.off = pp.off;
     ep.perm = pp.perm;
-    ep.active = c->active;
-    ep.n_active = c->n_active;
-    ep.desc = c->desc;
+    ep.active = W.active;
+    ep.n_active = W.n_active;
+    ep.desc = W.desc;
     ep.w_gate = c->gate + l * c->gate_layer;
     ep.w_up = c->up + l * c->gate_layer;
     ep.w_down = c->down + l * c->down_layer;
-    ep.act = c->act;
-    ep.y = c->y;
+    ep.act = W.act;
+    ep.y = W.y;
     ep.T = T;
     if (c->gemm_ok && T >= kGemmMinTokens) {
       // prefill-sized: grouped GEMM over (slot, feature tile, token tile) items
-      moe::GemmTileParams tp{pp.cnt, pp.off, T, c->tiles, c->n_tiles};
+      moe::GemmTileParams tp{pp.cnt, pp.off, T, W.tiles, W.n_tiles};
       MOE_HIP(moe::launch_tile_list(d, tp, s));
       moe::GemmParams gp{};
-      gp.xhat = c->xhat;
+      gp.xhat = W.xhat;
       gp.w_gate = ep.w_gate;
       gp.w_up = ep.w_up;
       gp.w_down = ep.w_down;
       gp.perm = pp.perm;
-      gp.tiles = c->tiles;
-      gp.n_tiles = c->n_tiles;
-      gp.act = c->act;
-      gp.y = c->y;
+      gp.tiles = W.tiles;
+      gp.n_tiles = W.n_tiles;
+      gp.act = W.act;
+      gp.y = W.y;
       gp.T = T;
-      gp.xhat_zero_row = static_cast<int>(c->tw);
-      gp.act_zero_row = static_cast<int>(c->tw * (g.top_k + g.n_shared));
+      gp.xhat_zero_row = static_cast<int>(W.tw);
+      gp.act_zero_row = static_cast<int>(W.tw * (g.top_k + g.n_shared));
       if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_EXPERT_UP], s));
       MOE_HIP(moe::launch_grouped_gemm(d, gp, 1, s));
       if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_EXPERT_UP], s));
@@ -542,7 +542,14 @@ int run_blocks(moe_verify_ctx* c, const void* hidden, int T, const moe_verify_au
   return MOE_OK;
 }
 
-int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, const int32_t* positions, int32_t B,
+// The context's own workspace (an empty one for a NULL context, which
+// step_impl rejects before using it).
+const moe::api::Workspace& ws_of(const moe_verify_ctx* c) {
+  static const moe::api::Workspace none{};
+  return c ? c->ws : none;
+}
+
+int step_impl(moe_verify_ctx* c, const moe::api::Workspace& W, const void* hidden, const int32_t* drafts, const int32_t* positions, int32_t B,
               int32_t K, int32_t* committed, int32_t* counts, const moe_verify_aux* aux, void* stream) {
   if (!c) return fail(MOE_EINVAL, "ctx is NULL");
   const moe_verify_config& g = c->cfg;
@@ -568,16 +575,16 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, cons
 
   const void* x_last = nullptr;
   MOE_HIP(mark(c->ev_before[MOE_STAGE_ALL], s));
-  if ((r = run_blocks(c, hidden, T, aux, 0, g.n_layers, s, &x_last, positions, B, K + 1))) return r;
+  if ((r = run_blocks(c, W, hidden, T, aux, 0, g.n_layers, s, &x_last, positions, B, K + 1))) return r;
 
   const int64_t H = g.hidden, k = g.top_k;
   const int li = g.n_layers - 1;
   moe::LmHeadParams lp{};
-  lp.xf = c->xhat;
+  lp.xf = W.xhat;
   lp.lm = c->lm;
   lp.T = T;
-  lp.keys = c->keys;
-  lp.key_stride = static_cast<int>(c->tw);
+  lp.keys = W.keys;
+  lp.key_stride = static_cast<int>(W.tw);
   lp.drafts = drafts;
   lp.B = B;
   lp.K = K;
@@ -587,24 +594,24 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, cons
   if (d.bf16) {
     // final combine + norm: one workgroup per row
     lp.x_in = x_last;
-    lp.y = c->y;
-    lp.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
-    lp.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
+    lp.y = W.y;
+    lp.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : W.idx[li & 1];
+    lp.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : W.w[li & 1];
     lp.gamma = c->final_gamma;
     lp.x_out = aux ? aux->hidden_out : nullptr;
     lp.m_out = aux && aux->moe_out ? aux->moe_out + li * T * H : nullptr;
-    lp.xf_out = c->xhat;
+    lp.xf_out = W.xhat;
     MOE_HIP(moe::launch_final_norm(d, lp, s));
   } else {
     moe::NormRouterParams nr{};
     nr.x_in = x_last;
-    nr.x_out = aux && aux->hidden_out ? aux->hidden_out : c->xres;
-    nr.y = c->y;
-    nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : c->idx[li & 1];
-    nr.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : c->w[li & 1];
+    nr.x_out = aux && aux->hidden_out ? aux->hidden_out : W.xres;
+    nr.y = W.y;
+    nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx + li * T * k : W.idx[li & 1];
+    nr.prev_w = aux && aux->topk_w ? aux->topk_w + li * T * k : W.w[li & 1];
     nr.m_out = aux && aux->moe_out ? aux->moe_out + li * T * H : nullptr;
     nr.gamma = c->final_gamma;
-    nr.xhat = c->xhat;
+    nr.xhat = W.xhat;
     nr.T = T;
     nr.combine = 1;
     nr.norm = 1;
@@ -620,6 +627,15 @@ int step_impl(moe_verify_ctx* c, const void* hidden, const int32_t* drafts, cons
 }
 
 }  // namespace
+
+namespace moe {
+namespace api {
+int verify_step_with(moe_verify_ctx* c, const Workspace& W, const void* hidden, const int32_t* drafts, int32_t B,
+                     int32_t K, int32_t* committed, int32_t* counts, void* stream) {
+  return step_impl(c, W, hidden, drafts, nullptr, B, K, committed, counts, nullptr, stream);
+}
+}  // namespace api
+}  // namespace moe
 
 extern "C" {
 
@@ -637,6 +653,9 @@ int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* weig
   } catch (...) {
     r = fail(MOE_ENOMEM, "host exception during init");
   }
+  // the static scratch of moe_verify_step_static on this device (the
+  // context's device is current here)
+  if (r == MOE_OK) r = moe::api::static_scratch_setup(c->device);
   if (r != MOE_OK) {
     const std::string keep = moe::api::last_error();
     ctx_free(c);
@@ -650,14 +669,14 @@ int moe_verify_init(const moe_verify_config* cfg, const moe_verify_weights* weig
 
 int moe_verify_step(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
                     int32_t* committed, int32_t* counts, void* hip_stream) {
-  const int r = step_impl(ctx, hidden, drafts, nullptr, B, K, committed, counts, nullptr, hip_stream);
+  const int r = step_impl(ctx, ws_of(ctx), hidden, drafts, nullptr, B, K, committed, counts, nullptr, hip_stream);
   if (ctx) clear_hooks(ctx);
   return r;
 }
 
 int moe_verify_step_ex(moe_verify_ctx* ctx, const void* hidden, const int32_t* drafts, int32_t B, int32_t K,
                        int32_t* committed, int32_t* counts, const moe_verify_aux* aux, void* hip_stream) {
-  const int r = step_impl(ctx, hidden, drafts, nullptr, B, K, committed, counts, aux, hip_stream);
+  const int r = step_impl(ctx, ws_of(ctx), hidden, drafts, nullptr, B, K, committed, counts, aux, hip_stream);
   if (ctx) clear_hooks(ctx);
   return r;
 }
@@ -669,7 +688,7 @@ int moe_verify_step_kv(moe_verify_ctx* ctx, const void* hidden, const int32_t* d
     if (ctx) clear_hooks(ctx);
     return fail(MOE_EINVAL, "positions is NULL");
   }
-  const int r = step_impl(ctx, hidden, drafts, positions, B, K, committed, counts, aux, hip_stream);
+  const int r = step_impl(ctx, ws_of(ctx), hidden, drafts, positions, B, K, committed, counts, aux, hip_stream);
   if (ctx) clear_hooks(ctx);
   return r;
 }
@@ -692,7 +711,7 @@ int moe_verify_graph_create(moe_verify_ctx* ctx, const void* hidden, const int32
     if (ctx->ev_before[i] || ctx->ev_after[i]) return fail(MOE_EINVAL, "a timing hook is set; clear it first");
   return moe::api::capture_graph(
       hip_stream,
-      [&]() { return step_impl(ctx, hidden, drafts, nullptr, B, K, committed, counts, nullptr, hip_stream); },
+      [&]() { return step_impl(ctx, ws_of(ctx), hidden, drafts, nullptr, B, K, committed, counts, nullptr, hip_stream); },
       out);
 }
 
@@ -707,7 +726,7 @@ int moe_verify_graph_create_kv(moe_verify_ctx* ctx, const void* hidden, const in
     if (ctx->ev_before[i] || ctx->ev_after[i]) return fail(MOE_EINVAL, "a timing hook is set; clear it first");
   return moe::api::capture_graph(
       hip_stream,
-      [&]() { return step_impl(ctx, hidden, drafts, positions, B, K, committed, counts, nullptr, hip_stream); },
+      [&]() { return step_impl(ctx, ws_of(ctx), hidden, drafts, positions, B, K, committed, counts, nullptr, hip_stream); },
       out);
 }
 
@@ -743,13 +762,13 @@ int block_impl(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, voi
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const void* x_last = nullptr;
   MOE_HIP(mark(ctx->ev_before[MOE_STAGE_ALL], s));
-  if ((r = run_blocks(ctx, x, T, aux, layer, 1, s, &x_last))) return r;
+  if ((r = run_blocks(ctx, ctx->ws, x, T, aux, layer, 1, s, &x_last))) return r;
   moe::NormRouterParams nr{};
   nr.x_in = x;
   nr.x_out = y;
-  nr.y = ctx->y;
-  nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx : ctx->idx[0];
-  nr.prev_w = aux && aux->topk_w ? aux->topk_w : ctx->w[0];
+  nr.y = ctx->ws.y;
+  nr.prev_idx = aux && aux->topk_idx ? aux->topk_idx : ctx->ws.idx[0];
+  nr.prev_w = aux && aux->topk_w ? aux->topk_w : ctx->ws.w[0];
   nr.m_out = aux ? aux->moe_out : nullptr;
   nr.T = T;
   nr.combine = 1;

@@ -12,12 +12,40 @@
 #include "kernels.h"
 #include "moe_verify.h"
 
+namespace moe {
+namespace api {
+
+// Device workspace of a verify step or block: the context's own (allocated
+// by moe_verify_init for max(max_tokens, max_prefill_tokens) rows), or one
+// carved out of the library's static scratch array for a call that may not
+// allocate.
+struct Workspace {
+  int64_t tw = 0;           // token capacity
+  char* xres = nullptr;     // [tw][H] storage
+  char* xhat = nullptr;     // [tw+1][H] storage (row tw all zero)
+  int* idx[2] = {nullptr, nullptr};   // [tw][k]
+  float* w[2] = {nullptr, nullptr};   // [tw][k]
+  int* cnt = nullptr;       // [E]
+  int* off = nullptr;       // [E+1]
+  int* perm = nullptr;      // [tw*k]
+  int* active = nullptr;    // [E]
+  int* n_active = nullptr;  // [1]
+  int4* desc = nullptr;     // [E] routed slot descriptors
+  char* act = nullptr;      // [tw*(k+S)+1][I] storage (last row all zero)
+  float* y = nullptr;       // [tw*(k+S)][H]
+  unsigned long long* keys = nullptr;  // [kKeySlots][tw], zero between steps
+  int4* tiles = nullptr;    // grouped-GEMM tile table (contexts with the GEMM path)
+  int* n_tiles = nullptr;
+};
+
+}  // namespace api
+}  // namespace moe
+
 struct moe_verify_ctx {
   moe_verify_config cfg;
   moe::Dims d;
   int device = 0;
   size_t esize = 0;         // bytes per stored element
-  int64_t tw = 0;           // workspace token capacity
   std::vector<void*> allocs;
 
   // repacked weights
@@ -30,20 +58,7 @@ struct moe_verify_ctx {
   char* lm = nullptr;       // bf16 tiled [Vpad/16][H/32][512]; f32 [V][H]
   size_t router_layer = 0, gate_layer = 0, down_layer = 0;
 
-  // workspace
-  char* xres = nullptr;     // [tw][H] storage
-  char* xhat = nullptr;     // [tw][H] storage
-  int* idx[2] = {nullptr, nullptr};   // [tw][k]
-  float* w[2] = {nullptr, nullptr};   // [tw][k]
-  int* cnt = nullptr;       // [E]
-  int* off = nullptr;       // [E+1]
-  int* perm = nullptr;      // [tw*k]
-  int* active = nullptr;    // [E]
-  int* n_active = nullptr;  // [1]
-  int4* desc = nullptr;     // [E] routed slot descriptors
-  char* act = nullptr;      // [tw*(k+S)][I] storage
-  float* y = nullptr;       // [tw*(k+S)][H]
-  unsigned long long* keys = nullptr;  // [kKeySlots][tw]
+  moe::api::Workspace ws;   // workspace of moe_verify_step and friends
 
   // attention (cfg.n_heads > 0)
   moe::Dims dq{}, dout{};              // q/k/v projection (3 slots), output projection (1 slot)
@@ -59,8 +74,6 @@ struct moe_verify_ctx {
   float* apart = nullptr;              // attention partials
   int* zero = nullptr;                 // a device 0 (no routed experts in the projections)
 
-  int4* tiles = nullptr;               // grouped-GEMM tile table
-  int* n_tiles = nullptr;
   bool gemm_ok = false;                // LDS allows the prefill grouped GEMM
 
   // one-call timing hooks (moe_verify_set_stage_events)
@@ -98,6 +111,14 @@ int capture_graph(void* hip_stream, const std::function<int()>& enqueue, moe_ver
 
 // Synchronise `device` and free every allocation in `allocs`.
 void dev_free_all(std::vector<void*>& allocs, int device);
+
+// A verify step (no attention, no aux outputs) on workspace W.
+int verify_step_with(moe_verify_ctx* c, const Workspace& W, const void* hidden, const int32_t* drafts, int32_t B,
+                     int32_t K, int32_t* committed, int32_t* counts, void* stream);
+
+// Look up, once per device, the device address of the static scratch array
+// behind moe_verify_step_static; `device` must be current.
+int static_scratch_setup(int device);
 
 }  // namespace api
 }  // namespace moe

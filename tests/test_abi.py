@@ -105,6 +105,8 @@ def test_step_and_block_reject_null_context():
     assert rc == B.MOE_EINVAL
     rc = lib.moe_block_forward(None, 0, FAKE, 4, FAKE, None, None)
     assert rc == B.MOE_EINVAL
+    rc = lib.moe_verify_step_static(None, FAKE, FAKE, 1, 3, FAKE, FAKE, None)
+    assert rc == B.MOE_EINVAL and "ctx" in B.moe_verify_last_error()
 
 
 def test_destroy_null_is_a_no_op():
