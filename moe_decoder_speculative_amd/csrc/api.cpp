@@ -313,7 +313,10 @@ int create(const moe_verify_config& g, const moe_verify_weights& w, hipStream_t 
   if ((r = ctx_alloc_t(c, E * sizeof(int), &c->ws.active))) return r;
   if ((r = ctx_alloc_t(c, 16, &c->ws.n_active))) return r;
   if ((r = ctx_alloc_t(c, E * sizeof(int4), &c->ws.desc))) return r;
-  if ((r = ctx_alloc(c, (rows + 1) * I * es, &c->ws.act))) return r;
+  // pair rows (decode kernels) plus an all-zero row, or the grouped GEMM's
+  // tiled rows, whichever is larger
+  const int64_t act_rows = std::max<int64_t>(rows + 1, c->gemm_ok ? moe::gemm_act_rows(d, static_cast<int>(tw)) : 0);
+  if ((r = ctx_alloc(c, act_rows * I * es, &c->ws.act))) return r;
   MOE_HIP(hipMemsetAsync(c->ws.act + rows * I * es, 0, I * es, s));
   if ((r = ctx_alloc_t(c, rows * H * sizeof(float), &c->ws.y))) return r;
   if ((r = ctx_alloc_t(c, moe::kKeySlots * tw * sizeof(unsigned long long), &c->ws.keys))) return r;
@@ -436,8 +439,14 @@ int run_attention(moe_verify_ctx* c, const moe::api::Workspace& W, const void* x
   return MOE_OK;
 }
 
+// True when a block over T rows runs its experts as grouped GEMMs.
+bool use_gemm(const moe_verify_ctx* c, int T) { return c->gemm_ok && T >= kGemmMinTokens; }
+
+// bf16_rows: the grouped GEMM writes bf16 gate-weighted expert rows (a
+// prefill block, combined by launch_combine_bf16) instead of fp32 rows.
 int run_blocks(moe_verify_ctx* c, const moe::api::Workspace& W, const void* hidden, int T, const moe_verify_aux* aux, int layer0, int nlayers,
-               hipStream_t s, const void** x_last, const int* positions = nullptr, int B = 0, int K1 = 0) {
+               hipStream_t s, const void** x_last, const int* positions = nullptr, int B = 0, int K1 = 0,
+               bool bf16_rows = false) {
   const moe::Dims& d = c->d;
   const moe_verify_config& g = c->cfg;
   const int64_t H = g.hidden, k = g.top_k, E = g.n_routed;
@@ -506,7 +515,7 @@ int run_blocks(moe_verify_ctx* c, const moe::api::Workspace& W, const void* hidd
     ep.act = W.act;
     ep.y = W.y;
     ep.T = T;
-    if (c->gemm_ok && T >= kGemmMinTokens) {
+    if (use_gemm(c, T)) {
       // prefill-sized: grouped GEMM over (slot, feature tile, token tile) items
       moe::GemmTileParams tp{pp.cnt, pp.off, T, W.tiles, W.n_tiles};
       MOE_HIP(moe::launch_tile_list(d, tp, s));
@@ -522,7 +531,8 @@ int run_blocks(moe_verify_ctx* c, const moe::api::Workspace& W, const void* hidd
       gp.y = W.y;
       gp.T = T;
       gp.xhat_zero_row = static_cast<int>(W.tw);
-      gp.act_zero_row = static_cast<int>(W.tw * (g.top_k + g.n_shared));
+      gp.yb = bf16_rows ? reinterpret_cast<bf16_t*>(W.y) : nullptr;
+      gp.gate_w = wg;
       if (li == 0) MOE_HIP(mark(c->ev_before[MOE_STAGE_EXPERT_UP], s));
       MOE_HIP(moe::launch_grouped_gemm(d, gp, 1, s));
       if (li == 0) MOE_HIP(mark(c->ev_after[MOE_STAGE_EXPERT_UP], s));
@@ -762,7 +772,20 @@ int block_impl(moe_verify_ctx* ctx, int32_t layer, const void* x, int32_t T, voi
   hipStream_t s = static_cast<hipStream_t>(hip_stream);
   const void* x_last = nullptr;
   MOE_HIP(mark(ctx->ev_before[MOE_STAGE_ALL], s));
-  if ((r = run_blocks(ctx, ctx->ws, x, T, aux, layer, 1, s, &x_last))) return r;
+  const bool bf16_rows = use_gemm(ctx, T);
+  if ((r = run_blocks(ctx, ctx->ws, x, T, aux, layer, 1, s, &x_last, nullptr, 0, 0, bf16_rows))) return r;
+  if (bf16_rows) {
+    moe::CombineParams cp{};
+    cp.x_in = x;
+    cp.x_out = y;
+    cp.yb = reinterpret_cast<const bf16_t*>(ctx->ws.y);
+    cp.idx = aux && aux->topk_idx ? aux->topk_idx : ctx->ws.idx[0];
+    cp.m_out = aux ? aux->moe_out : nullptr;
+    cp.T = T;
+    MOE_HIP(moe::launch_combine_bf16(ctx->d, cp, s));
+    MOE_HIP(mark(ctx->ev_after[MOE_STAGE_ALL], s));
+    return MOE_OK;
+  }
   moe::NormRouterParams nr{};
   nr.x_in = x;
   nr.x_out = y;

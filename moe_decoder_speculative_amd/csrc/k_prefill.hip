@@ -1,26 +1,36 @@
-// Expert grouped GEMM on bf16 MFMA for prefill-sized token counts.
+// Expert grouped GEMM on bf16 MFMA for prefill-sized token counts, and the
+// combine of its bf16 expert rows.
 //
 // At prefill sizes (about 915 tokens per routed expert, every token for each
 // shared expert) the experts are bound by MFMA throughput, not HBM.  Work item
-// = (expert slot, tile of 128 output features, tile of 256 of the slot's
-// tokens).  A 512-thread workgroup computes one item: its operands for each
-// 32-wide step of the reduction dimension -- 16 weight row tiles (already in
-// MFMA operand order in HBM) and 16 token tiles gathered through the
-// permutation (padding lanes read an all-zero row) -- go straight from global
-// memory into a 4-stage LDS ring with gfx950's direct-to-LDS 16-byte loads
-// (no registers, three steps in flight), and each of the eight wavefronts
-// (two per SIMD, so one's MFMAs cover the other's waits) accumulates a
-// 128 x 64 (rows x tokens) tile with 16x16x32 bf16 MFMAs (128 accumulators
-// per lane).
-//   up:   rows are 8 gate + 8 up tiles of the same 128 features; epilogue
-//         a = round(silu(g) * u) written per pair (bf16)
-//   down: rows are 16 tiles of 16 hidden features; epilogue y (fp32) per pair
-// Items are numbered slot-major, feature-tile, token-tile, and handed out so
+// = (expert slot, tile of 256 weight rows, tile of 128 of the slot's tokens).
+// A 256-thread workgroup computes one item, one wavefront per SIMD, each
+// wavefront a 128 x 64 (rows x tokens) block of 32x32x16 bf16 MFMAs (128
+// accumulators per lane); a workgroup needs 72 KiB of LDS, so two run on
+// every CU and one's prologue, epilogue and memory waits are covered by the
+// other's MFMAs.  The operands of each 32-wide step of the reduction -- 16
+// weight row tiles (already in 16x32 MFMA operand order in HBM) and 8 token
+// tiles -- go straight from global memory into a 3-stage LDS ring with
+// gfx950's direct-to-LDS 16-byte loads (two steps in flight); the 32x32x16
+// fragments are read out of the 16x32 tiles with a lane-dependent offset.
+// The loads, not the MFMAs, bound the loop (the vector-memory address unit
+// is busy most of the time): a 16x32 token tile gathered from 16 rows costs
+// it more than a contiguous 1 KiB tile, so the down GEMM reads activation
+// tiles that the up GEMM wrote in operand-tile order.
+//   up:   rows are 8 gate + 8 up tiles of the same 128 features; token rows
+//         of xhat gathered through the permutation (padding lanes read an
+//         all-zero row); epilogue a = round(silu(g) * u) written in
+//         operand-tile order at row 128 * (item's token tile) + token
+//   down: rows are 16 tiles of 16 hidden features; epilogue per pair either
+//         y (fp32; a verify step, whose next router must see the exact sum)
+//         or round(w * y) (bf16, the pair's gate weight applied; the prefill
+//         block, which the 2e-2 tolerance of its output covers)
+// Items are numbered slot-major, token tile, feature tile, and handed out so
 // that each XCD works through a contiguous range of them: the workgroups that
-// share a weight tile run together on one XCD and hit in its L2.
-// Shared experts occupy slots 0..S-1.  The 64 routed + 2 shared experts with
-// top-6 routing follow the page "Jina AI releases lightweight OCR model with
-// built-in speculative decoding", section "Lean architecture with a
+// share a token tile or a weight tile run together on one XCD and hit in its
+// L2.  Shared experts occupy slots 0..S-1.  The 64 routed + 2 shared experts
+// with top-6 routing follow the page "Jina AI releases lightweight OCR model
+// with built-in speculative decoding", section "Lean architecture with a
 // compressed encoder"; a page holds at most 1,156 visual tokens (same
 // section), which makes a multi-page prefill thousands of rows.
 #include "kernels.h"
@@ -29,13 +39,16 @@ namespace moe {
 
 namespace {
 
-constexpr int kBT = 256;          // tokens per item
-constexpr int kRowTiles = 16;     // MFMA row tiles per item
+constexpr int kBT = 128;          // tokens per item
+constexpr int kRowTiles = 16;     // MFMA row tiles per item (256 rows)
 constexpr int kTokTiles = kBT / kTile;
-constexpr int kStages = 4;        // LDS ring depth (one 32-wide k-step per stage), 128 KiB
-constexpr int kStageBytes = (kRowTiles + kTokTiles) * kFragElems * 2;   // 32 KiB
+constexpr int kStages = 3;        // LDS ring depth (one 32-wide k-step per stage, 24 KiB each)
+constexpr int kStageBytes = (kRowTiles + kTokTiles) * kFragElems * 2;
 constexpr int kXcds = 8;
-constexpr int kGemmThreads = 512;  // 8 wavefronts: two per SIMD
+constexpr int kGemmThreads = 256;  // 4 wavefronts: one per SIMD; two workgroups per CU
+constexpr int kLoadsA = kRowTiles / 4;  // weight fragments a wavefront stages per step (4)
+constexpr int kLoadsB = kTokTiles / 4;  // token fragments a wavefront stages per step (2)
+constexpr int kLoads = kLoadsA + kLoadsB;
 
 // Tile table: one entry per (slot, token tile), shared slots first, then the
 // routed experts in ascending order.  Built on the device after the
@@ -64,14 +77,17 @@ __global__ __launch_bounds__(64) void k_tile_list(Dims d, GemmTileParams p) {
   if (lane == kWave - 1) *p.n_tiles = n_shared + incl;
 }
 
-template <bool UP>
-__global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(Dims d, GemmParams p) {
+// OUT: 0 act (up), 1 fp32 y (down), 2 bf16 gate-weighted y (down)
+template <bool UP, int OUT>
+__global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(Dims d, GemmParams p) {
   // LDS ring of kStages stages; a stage holds one 32-wide k-step: 16 weight
-  // fragments then 16 token fragments, 1 KiB each, in MFMA operand order.
+  // fragments then 8 token fragments, 1 KiB each, in MFMA operand order.
   extern __shared__ __align__(16) unsigned char smem[];
 
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int wr = wave / 4, wt = wave % 4;         // wavefront's row half / token quarter
+  // the wavefront index is uniform: keeping it in a scalar register makes the
+  // LDS destinations and weight pointers of the loads scalar
+  const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wr = wave / 2, wt = wave % 2;         // wavefront's row half / token half
   const int n_ft = UP ? d.I / 128 : d.H / 256;     // feature tiles per slot
   const int n_items = *p.n_tiles * n_ft;
   const int chunk = (n_items + kXcds - 1) / kXcds;
@@ -85,8 +101,7 @@ __global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(Dims d, GemmParam
   const bool shared = tile.y >= 0;
   const int base = shared ? 0 : -1 - tile.y;
 
-  // pair id of the item's i-th token (-1: padding); its result row.  Read from
-  // the permutation when needed (the LDS is all ring).
+  // pair id of the item's i-th token (-1: padding); its result row
   auto pair_of = [&](int i) -> int {
     if (i >= ntok) return -1;
     return shared ? p.T * d.k + tile.y * p.T + m0 + i : p.perm[base + m0 + i];
@@ -97,17 +112,15 @@ __global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(Dims d, GemmParam
   const bf16_t* wa = reinterpret_cast<const bf16_t*>(UP ? p.w_gate : p.w_down);
   const bf16_t* wu = reinterpret_cast<const bf16_t*>(p.w_up);
   const bf16_t* src = reinterpret_cast<const bf16_t*>(UP ? p.xhat : p.act);
-  const int zero_row = UP ? p.xhat_zero_row : p.act_zero_row;
   const int rows_per_expert_tiles = UP ? d.I / kTile : d.H / kTile;
 
-  // this wavefront fills weight fragments 2w, 2w+1 and token fragments
-  // 2w, 2w+1 of every stage; lane offsets (elements, 32-bit) advance by one
-  // k-step per stage
-  int woff[2], toff[2];
-  const bf16_t* wmat[2];
+  // this wavefront stages weight fragments 4w..4w+3 and token fragments
+  // 2w, 2w+1 of every stage; lane offsets (elements) from scalar bases
+  uint32_t woff = lane * 8, toff[kLoadsB];
+  const bf16_t* wmat[kLoadsA];
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int r = wave * 2 + q;  // weight row tile of the item
+  for (int q = 0; q < kLoadsA; ++q) {
+    const int r = wave * kLoadsA + q;  // weight row tile of the item
     int row_tile;
     if (UP) {
       const int half = r / 8, qq = r % 8;
@@ -117,142 +130,267 @@ __global__ __launch_bounds__(kGemmThreads) void k_grouped_gemm(Dims d, GemmParam
       wmat[q] = wa;
       row_tile = ft * 16 + r;
     }
-    woff[q] = ((expert * rows_per_expert_tiles + row_tile) * KT) * kFragElems + lane * 8;
-    const int pr = pair_of(r * kTile + lane % kTile);  // token tile r of the item
-    int row = zero_row;
-    if (pr >= 0) row = UP ? (shared ? pr - p.T * d.k - tile.y * p.T : pr / d.k) : pr;
-    toff[q] = row * Kd + (lane / kTile) * 8;
+    wmat[q] += static_cast<int64_t>(expert * rows_per_expert_tiles + row_tile) * KT * kFragElems;
+  }
+  // up: token rows of xhat gathered through the permutation (padding lanes
+  // read an all-zero row), 64 contiguous bytes per row and k-step;
+  // down: the item's activation tiles, 1 KiB contiguous per fragment (the up
+  // GEMM writes them in operand-tile order at the item's tile index)
+  const int tix = item / n_ft;
+#pragma unroll
+  for (int q = 0; q < kLoadsB; ++q) {
+    const int r = wave * kLoadsB + q;  // token tile of the item
+    if constexpr (UP) {
+      const int pr = pair_of(r * kTile + lane % kTile);
+      int row = p.xhat_zero_row;
+      if (pr >= 0) row = shared ? pr - p.T * d.k - tile.y * p.T : pr / d.k;
+      toff[q] = static_cast<uint32_t>(row) * Kd + (lane / kTile) * 8;
+    } else {
+      toff[q] = static_cast<uint32_t>((tix * kTokTiles + r) * KT) * kFragElems + lane * 8;
+    }
   }
   auto issue = [&](int kt) {
     unsigned char* st = smem + (kt % kStages) * kStageBytes;
 #pragma unroll
-    for (int q = 0; q < 2; ++q) {
-      __builtin_amdgcn_global_load_lds((void*)(wmat[q] + woff[q] + kt * kFragElems),
-                                       (lds_ptr_t)(st + (wave * 2 + q) * 1024), 16, 0, 0);
-      __builtin_amdgcn_global_load_lds((void*)(src + toff[q] + kt * kKStep),
-                                       (lds_ptr_t)(st + (kRowTiles + wave * 2 + q) * 1024), 16, 0, 0);
-    }
+    for (int q = 0; q < kLoadsA; ++q)
+      __builtin_amdgcn_global_load_lds((void*)((wmat[q] + kt * kFragElems) + woff),
+                                       (lds_ptr_t)(st + (wave * kLoadsA + q) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kLoadsB; ++q)
+      __builtin_amdgcn_global_load_lds((void*)((src + kt * (UP ? kKStep : kFragElems)) + toff[q]),
+                                       (lds_ptr_t)(st + (kRowTiles + wave * kLoadsB + q) * 1024), 16, 0, 0);
   };
 
-  // result rows of this wavefront's 64 tokens, looked up while the loop runs
-  int out_pair[4];
+  // result rows of this wavefront's 64 tokens (token blocks of 32), looked up
+  // while the loop runs
+  int out_pair[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) out_pair[j] = pair_of((wt * 4 + j) * kTile + lane % kTile);
+  for (int n = 0; n < 2; ++n) out_pair[n] = pair_of(wt * 64 + n * 32 + lane % 32);
 
-  f32x4_t acc[8][4];
+  // 32x32x16 MFMAs on fragments read from the 16x32 operand tiles of the
+  // ring: the fragment of 32 rows (tiles 2b, 2b+1) and reduction half kk of a
+  // step gives lane L row L%32, reduction elements 16kk + 8(L/32) .. +8, which
+  // sit in tile 2b + (L%32)/16 at lane slot L%16 + 16(2kk + L/32).
+  const int lane_off = ((lane >> 4) & 1) * 1024 + ((lane & 15) + 16 * (lane >> 5)) * 16;
+  f32x16_t acc[4][2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  // Fragment registers, double buffered: step k+1 is read from LDS while the
-  // 32 MFMAs of step k run.  KT is even (H and I are multiples of 128), so the
-  // loop runs in pairs with the two register sets in fixed roles.
+  // Fragment registers, double buffered (step k+1 is read from LDS while the
+  // 16 MFMAs of step k run); the loop is unrolled by two so the two register
+  // sets keep fixed roles.
   //
   // The barriers are bare: a fenced barrier would wait for every load in
   // flight, later steps included, and drain the ring.  LDS-DMA writes are
   // complete once vmcnt says so; each wavefront waits for its own loads of a
   // step before the barrier, so after it every wavefront's share has landed.
-  bf16x8_t a0[8], b0[4], a1[8], b1[4];
+  // Each wavefront also waits for its own LDS reads of the stage the loads
+  // issued after the barrier overwrite (read one step earlier) before it
+  // arrives, so no read of a stage can be overtaken by its refill.
+  bf16x8_t a0[2][4], b0[2][2], a1[2][4], b1[2][2];
 #define MOE_READ_STEP(K, A, B)                                                                     \
   {                                                                                                \
-    const unsigned char* st_ = smem + ((K) % kStages) * kStageBytes;                               \
-    _Pragma("unroll") for (int j = 0; j < 4; ++j) B[j] =                                           \
-        *reinterpret_cast<const bf16x8_t*>(st_ + (kRowTiles + wt * 4 + j) * 1024 + lane * 16);     \
-    _Pragma("unroll") for (int i = 0; i < 8; ++i) A[i] =                                           \
-        *reinterpret_cast<const bf16x8_t*>(st_ + (wr * 8 + i) * 1024 + lane * 16);                 \
+    const unsigned char* st_ = smem + ((K) % kStages) * kStageBytes + lane_off;                    \
+    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                             \
+      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
+        B[kk][j] = *reinterpret_cast<const bf16x8_t*>(st_ + (kRowTiles + wt * 4 + 2 * j) * 1024 + kk * 512); \
+      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
+        A[kk][i] = *reinterpret_cast<const bf16x8_t*>(st_ + (wr * 8 + 2 * i) * 1024 + kk * 512);   \
+    }                                                                                              \
   }
 #define MOE_MMA_STEP(A, B)                                                                         \
-  _Pragma("unroll") for (int i = 0; i < 8; ++i)                                                    \
-  _Pragma("unroll") for (int j = 0; j < 4; ++j) acc[i][j] = mfma16(A[i], B[j], acc[i][j]);
-  // wait for this wavefront's loads of step k+1 at iteration k: the steps
-  // issued after it (up to two) may stay in flight, 4 loads each
-#define MOE_WAIT_NEXT(K)                                                                           \
+  _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                                 \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(A[kk][i], B[kk][j], acc[i][j]);
+// One step K (its fragments in CA/CB): make step K+1 available -- wait until
+// at most VM of this wavefront's loads (the steps issued after K+1) are in
+// flight, wait for its own reads of step K, bare barrier, refill step K's
+// stage with step K+3 when ISSUE -- then run step K's 16 MFMAs with step
+// K+1's 12 fragment reads interleaved.
+#define MOE_STEP(K, CA, CB, NA, NB, VM, ISSUE, NEXT)                                               \
   {                                                                                                \
-    const int later_ = min(KT, (K) + kStages) - (K) - 2;                                           \
-    if (later_ >= 2) __builtin_amdgcn_s_waitcnt(waitcnt_vm(8));                                    \
-    else if (later_ == 1) __builtin_amdgcn_s_waitcnt(waitcnt_vm(4));                               \
-    else __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));                                                \
-  }
-// One step: make step K+1 available (wait for this wavefront's loads, bare
-// barrier, refill the ring), then run step K's 32 MFMAs with step K+1's 12
-// fragment reads interleaved (a read after every 2 or 3 MFMAs).  Interleaving
-// matters: with all reads ahead of the MFMAs, the first MFMA waits for all of
-// them (the LDS counter cannot express "16 newer reads may stay in flight").
-// At the last step the reads fetch a stale stage that is never used.
-#define MOE_STEP(K, CA, CB, NA, NB)                                                                \
-  {                                                                                                \
-    if ((K) + 1 < KT) {                                                                            \
-      MOE_WAIT_NEXT(K)                                                                             \
+    if (NEXT) {                                                                                    \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));                                                  \
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0); /* this wavefront's reads of step K done */       \
       __builtin_amdgcn_s_barrier(); /* step K+1 landed; everyone has read step K */                \
-      if ((K) + kStages < KT) issue((K) + kStages); /* into step K's buffer */                     \
+      if (ISSUE) issue((K) + kStages); /* into step K's buffer */                                  \
     }                                                                                              \
     MOE_MMA_STEP(CA, CB)                                                                           \
-    MOE_READ_STEP((K) + 1, NA, NB)                                                                 \
-    _Pragma("unroll") for (int g_ = 0; g_ < 8; ++g_) {                                             \
-      __builtin_amdgcn_sched_group_barrier(0x008, 3, 0); /* 3 MFMA */                              \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* 1 LDS read */                          \
-    }                                                                                              \
-    _Pragma("unroll") for (int g_ = 0; g_ < 4; ++g_) {                                             \
-      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0); /* 2 MFMA */                              \
-      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* 1 LDS read */                          \
+    if (NEXT) {                                                                                    \
+      MOE_READ_STEP((K) + 1, NA, NB)                                                               \
+      _Pragma("unroll") for (int g_ = 0; g_ < 4; ++g_) {                                           \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* 1 MFMA */                            \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* 1 LDS read */                        \
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
+        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                         \
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
+      }                                                                                            \
     }                                                                                              \
   }
 
+  // KT is even and >= 8 (H and I are multiples of 128).  Steps 0..KT-4 refill
+  // the ring (issue step k+3) and wait until one later step may stay in
+  // flight; steps KT-3..KT-1 drain it.  Step k uses register set k % 2.
 #pragma unroll
-  for (int s = 0; s < kStages; ++s)
-    if (s < KT) issue(s);
-  // step 0 landed once the other issued steps (up to kStages - 1) remain
-  static_assert(kStages == 4, "wait counts below assume a 4-stage ring");
-  switch (min(KT, kStages) - 1) {
-    case 3: __builtin_amdgcn_s_waitcnt(waitcnt_vm(12)); break;
-    case 2: __builtin_amdgcn_s_waitcnt(waitcnt_vm(8)); break;
-    case 1: __builtin_amdgcn_s_waitcnt(waitcnt_vm(4)); break;
-    default: __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); break;
-  }
+  for (int s = 0; s < kStages; ++s) issue(s);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoads));  // step 0 landed, 1 and 2 may be in flight
   __builtin_amdgcn_s_barrier();
   MOE_READ_STEP(0, a0, b0)
-  for (int k = 0; k < KT; k += 2) {
-    MOE_STEP(k, a0, b0, a1, b1)
-    MOE_STEP(k + 1, a1, b1, a0, b0)
+  MOE_STEP(0, a0, b0, a1, b1, kLoads, true, true)
+  for (int k = 1; k < KT - kStages; k += 2) {
+    MOE_STEP(k, a1, b1, a0, b0, kLoads, true, true)
+    MOE_STEP(k + 1, a0, b0, a1, b1, kLoads, true, true)
   }
+  MOE_STEP(KT - 3, a1, b1, a0, b0, kLoads, false, true)
+  MOE_STEP(KT - 2, a0, b0, a1, b1, 0, false, true)
+  MOE_STEP(KT - 1, a1, b1, a0, b0, 0, false, false)
 #undef MOE_STEP
-#undef MOE_WAIT_NEXT
 #undef MOE_MMA_STEP
 #undef MOE_READ_STEP
 
-  // epilogue: lane holds rows 4*(lane/16)+i of each row tile, token lane%16
-  if (UP) {
+  // epilogue: lane holds, of each 32 x 32 block, column (token) lane%32 and
+  // rows 8g + 4(lane/32) + r for g, r in 0..3 (element 4g + r)
+  if constexpr (UP) {
+    // a in operand-tile order at the item's tile index: row R = 128 tix + token,
+    // feature f sit in tile (R/16, f/32), lane slot R%16 + 16((f%32)/8),
+    // element f%8 (padding tokens are not written and never read back into
+    // a result column that is stored)
     bf16_t* act = reinterpret_cast<bf16_t*>(p.act);
+    const int IT = d.I / kKStep;
 #pragma unroll
-    for (int f = 0; f < 4; ++f) {
-      const int feat = (ft * 8 + wr * 4 + f) * kTile + 4 * (lane / kTile);
+    for (int bl = 0; bl < 2; ++bl)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pr = out_pair[j];
-        if (pr < 0) continue;
-        uint2 v;
-        v.x = pack_bf16x2(silu_mul(acc[f][j][0], acc[f + 4][j][0]), silu_mul(acc[f][j][1], acc[f + 4][j][1]));
-        v.y = pack_bf16x2(silu_mul(acc[f][j][2], acc[f + 4][j][2]), silu_mul(acc[f][j][3], acc[f + 4][j][3]));
-        *reinterpret_cast<uint2*>(act + static_cast<int64_t>(pr) * d.I + feat) = v;
+      for (int n = 0; n < 2; ++n) {
+        if (out_pair[n] < 0) continue;
+        const int rt = tix * kTokTiles + wt * 4 + n * 2 + (lane % 32) / 16;   // R / 16
+        const int ct = ft * 4 + wr * 2 + bl;                                    // f / 32
+        bf16_t* dst = act + (static_cast<int64_t>(rt) * IT + ct) * kFragElems + (lane % 16) * 8 + 4 * (lane / 32);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& gt = acc[bl][n];
+          const f32x16_t& up = acc[bl + 2][n];
+          uint2 v;
+          v.x = pack_bf16x2(silu_mul(gt[4 * g], up[4 * g]), silu_mul(gt[4 * g + 1], up[4 * g + 1]));
+          v.y = pack_bf16x2(silu_mul(gt[4 * g + 2], up[4 * g + 2]), silu_mul(gt[4 * g + 3], up[4 * g + 3]));
+          *reinterpret_cast<uint2*>(dst + g * 16 * 8) = v;
+        }
       }
-    }
   } else {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int feat = (ft * 16 + wr * 8 + i) * kTile + 4 * (lane / kTile);
+    for (int n = 0; n < 2; ++n) {
+      const int pr = out_pair[n];
+      if (pr < 0) continue;
+      const float gw = (OUT == 2 && !shared) ? p.gate_w[pr] : 1.0f;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int pr = out_pair[j];
-        if (pr < 0) continue;
-        *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(pr) * d.H + feat) =
-            make_float4(acc[i][j][0], acc[i][j][1], acc[i][j][2], acc[i][j][3]);
+      for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int feat = ft * 256 + wr * 128 + bl * 32 + 8 * g + 4 * (lane / 32);
+          const f32x16_t& c = acc[bl][n];
+          if constexpr (OUT == 2) {
+            uint2 v;
+            v.x = pack_bf16x2(gw * c[4 * g], gw * c[4 * g + 1]);
+            v.y = pack_bf16x2(gw * c[4 * g + 2], gw * c[4 * g + 3]);
+            *reinterpret_cast<uint2*>(p.yb + static_cast<int64_t>(pr) * d.H + feat) = v;
+          } else {
+            *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(pr) * d.H + feat) =
+                make_float4(c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
+          }
+        }
+    }
+  }
+}
+
+// Combine of a prefill block from bf16 gate-weighted expert rows: one
+// wavefront per token row, m = sum of the shared rows then the routed rows in
+// ascending expert order (fp32, fixed order), x' = round(x + m).  Every row
+// of a token is requested before the first is added.
+constexpr int kCombineRows = 4;   // token rows (wavefronts) per workgroup
+constexpr int kCombineChunks = 3; // 8-element chunks per lane: H <= 1536
+__global__ __launch_bounds__(kCombineRows * kWave) void k_combine_bf16(Dims d, CombineParams p) {
+  const int lane = threadIdx.x % kWave;
+  const int t = blockIdx.x * kCombineRows + threadIdx.x / kWave;
+  if (t >= p.T) return;
+  const int H = d.H, k = d.k, nch = H / 8;
+  // the token's routed slots by ascending expert
+  int ids[kMaxTopK], js[kMaxTopK];
+  for (int j = 0; j < k; ++j) {
+    ids[j] = p.idx[t * k + j];
+    js[j] = j;
+  }
+  for (int a = 1; a < k; ++a) {
+    const int ia = ids[a], ja = js[a];
+    int b = a - 1;
+    while (b >= 0 && ids[b] > ia) {
+      ids[b + 1] = ids[b];
+      js[b + 1] = js[b];
+      --b;
+    }
+    ids[b + 1] = ia;
+    js[b + 1] = ja;
+  }
+  const int nrows = d.S + k;
+  uint4 xv[kCombineChunks];
+  uint4 yv[kCombineChunks][kMaxTopK + 4];
+  const bf16_t* xr = reinterpret_cast<const bf16_t*>(p.x_in) + static_cast<int64_t>(t) * H;
+#pragma unroll
+  for (int c = 0; c < kCombineChunks; ++c) {
+    const int ch = lane + c * kWave;
+    if (ch < nch) xv[c] = *reinterpret_cast<const uint4*>(xr + 8 * ch);
+  }
+#pragma unroll
+  for (int r = 0; r < kMaxTopK + 4; ++r) {
+    if (r < nrows) {
+      const int64_t row = r < d.S ? static_cast<int64_t>(p.T) * k + static_cast<int64_t>(r) * p.T + t
+                                  : static_cast<int64_t>(t) * k + js[r - d.S];
+      const bf16_t* yr = p.yb + row * H;
+#pragma unroll
+      for (int c = 0; c < kCombineChunks; ++c) {
+        const int ch = lane + c * kWave;
+        if (ch < nch) yv[c][r] = *reinterpret_cast<const uint4*>(yr + 8 * ch);
       }
+    }
+  }
+  bf16_t* xo = reinterpret_cast<bf16_t*>(p.x_out) + static_cast<int64_t>(t) * H;
+  float* mo = p.m_out ? p.m_out + static_cast<int64_t>(t) * H : nullptr;
+#pragma unroll
+  for (int c = 0; c < kCombineChunks; ++c) {
+    const int ch = lane + c * kWave;
+    if (ch >= nch) continue;
+    float m[8];
+#pragma unroll
+    for (int e = 0; e < 8; ++e) m[e] = 0.0f;
+#pragma unroll
+    for (int r = 0; r < kMaxTopK + 4; ++r) {
+      if (r < nrows) {
+        const uint32_t w4[4] = {yv[c][r].x, yv[c][r].y, yv[c][r].z, yv[c][r].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          m[2 * e] = __fadd_rn(m[2 * e], __uint_as_float(w4[e] << 16));
+          m[2 * e + 1] = __fadd_rn(m[2 * e + 1], __uint_as_float(w4[e] & 0xffff0000u));
+        }
+      }
+    }
+    const uint32_t x4[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
+    uint32_t o4[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e)
+      o4[e] = pack_bf16x2(__fadd_rn(__uint_as_float(x4[e] << 16), m[2 * e]),
+                          __fadd_rn(__uint_as_float(x4[e] & 0xffff0000u), m[2 * e + 1]));
+    *reinterpret_cast<uint4*>(xo + 8 * ch) = make_uint4(o4[0], o4[1], o4[2], o4[3]);
+    if (mo) {
+      *reinterpret_cast<float4*>(mo + 8 * ch) = make_float4(m[0], m[1], m[2], m[3]);
+      *reinterpret_cast<float4*>(mo + 8 * ch + 4) = make_float4(m[4], m[5], m[6], m[7]);
     }
   }
 }
 
 }  // namespace
+
+int64_t gemm_act_rows(const Dims& d, int T) { return static_cast<int64_t>(gemm_max_tiles(d, T)) * kBT; }
 
 int gemm_max_tiles(const Dims& d, int T) {
   // routed: at most one partial tile per expert beyond the full ones
@@ -273,10 +411,21 @@ hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipSt
   const int64_t items = static_cast<int64_t>(gemm_max_tiles(d, p.T)) * n_ft;
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   const size_t smem = gemm_lds_bytes();
+  const dim3 g(static_cast<unsigned>(grid)), b(kGemmThreads);
   if (up)
-    hipLaunchKernelGGL(k_grouped_gemm<true>, dim3(static_cast<unsigned>(grid)), dim3(kGemmThreads), smem, s, d, p);
+    hipLaunchKernelGGL((k_grouped_gemm<true, 0>), g, b, smem, s, d, p);
+  else if (p.yb)
+    hipLaunchKernelGGL((k_grouped_gemm<false, 2>), g, b, smem, s, d, p);
   else
-    hipLaunchKernelGGL(k_grouped_gemm<false>, dim3(static_cast<unsigned>(grid)), dim3(kGemmThreads), smem, s, d, p);
+    hipLaunchKernelGGL((k_grouped_gemm<false, 1>), g, b, smem, s, d, p);
+  return hipGetLastError();
+}
+
+hipError_t launch_combine_bf16(const Dims& d, const CombineParams& p, hipStream_t s) {
+  if (p.T <= 0) return hipSuccess;
+  if (d.H % 8 != 0 || d.H / 8 > kCombineChunks * kWave || d.S + d.k > kMaxTopK + 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_combine_bf16, dim3((p.T + kCombineRows - 1) / kCombineRows), dim3(kCombineRows * kWave), 0,
+                     s, d, p);
   return hipGetLastError();
 }
 

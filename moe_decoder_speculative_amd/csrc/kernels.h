@@ -137,16 +137,30 @@ struct GemmParams {
   const int* perm;       // [T*k]
   const int4* tiles;
   const int* n_tiles;
-  void* act;             // [T*k + S*T][I] bf16
-  float* y;              // [T*k + S*T][H] float32
+  void* act;             // SwiGLU activations in operand-tile order, gemm_act_rows rows of I
+  float* y;              // [T*k + S*T][H] float32 (down, when yb is null)
+  bf16_t* yb;            // [T*k + S*T][H] bf16 gate-weighted rows (down), or null
+  const float* gate_w;   // [T][k] gate weights (down with yb)
   int T;
   int xhat_zero_row;     // an all-zero row of xhat (padding tokens read it)
-  int act_zero_row;      // an all-zero row of act
 };
 int gemm_max_tiles(const Dims& d, int T);
+int64_t gemm_act_rows(const Dims& d, int T);  // rows of the tiled activation buffer
 size_t gemm_lds_bytes();
 hipError_t launch_tile_list(const Dims& d, const GemmTileParams& p, hipStream_t s);
 hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipStream_t s);
+
+// Combine of a block whose expert rows are bf16 and already gate-weighted:
+// m = shared rows + routed rows by ascending expert (fp32), x_out = round(x_in + m).
+struct CombineParams {
+  const void* x_in;      // [T][H] bf16
+  void* x_out;           // [T][H] bf16
+  const bf16_t* yb;      // [T*k + S*T][H] bf16
+  const int* idx;        // [T][k] the block's selection
+  float* m_out;          // [T][H] float32, optional
+  int T;
+};
+hipError_t launch_combine_bf16(const Dims& d, const CombineParams& p, hipStream_t s);
 
 // LM head + greedy arg-max + prefix acceptance.
 constexpr int kKeySlots = 32;  // arg-max keys are spread over this many copies

@@ -240,6 +240,16 @@ def test_block_forward_grouped_gemm_small(T):
     _prefill_case_check(workloads.build_case(w), f"gemm small T{T}")
 
 
+def test_verify_step_on_the_grouped_gemm_path():
+    """A verify step of 520 rows (130 sequences x 4) over two blocks runs its
+    experts on the grouped GEMM with float32 expert rows, combined by the next
+    block's router launch and the final norm: end to end against the oracle."""
+    w = workloads.small_bf16(B=130, K=3, L=2, seed_id=77)
+    case = workloads.build_case(w)
+    model, _ = _run_case(case, "verify on gemm T520")
+    model.close()
+
+
 def test_prefill_8pages_full_shape():
     case = workloads.cached_case("prefill_8pages")
     _prefill_case_check(case, "prefill_8pages")
