@@ -36,6 +36,8 @@ constexpr int kWaves = kThreads / kWave;
 constexpr int kRows = 16;        // token rows a workgroup can hold (MFMA tile columns)
 constexpr int kRouterHelpers = 64;  // workgroups that only bring the router matrix into L2
 constexpr int kGroup = 2;        // expert rows loaded together in the combine
+constexpr int kSplitShared = 2;  // most shared experts on the split path
+constexpr int kSplitRouted = 6;  // most routed experts per token on the split path
 
 template <typename ST>
 struct alignas(8) Vec4 { ST v[4]; };
@@ -134,7 +136,17 @@ __device__ void counting_sort_block(const Dims& d, const SortParams& s, int P, i
 // fragments are requested at kernel start, their latency overlapping the row
 // loads; with a combine they are requested after phase 1 (to keep phase 1
 // within 128 registers).
-template <typename ST, int KQ, bool EARLY>  // KQ = H / 128: router k-steps per wavefront (bf16)
+// SPLIT (bf16, steps of 17..256 rows): one row per workgroup (so the row
+// reads spread over as many CUs as there are rows) and eight wavefronts per
+// row in phase 1, wavefront c of a row owning the row's
+// 4-element chunks c*64 + lane -- the chunks one wavefront holds in slot c
+// otherwise -- so that every row of the combine is requested at once (one
+// memory round trip, not one per pair of expert rows) and the router
+// fragments can be requested at kernel start.  The per-lane partial sums of
+// squares of the slots are added in slot order through LDS before the same
+// wavefront reduction, so the normalised rows are bit-identical to the
+// one-wavefront-per-row path (a sequence gives the same rows at any batch).
+template <typename ST, int KQ, bool EARLY, bool SPLIT>  // KQ = H / 128: router k-steps per wavefront (bf16)
 __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterParams p, int rows) {
   // dynamic LDS: [0, 16 KiB) router partials zp[4][16][64] (reused by the sort);
   // then bf16 xh operand tiles [H/32][64 lanes][8] or f32 xh rows [16][H]
@@ -193,6 +205,109 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   };
 
   // ------------------------------------------------------------ phase 1
+  if constexpr (SPLIT) {
+    static_assert(sizeof(ST) == 2, "the split phase 1 is for bfloat16 storage");
+    const int n1 = wave / 8, c1 = wave % 8;   // row, chunk slot
+    const int t1 = t0 + n1;
+    const int ch = lane + c1 * kWave;
+    const bool mine = n1 < rows && t1 < T && c1 < CPL && ch < nchunks;
+    float xv[4];
+    Vec4<ST> gv;
+    if (mine) {
+      load4<ST>(reinterpret_cast<const ST*>(p.x_in) + static_cast<int64_t>(t1) * H + 4 * ch, xv);
+      if (p.norm) gv = *reinterpret_cast<const Vec4<ST>*>(reinterpret_cast<const ST*>(p.gamma) + 4 * ch);
+    }
+    // the router fragments after the row loads (loads complete in order)
+    load_router();
+    if (mine && p.combine) {
+      // every row is requested at once, by slot (row r < S: shared expert r;
+      // r >= S: routed slot r - S, pair t*k + r - S), before the selection
+      // that orders them is known; the routed rows are then added by
+      // ascending expert (the rank of each slot's expert among the token's)
+      int ids[kSplitRouted];
+      float ws[kSplitRouted];
+#pragma unroll
+      for (int j = 0; j < kSplitRouted; ++j) {
+        ids[j] = j < k ? p.prev_idx[t1 * k + j] : 0x7fffffff;
+        ws[j] = j < k ? p.prev_w[t1 * k + j] : 0.0f;
+      }
+      const int P = T * k;
+      float4 vs[kSplitShared], vr[kSplitRouted];
+#pragma unroll
+      for (int r = 0; r < kSplitShared; ++r)
+        if (r < d.S) vs[r] = *reinterpret_cast<const float4*>(p.y + (static_cast<int64_t>(P) + r * T + t1) * H + 4 * ch);
+#pragma unroll
+      for (int j = 0; j < kSplitRouted; ++j)
+        if (j < k) vr[j] = *reinterpret_cast<const float4*>(p.y + (static_cast<int64_t>(t1) * k + j) * H + 4 * ch);
+      int rank[kSplitRouted];
+#pragma unroll
+      for (int j = 0; j < kSplitRouted; ++j) {
+        rank[j] = 0;
+#pragma unroll
+        for (int jj = 0; jj < kSplitRouted; ++jj)
+          if (jj < k) rank[j] += ids[jj] < ids[j] ? 1 : 0;
+      }
+      float m[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+      auto add = [&](float g, const float4& y) {
+        m[0] = __fadd_rn(m[0], __fmul_rn(g, y.x));
+        m[1] = __fadd_rn(m[1], __fmul_rn(g, y.y));
+        m[2] = __fadd_rn(m[2], __fmul_rn(g, y.z));
+        m[3] = __fadd_rn(m[3], __fmul_rn(g, y.w));
+      };
+#pragma unroll
+      for (int r = 0; r < kSplitShared; ++r)
+        if (r < d.S) add(1.0f, vs[r]);  // shared expert: weight 1 (1*y == y exactly)
+#pragma unroll
+      for (int q = 0; q < kSplitRouted; ++q) {
+        if (q < k) {
+          // the routed slot whose expert is the q-th smallest of the token's
+          float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+          float g = 0.0f;
+#pragma unroll
+          for (int j = 0; j < kSplitRouted; ++j)
+            if (j < k && rank[j] == q) {
+              y = vr[j];
+              g = ws[j];
+            }
+          add(g, y);
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) xv[i] = Storage<ST>::round(__fadd_rn(xv[i], m[i]));
+      store4<ST>(reinterpret_cast<ST*>(p.x_out) + static_cast<int64_t>(t1) * H + 4 * ch, xv);
+      if (p.m_out)
+        *reinterpret_cast<float4*>(p.m_out + static_cast<int64_t>(t1) * H + 4 * ch) = make_float4(m[0], m[1], m[2], m[3]);
+    }
+    if (p.norm) {
+      // per-lane partial of this slot, added to the others in slot order
+      float* sq = zp;  // [2][8][64], free until phase 2
+      float part = 0.0f;
+      if (mine)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) part = __fadd_rn(part, __fmul_rn(xv[i], xv[i]));
+      sq[(n1 * 8 + c1) * kWave + lane] = part;
+      __syncthreads();
+      if (n1 < rows && t1 < T && c1 < CPL) {
+        float ss = 0.0f;
+        for (int c = 0; c < CPL; ++c) ss = __fadd_rn(ss, sq[(n1 * 8 + c) * kWave + lane]);
+        ss = wave_sum(ss);
+        const float rms = sqrtf(ss / static_cast<float>(H) + d.eps);
+        if (ch < nchunks) {
+          float v[4];
+#pragma unroll
+          for (int i = 0; i < 4; ++i) v[i] = Storage<ST>::round(__fmul_rn(xv[i] / rms, Storage<ST>::load(gv.v, i)));
+          store4<ST>(reinterpret_cast<ST*>(p.xhat) + static_cast<int64_t>(t1) * H + 4 * ch, v);
+          if (p.route) {
+            const int h = 4 * ch;
+            bf16_t* tile = reinterpret_cast<bf16_t*>(xs);
+            const int kt = h / 32, ln = n1 + 16 * ((h % 32) / 8);
+            store4<bf16_t>(tile + (kt * kWave + ln) * 8 + (h % 8), v);
+          }
+        }
+      }
+      __syncthreads();  // sq is reused as the router partials
+    }
+  } else {
   float x[CPL][4];
   Vec4<ST> gg[CPL];  // the gain, loaded with the row, converted when used
   const ST* xin = reinterpret_cast<const ST*>(p.x_in) + static_cast<int64_t>(t) * H;
@@ -293,13 +408,17 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
       }
     }
     if (p.norm) {
+      // per-lane partial of each chunk slot, added in slot order (the split
+      // path adds the same partials in the same order)
       float ss = 0.0f;
 #pragma unroll
       for (int c = 0; c < CPL; ++c) {
         const int ch = lane + c * kWave;
+        float part = 0.0f;
         if (ch < nchunks)
 #pragma unroll
-          for (int i = 0; i < 4; ++i) ss = __fadd_rn(ss, __fmul_rn(x[c][i], x[c][i]));
+          for (int i = 0; i < 4; ++i) part = __fadd_rn(part, __fmul_rn(x[c][i], x[c][i]));
+        ss = __fadd_rn(ss, part);
       }
       ss = wave_sum(ss);
       const float rms = sqrtf(ss / static_cast<float>(H) + d.eps);
@@ -328,8 +447,9 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
       }
     }
   }
+  }  // SPLIT
   if (!p.route) return;
-  if constexpr (!EARLY) load_router();
+  if constexpr (!EARLY && !SPLIT) load_router();
   const int nrows = min(rows, T - t0);
   if constexpr (sizeof(ST) == 2) {
     // rows of this workgroup past T: zero operand lanes so MFMA reads defined values
@@ -425,15 +545,23 @@ hipError_t launch_kq(const Dims& d, const NormRouterParams& p, hipStream_t s) {
   // 16 rows per workgroup when one workgroup takes the whole step (fused sort)
   // or the step is prefill-sized; 4 otherwise, so that a verify step of a few
   // hundred rows spreads its combine reads over more CUs
-  const int rows = (p.T <= kRows || p.T > 256) ? kRows : 4;
+  // (split path: 2 rows per workgroup, eight wavefronts per row)
+  const bool split = sizeof(ST) == 2 && p.T > kRows && p.T <= 256 && !p.sort.fused && d.S <= kSplitShared && d.k <= kSplitRouted;
+  const int rows = split ? 1 : (p.T <= kRows || p.T > 256) ? kRows : 4;
   // the rows' workgroups, then the router-matrix helpers (bf16 routing only)
   const dim3 grid((p.T + rows - 1) / rows + (p.route && sizeof(ST) == 2 ? kRouterHelpers : 0));
   const size_t xs = p.route ? (sizeof(ST) == 2 ? static_cast<size_t>(d.H) * 32 : static_cast<size_t>(d.H) * kRows * 4) : 0;
   const size_t smem = 4 * kRows * 64 * sizeof(float) + xs;
+  if constexpr (sizeof(ST) == 2) {
+    if (split) {
+      hipLaunchKernelGGL((k_norm_router<ST, KQ, false, true>), grid, dim3(kThreads), smem, s, d, p, rows);
+      return hipGetLastError();
+    }
+  }
   if (!p.combine && p.route && sizeof(ST) == 2)
-    hipLaunchKernelGGL((k_norm_router<ST, KQ, true>), grid, dim3(kThreads), smem, s, d, p, rows);
+    hipLaunchKernelGGL((k_norm_router<ST, KQ, true, false>), grid, dim3(kThreads), smem, s, d, p, rows);
   else
-    hipLaunchKernelGGL((k_norm_router<ST, KQ, false>), grid, dim3(kThreads), smem, s, d, p, rows);
+    hipLaunchKernelGGL((k_norm_router<ST, KQ, false, false>), grid, dim3(kThreads), smem, s, d, p, rows);
   return hipGetLastError();
 }
 
