@@ -48,6 +48,10 @@ __device__ __forceinline__ bool slot_info(const Dims& d, const ExpertParams& p, 
   }
   if (slot >= d.S + d.E) return false;
   const int4 ds = p.desc[slot - d.S];
+  // all three fields are used before the validity test, so the descriptor
+  // arrives in one scalar load instead of the expert id first and the rest
+  // in a second, dependent one
+  asm volatile("" ::"s"(ds.x), "s"(ds.y), "s"(ds.z));
   if (ds.x < 0) return false;
   si.expert = ds.x;
   si.ntok = ds.y;
@@ -104,6 +108,13 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
   const int nt = (si.ntok + kTile - 1) / kTile;
 
   const int kt0 = wave * KW;
+  const bf16_t* xh = reinterpret_cast<const bf16_t*>(p.xhat);
+  bf16_t* act = reinterpret_cast<bf16_t*>(p.act);
+  // the first token tile's pairs are requested before the weights: loads
+  // complete in order, and the activation rows they address can then be
+  // requested while the weights are in flight instead of after them
+  const int n0 = c * kTile + lane % kTile, nc0 = min(n0, si.ntok - 1);
+  const int pr0 = slot_pair(d, p, si, nc0);
   const int64_t tile = (static_cast<int64_t>(si.expert) * RT + rt) * KT + kt0;
   const bf16_t* g = reinterpret_cast<const bf16_t*>(p.w_gate) + tile * kFragElems + lane * 8;
   const bf16_t* u = reinterpret_cast<const bf16_t*>(p.w_up) + tile * kFragElems + lane * 8;
@@ -113,19 +124,20 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
     ag[i] = load_frag(g + i * kFragElems);
     au[i] = load_frag(u + i * kFragElems);
   }
-  const bf16_t* xh = reinterpret_cast<const bf16_t*>(p.xhat);
-  bf16_t* act = reinterpret_cast<bf16_t*>(p.act);
 
-  // activation fragments of the token tile at tile0 (column lane % 16); rows
-  // past the slot's tokens repeat its last token and are never stored
-  auto load_tile = [&](int tile0, int& pair, bf16x8_t (&b)[KW]) {
-    const int n = tile0 + lane % kTile, nc = min(n, si.ntok - 1);
-    const int pr = slot_pair(d, p, si, nc);
+  // activation fragments of a token tile (column lane % 16) given the pair of
+  // its n-th token (nc = n clamped); rows past the slot's tokens repeat its
+  // last token and are never stored
+  auto load_rows = [&](int n, int nc, int pr, int& pair, bf16x8_t (&b)[KW]) {
     pair = n < si.ntok ? pr : -1;
     const int tok = si.shared >= 0 ? nc : pr / d.k;
     const bf16_t* xr = xh + static_cast<int64_t>(tok) * d.H + kt0 * kKStep + (lane / kTile) * 8;
 #pragma unroll
     for (int i = 0; i < KW; ++i) b[i] = load_frag(xr + i * kKStep);
+  };
+  auto load_tile = [&](int tile0, int& pair, bf16x8_t (&b)[KW]) {
+    const int n = tile0 + lane % kTile, nc = min(n, si.ntok - 1);
+    load_rows(n, nc, slot_pair(d, p, si, nc), pair, b);
   };
   auto do_tile = [&](int pair, const bf16x8_t (&b)[KW]) {
     f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
@@ -156,7 +168,7 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
 
   int pair;
   bf16x8_t b[KW];
-  load_tile(c * kTile, pair, b);
+  load_rows(n0, nc0, pr0, pair, b);
   if (c + split_ >= nt) {
     do_tile(pair, b);
     return;
@@ -224,6 +236,10 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
   const int nt = (si.ntok + kTile - 1) / kTile;
 
   const int kt0 = wave * KW;
+  const bf16_t* act = reinterpret_cast<const bf16_t*>(p.act);
+  // the first token tile's pairs before the weights (see the up kernel)
+  const int n0 = c * kTile + lane % kTile;
+  const int pr0 = slot_pair(d, p, si, min(n0, si.ntok - 1));
   bf16x8_t a[RPW][KW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
@@ -232,19 +248,21 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
 #pragma unroll
     for (int i = 0; i < KW; ++i) a[r][i] = load_frag(w + i * kFragElems);
   }
-  const bf16_t* act = reinterpret_cast<const bf16_t*>(p.act);
 
-  // activation fragments of the token tile at tile0 (column lane % 16); rows
-  // past the slot's tokens repeat its last pair and are never stored
-  auto load_tile = [&](int tile0, int& pair, bf16x8_t (&b)[KW]) {
-    const int n = tile0 + lane % kTile;
-    const int pr = slot_pair(d, p, si, min(n, si.ntok - 1));
+  // activation fragments of a token tile (column lane % 16) given the pair of
+  // its n-th token; rows past the slot's tokens repeat its last pair and are
+  // never stored
+  auto load_rows = [&](int n, int pr, int& pair, bf16x8_t (&b)[KW]) {
     pair = n < si.ntok ? pr : -1;
     // a linear layer's slots all read the token's own row
     const int arow = EPI == 0 ? pr : min(n, si.ntok - 1);
     const bf16_t* ar = act + static_cast<int64_t>(arow) * d.I + kt0 * kKStep + (lane / kTile) * 8;
 #pragma unroll
     for (int i = 0; i < KW; ++i) b[i] = load_frag(ar + i * kKStep);
+  };
+  auto load_tile = [&](int tile0, int& pair, bf16x8_t (&b)[KW]) {
+    const int n = tile0 + lane % kTile;
+    load_rows(n, slot_pair(d, p, si, min(n, si.ntok - 1)), pair, b);
   };
   auto do_tile = [&](int pair, const bf16x8_t (&b)[KW]) {
     f32x4_t c[RPW];
@@ -287,7 +305,7 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
 
   int pair;
   bf16x8_t b[KW];
-  load_tile(c * kTile, pair, b);
+  load_rows(n0, pr0, pair, b);
   if (c + split_ >= nt) {
     do_tile(pair, b);
     return;
