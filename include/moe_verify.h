@@ -215,9 +215,10 @@ int moe_verify_step(moe_verify_ctx* ctx, const void* hidden, const int32_t* draf
  * library's reading of the decoder on the page "Jina AI releases lightweight
  * OCR model with built-in speculative decoding", section "Lean architecture
  * with a compressed encoder" (12 layers, 32,768 positions).
- *   positions device, int32 [B]: 0 <= positions[b] <= max_positions - (K+1)
- *             (other values give unspecified results, never an access
- *             outside the cache)
+ *   positions device, int32 [B]: 0 <= positions[b] <= max_positions - (K+1);
+ *             a value outside that range is clamped to it (the step then
+ *             behaves exactly as at the clamped position, for the rotary
+ *             angles, the cache rows written and the rows attended alike)
  * Other arguments as moe_verify_step_ex; requires B <= max_seqs and
  * K+1 <= max_positions.  Asynchronous; allocates nothing.
  */

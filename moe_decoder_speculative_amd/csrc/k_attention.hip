@@ -45,7 +45,7 @@ __device__ __forceinline__ float exp_f(float x) { return __builtin_amdgcn_exp2f(
 __device__ __forceinline__ int used_groups(int len, int G) { return min(G, (len + 4 * kPosTile - 1) / (4 * kPosTile)); }
 
 __device__ __forceinline__ int clamped_pos(const AttnParams& p, int b, int K1) {
-  return min(max(p.positions[b], 0), p.P - K1);
+  return step_position(p.positions, b, p.P, K1);
 }
 
 template <int K1>
@@ -148,6 +148,11 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) wsm[wave][jq][pt * 16 + 4 * (lane / 16) + i] = sc[pt][i] * c;
     }
+    // the weights cross lanes of this wavefront through LDS: its stores are
+    // complete and visible before any lane reads them
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     // values: every lane rescales its accumulators by query j's factor (held
     // by lane j) and adds the tile's weighted value rows
 #pragma unroll
@@ -169,6 +174,10 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
         for (int e = 0; e < 8; ++e) acc[j][e] = fmaf(wq, vf[e], acc[j][e]);
       }
     }
+    // every lane has read this tile's weights before the next tile's stores
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
   // the four lane groups' partial sums of every dimension
 #pragma unroll

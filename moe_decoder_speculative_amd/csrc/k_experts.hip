@@ -196,7 +196,7 @@ __device__ __forceinline__ void linear_epilogue(const Dims& d, const ExpertParam
                                                 int n, int f, float v0, float v1) {
   if constexpr (EPI == 1) {
     const int b = n / e.K1, j = n % e.K1;
-    const int pos = e.positions[b] + j;
+    const int pos = step_position(e.positions, b, e.P, e.K1) + j;  // the attention's clamp
     const int h = f / kHeadDim, dd = f % kHeadDim;
     if (slot < 2) {  // rotate q and k by pos * inv_freq of the pair
       float sn, cs;
@@ -209,7 +209,7 @@ __device__ __forceinline__ void linear_epilogue(const Dims& d, const ExpertParam
     const uint32_t packed = pack_bf16x2(v0, v1);
     if (slot == 0) {
       *reinterpret_cast<uint32_t*>(e.q + static_cast<int64_t>(n) * d.H + f) = packed;
-    } else if (pos >= 0 && pos < e.P) {
+    } else {
       bf16_t* cache = slot == 1 ? e.kc : e.vc;
       *reinterpret_cast<uint32_t*>(cache + ((static_cast<int64_t>(b) * e.nh + h) * e.P + pos) * kHeadDim + dd) =
           packed;

@@ -104,6 +104,15 @@ struct EpiParams {
 hipError_t launch_linear_qkv(const Dims& d, const ExpertParams& p, const EpiParams& e, hipStream_t s);
 hipError_t launch_linear_resid(const Dims& d, const ExpertParams& p, const EpiParams& e, hipStream_t s);
 
+// First cache position of sequence b's verify step: positions[b] clamped into
+// [0, P - K1], so every row the step writes or reads stays inside the cache.
+// The q/k/v projection (rotary angle, cache rows written) and the attention
+// (rows attended) both take it from here, so a position outside the range
+// behaves exactly like the nearest one inside it.
+__device__ __forceinline__ int step_position(const int* positions, int b, int P, int K1) {
+  return min(max(positions[b], 0), P - K1);
+}
+
 // Decode attention of the verify step: K1 query rows per sequence against
 // positions 0..positions[b]+j of the cache (keys / values [seqs][nh][P][128]).
 struct AttnParams {

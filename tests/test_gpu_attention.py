@@ -146,6 +146,48 @@ def test_attention_two_steps_continue_the_cache():
         vm.close()
 
 
+@pytest.mark.parametrize("pos_in,pos_out", [(60, 200), (0, -9)])
+def test_attention_positions_outside_the_cache_are_clamped(pos_in, pos_out):
+    """Two sequences with identical rows, drafts and cache contents, one at a
+    position at the edge of the range (0 or P - K - 1) and one beyond it on
+    the same side: the second is clamped to the first in every kernel, so
+    both give the same picks, counts, committed tokens, residual rows and
+    cache rows, bit for bit; the first is also checked against the oracle."""
+    B, K, L, P = 2, 3, 2, 64
+    w, _ = _small_case(B, K, L, P, seed=733, edge=False)
+    positions = np.array([pos_in, pos_out], np.int32)
+    clamped = np.array([pos_in, pos_in], np.int32)
+    parity.say(f"[attn clamp] positions {positions.tolist()} (both at {pos_in}) K={K} L={L} P={P} entry=moe_verify_step_kv")
+    weights = synth.gen_weights(w)
+    K1 = K + 1
+    one = synth.to_storage(synth.HiddenNoise(w).draw(K1), w.dtype)
+    hidden = np.concatenate([one, one])
+    kv0, bits = _prefix(w, clamped, seqs=[0])
+    kv0 = [(np.concatenate([k, k]), np.concatenate([v, v])) for k, v in kv0]
+    d1 = _drafts(w.with_(B=1, T=K1), weights, one, clamped[:1], [(k[:1], v[:1]) for k, v in kv0])
+    drafts = np.concatenate([d1, d1])
+    vm = VerifyModel(w, weights, max_tokens=w.T, max_seqs=B)
+    try:
+        for (l, b), (k, v) in bits.items():
+            vm.kv_write(l, 0, k, v)
+            vm.kv_write(l, 1, k, v)
+        out = _gpu_step(vm, w, hidden, drafts, positions, B, K)
+        kv = _gpu_kv(vm, w, range(B))
+        for name in ("hidden_out", "tstar"):
+            assert np.array_equal(out[name][:K1], out[name][K1:]), name
+        for name in ("attn_out", "moe_out", "topk_idx", "topk_w"):
+            assert np.array_equal(out[name][:, :K1], out[name][:, K1:]), name
+        assert out["counts"][0] == out["counts"][1] and np.array_equal(out["committed"][0], out["committed"][1])
+        for l in range(L):
+            assert np.array_equal(kv[l][0][0], kv[l][0][1]) and np.array_equal(kv[l][1][0], kv[l][1][1]), l
+        msg = parity.check_attn_step_teacher_forced(_rows(out, [0], K1), [(k[:1], v[:1]) for k, v in kv], one, d1,
+                                                    clamped[:1], [(k[:1], v[:1]) for k, v in kv0], weights,
+                                                    workloads.shape_of(w), _ash(w))
+        parity.say(f"[attn clamp] ok: the clamped sequence equals the in-range one; {msg}")
+    finally:
+        vm.close()
+
+
 @pytest.mark.parametrize("name,sample", [("attn_b1", None), ("attn_b32_zipf", [0, 7, 19, 31])])
 def test_attention_full_size_one_layer(name, sample):
     w = synth.WORKLOADS[name]
