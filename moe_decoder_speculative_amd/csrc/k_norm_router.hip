@@ -1,6 +1,7 @@
 // Combine + RMSNorm + top-k softmax router (+ counting sort for small steps),
-// one 1024-thread workgroup (16 wavefronts) per 16 token rows (4 for steps of
-// 17..256 rows, to spread the combine reads over more CUs).
+// one 1024-thread workgroup (16 wavefronts) per 16 token rows; steps of
+// 17..256 rows take one row per workgroup (bfloat16, the split phase 1 below)
+// or four, to spread the combine reads over more CUs.
 //
 // Phase 1 (wavefront w owns row w): optionally finish the previous block
 //   (m = shared outputs + gate-weighted routed outputs in ascending expert
@@ -543,9 +544,9 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
 template <typename ST, int KQ>
 hipError_t launch_kq(const Dims& d, const NormRouterParams& p, hipStream_t s) {
   // 16 rows per workgroup when one workgroup takes the whole step (fused sort)
-  // or the step is prefill-sized; 4 otherwise, so that a verify step of a few
-  // hundred rows spreads its combine reads over more CUs
-  // (split path: 2 rows per workgroup, eight wavefronts per row)
+  // or the step is prefill-sized; otherwise one (split path, eight wavefronts
+  // per row) or four, so that a verify step of a few hundred rows spreads its
+  // combine reads over more CUs
   const bool split = sizeof(ST) == 2 && p.T > kRows && p.T <= 256 && !p.sort.fused && d.S <= kSplitShared && d.k <= kSplitRouted;
   const int rows = split ? 1 : (p.T <= kRows || p.T > 256) ? kRows : 4;
   // the rows' workgroups, then the router-matrix helpers (bf16 routing only)
