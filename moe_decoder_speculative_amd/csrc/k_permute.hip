@@ -2,10 +2,12 @@
 //
 // Used for large steps (prefill).  One 1024-thread workgroup per expert e
 // (grid = E).  Every workgroup first copies the expert id of every pair into
-// LDS as one byte (coalesced 16-byte reads), builds the full 64-bin histogram
-// with LDS atomics (it needs the counts of all experts below it for its
-// offset and its rank among the active experts), then gathers the pairs routed
-// to e in increasing pair order: each thread scans a contiguous run of pairs,
+// LDS as one byte (coalesced 16-byte reads, eight in flight per thread) and
+// adds them, from registers, to the full 64-bin histogram with LDS atomics
+// (it needs the counts of all experts below it for its offset and its rank
+// among the active experts), then gathers the pairs routed to e in
+// increasing pair order: each thread scans a contiguous run of pairs, four
+// ids per LDS word,
 // a block-wide exclusive scan of the per-thread match counts gives every
 // thread its output position, and the thread writes its matches in order.
 // Outputs cnt[e], off[e] (and off[E] = P), perm[off[e] ..] and the list of
@@ -33,23 +35,42 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(int E, PermuteParams p
   const int e = blockIdx.x;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int P = p.P;
-  auto id_of = [&](int i) -> int { return cache_in_lds ? ids[i] : p.idx[i]; };
 
   if (tid < kMaxExperts) hist[tid] = 0;
+  __syncthreads();
   if (cache_in_lds) {
+    // batches of 16-byte reads in flight at once; each 4 ids become one
+    // 32-bit LDS word and go straight into the histogram from registers
+    constexpr int kBatch = 8;
     const int P4 = P / 4;
     const int4* src = reinterpret_cast<const int4*>(p.idx);
-    for (int i = tid; i < P4; i += kPermThreads) {
-      const int4 v = src[i];
-      ids[4 * i] = static_cast<unsigned char>(v.x);
-      ids[4 * i + 1] = static_cast<unsigned char>(v.y);
-      ids[4 * i + 2] = static_cast<unsigned char>(v.z);
-      ids[4 * i + 3] = static_cast<unsigned char>(v.w);
+    uint32_t* ids32 = reinterpret_cast<uint32_t*>(ids);
+    for (int i0 = tid; i0 < P4; i0 += kBatch * kPermThreads) {
+      int4 v[kBatch];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) v[u] = src[min(i0 + u * kPermThreads, P4 - 1)];
+#pragma unroll
+      for (int u = 0; u < kBatch; ++u) {
+        if (i0 + u * kPermThreads < P4) {
+          ids32[i0 + u * kPermThreads] = (static_cast<uint32_t>(v[u].x) & 255u) |
+                                         ((static_cast<uint32_t>(v[u].y) & 255u) << 8) |
+                                         ((static_cast<uint32_t>(v[u].z) & 255u) << 16) |
+                                         (static_cast<uint32_t>(v[u].w) << 24);
+          atomicAdd(&hist[v[u].x], 1);
+          atomicAdd(&hist[v[u].y], 1);
+          atomicAdd(&hist[v[u].z], 1);
+          atomicAdd(&hist[v[u].w], 1);
+        }
+      }
     }
-    for (int i = 4 * P4 + tid; i < P; i += kPermThreads) ids[i] = static_cast<unsigned char>(p.idx[i]);
+    for (int i = 4 * P4 + tid; i < P; i += kPermThreads) {
+      const int e_i = p.idx[i];
+      ids[i] = static_cast<unsigned char>(e_i);
+      atomicAdd(&hist[e_i], 1);
+    }
+  } else {
+    for (int i = tid; i < P; i += kPermThreads) atomicAdd(&hist[p.idx[i]], 1);
   }
-  __syncthreads();
-  for (int i = tid; i < P; i += kPermThreads) atomicAdd(&hist[id_of(i)], 1);
   __syncthreads();
 
   if (wave == 0) {
@@ -86,12 +107,22 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(int E, PermuteParams p
   __syncthreads();
   if (cnt_e == 0) return;
 
-  // contiguous run of pairs per thread; a block-wide exclusive scan of the
-  // per-thread match counts gives each thread its output position
-  const int run = (P + kPermThreads - 1) / kPermThreads;
+  // contiguous run of pairs per thread (a multiple of 4, so a cached run is
+  // whole LDS words); a block-wide exclusive scan of the per-thread match
+  // counts gives each thread its output position
+  const int run = (P + 4 * kPermThreads - 1) / (4 * kPermThreads) * 4;
   const int lo = min(P, tid * run), hi = min(P, lo + run);
+  const uint32_t* ids32 = reinterpret_cast<const uint32_t*>(ids);
   int mine = 0;
-  for (int i = lo; i < hi; ++i) mine += (id_of(i) == e);
+  if (cache_in_lds) {
+    for (int i = lo; i < hi; i += 4) {
+      const uint32_t w4 = ids32[i / 4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) mine += (i + q < hi && static_cast<int>((w4 >> (8 * q)) & 255u) == e) ? 1 : 0;
+    }
+  } else {
+    for (int i = lo; i < hi; ++i) mine += (p.idx[i] == e);
+  }
   int incl = mine;
 #pragma unroll
   for (int o = 1; o < kWave; o <<= 1) {
@@ -102,8 +133,18 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(int E, PermuteParams p
   __syncthreads();
   int pos = base_e + incl - mine;
   for (int w = 0; w < wave; ++w) pos += wave_tot[w];
-  for (int i = lo; i < hi; ++i)
-    if (id_of(i) == e) p.perm[pos++] = i;
+  if (mine == 0) return;
+  if (cache_in_lds) {
+    for (int i = lo; i < hi; i += 4) {
+      const uint32_t w4 = ids32[i / 4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        if (i + q < hi && static_cast<int>((w4 >> (8 * q)) & 255u) == e) p.perm[pos++] = i + q;
+    }
+  } else {
+    for (int i = lo; i < hi; ++i)
+      if (p.idx[i] == e) p.perm[pos++] = i;
+  }
 }
 
 }  // namespace

@@ -3,24 +3,26 @@
 //
 // At prefill sizes (about 915 tokens per routed expert, every token for each
 // shared expert) the experts are bound by MFMA throughput, not HBM.  Work item
-// = (expert slot, tile of 256 weight rows, tile of 128 of the slot's tokens).
-// A 256-thread workgroup computes one item, one wavefront per SIMD, each
+// = (expert slot, tile of 256 weight rows, tile of 256 of the slot's tokens).
+// A 512-thread workgroup computes one item, two wavefronts per SIMD, each
 // wavefront a 128 x 64 (rows x tokens) block of 32x32x16 bf16 MFMAs (128
-// accumulators per lane); a workgroup needs 72 KiB of LDS, so two run on
-// every CU and one's prologue, epilogue and memory waits are covered by the
-// other's MFMAs.  The operands of each 32-wide step of the reduction -- 16
-// weight row tiles (already in 16x32 MFMA operand order in HBM) and 8 token
-// tiles -- go straight from global memory into a 3-stage LDS ring with
-// gfx950's direct-to-LDS 16-byte loads (two steps in flight); the 32x32x16
-// fragments are read out of the 16x32 tiles with a lane-dependent offset.
-// The loads, not the MFMAs, bound the loop (the vector-memory address unit
-// is busy most of the time): a 16x32 token tile gathered from 16 rows costs
-// it more than a contiguous 1 KiB tile, so the down GEMM reads activation
-// tiles that the up GEMM wrote in operand-tile order.
+// accumulators per lane); one workgroup per CU (128 KiB of LDS).  The operands
+// of each 32-wide step of the reduction -- 16 weight row tiles (already in
+// 16x32 MFMA operand order in HBM) and 16 token tiles -- go straight from
+// global memory into a 4-stage LDS ring with gfx950's direct-to-LDS 16-byte
+// loads (three steps in flight), placed between the MFMAs; the 32x32x16
+// fragments are read out of the 16x32 tiles with a lane-dependent offset,
+// double buffered by half step.  The vector-memory path bounds the loop: a
+// CU moves about 32 bytes of operands per cycle with 8 wavefronts issuing,
+// so the 256 x 256 item (32 KiB per step for 1,024 MFMA cycles per SIMD) is
+// the smallest that does not leave the MFMAs waiting on it, and a 16x32
+// token tile gathered from 16 rows costs it more than a contiguous 1 KiB
+// tile -- the down GEMM reads activation tiles that the up GEMM wrote in
+// operand-tile order.
 //   up:   rows are 8 gate + 8 up tiles of the same 128 features; token rows
 //         of xhat gathered through the permutation (padding lanes read an
 //         all-zero row); epilogue a = round(silu(g) * u) written in
-//         operand-tile order at row 128 * (item's token tile) + token
+//         operand-tile order at row 256 * (item's token tile) + token
 //   down: rows are 16 tiles of 16 hidden features; epilogue per pair either
 //         y (fp32; a verify step, whose next router must see the exact sum)
 //         or round(w * y) (bf16, the pair's gate weight applied; the prefill
@@ -39,15 +41,16 @@ namespace moe {
 
 namespace {
 
-constexpr int kBT = 128;          // tokens per item
+constexpr int kBT = 256;          // tokens per item
 constexpr int kRowTiles = 16;     // MFMA row tiles per item (256 rows)
 constexpr int kTokTiles = kBT / kTile;
-constexpr int kStages = 3;        // LDS ring depth (one 32-wide k-step per stage, 24 KiB each)
+constexpr int kStages = 4;        // LDS ring depth (one 32-wide k-step per stage, 32 KiB each)
 constexpr int kStageBytes = (kRowTiles + kTokTiles) * kFragElems * 2;
 constexpr int kXcds = 8;
-constexpr int kGemmThreads = 256;  // 4 wavefronts: one per SIMD; two workgroups per CU
-constexpr int kLoadsA = kRowTiles / 4;  // weight fragments a wavefront stages per step (4)
-constexpr int kLoadsB = kTokTiles / 4;  // token fragments a wavefront stages per step (2)
+constexpr int kGemmThreads = 512;  // 8 wavefronts: two per SIMD; one workgroup per CU
+constexpr int kGemmWaves = kGemmThreads / kWave;
+constexpr int kLoadsA = kRowTiles / kGemmWaves;  // weight fragments a wavefront stages per step
+constexpr int kLoadsB = kTokTiles / kGemmWaves;  // token fragments a wavefront stages per step
 constexpr int kLoads = kLoadsA + kLoadsB;
 
 // Tile table: one entry per (slot, token tile), shared slots first, then the
@@ -79,15 +82,15 @@ __global__ __launch_bounds__(64) void k_tile_list(Dims d, GemmTileParams p) {
 
 // OUT: 0 act (up), 1 fp32 y (down), 2 bf16 gate-weighted y (down)
 template <bool UP, int OUT>
-__global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(Dims d, GemmParams p) {
+__global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm(Dims d, GemmParams p) {
   // LDS ring of kStages stages; a stage holds one 32-wide k-step: 16 weight
-  // fragments then 8 token fragments, 1 KiB each, in MFMA operand order.
+  // fragments then 16 token fragments, 1 KiB each, in MFMA operand order.
   extern __shared__ __align__(16) unsigned char smem[];
 
   // the wavefront index is uniform: keeping it in a scalar register makes the
   // LDS destinations and weight pointers of the loads scalar
   const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  const int wr = wave / 2, wt = wave % 2;         // wavefront's row half / token half
+  const int wr = wave / (kGemmWaves / 2), wt = wave % (kGemmWaves / 2);  // wavefront's row half / token quarter
   const int n_ft = UP ? d.I / 128 : d.H / 256;     // feature tiles per slot
   const int n_items = *p.n_tiles * n_ft;
   const int chunk = (n_items + kXcds - 1) / kXcds;
@@ -114,8 +117,9 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(Dims d, GemmPa
   const bf16_t* src = reinterpret_cast<const bf16_t*>(UP ? p.xhat : p.act);
   const int rows_per_expert_tiles = UP ? d.I / kTile : d.H / kTile;
 
-  // this wavefront stages weight fragments 4w..4w+3 and token fragments
-  // 2w, 2w+1 of every stage; lane offsets (elements) from scalar bases
+  // this wavefront stages weight fragments kLoadsA*w .. +kLoadsA and token
+  // fragments kLoadsB*w .. +kLoadsB of every stage; lane offsets (elements)
+  // from scalar bases
   uint32_t woff = lane * 8, toff[kLoadsB];
   const bf16_t* wmat[kLoadsA];
 #pragma unroll
@@ -178,78 +182,84 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(Dims d, GemmPa
 #pragma unroll
     for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
 
-  // Fragment registers, double buffered (step k+1 is read from LDS while the
-  // 16 MFMAs of step k run); the loop is unrolled by two so the two register
-  // sets keep fixed roles.
+  // Fragment registers, double buffered by half step: x holds reduction half
+  // 0 of a step, y half 1.  While the 8 MFMAs of (k, 0) run, (k, 1) is read
+  // from the ring; while those of (k, 1) run, (k+1, 0) is.  48 registers
+  // instead of 96 for whole steps, which leaves the allocator room to keep
+  // the two sets apart (shared registers would order each read after the
+  // MFMA that last used them).
   //
   // The barriers are bare: a fenced barrier would wait for every load in
   // flight, later steps included, and drain the ring.  LDS-DMA writes are
   // complete once vmcnt says so; each wavefront waits for its own loads of a
   // step before the barrier, so after it every wavefront's share has landed.
-  // Each wavefront also waits for its own LDS reads of the stage the loads
-  // issued after the barrier overwrite (read one step earlier) before it
-  // arrives, so no read of a stage can be overtaken by its refill.
-  bf16x8_t a0[2][4], b0[2][2], a1[2][4], b1[2][2];
-#define MOE_READ_STEP(K, A, B)                                                                     \
+  // Each wavefront also waits for its own reads of step k (both halves)
+  // before it arrives, so the refill of step k's stage, issued after the
+  // barrier, cannot overtake a read of it.
+  bf16x8_t xa[4], xb[2], ya[4], yb[2];
+#define MOE_READ_HALF(K, KK, FA, FB)                                                               \
   {                                                                                                \
-    const unsigned char* st_ = smem + ((K) % kStages) * kStageBytes + lane_off;                    \
-    _Pragma("unroll") for (int kk = 0; kk < 2; ++kk) {                                             \
-      _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                \
-        B[kk][j] = *reinterpret_cast<const bf16x8_t*>(st_ + (kRowTiles + wt * 4 + 2 * j) * 1024 + kk * 512); \
-      _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                \
-        A[kk][i] = *reinterpret_cast<const bf16x8_t*>(st_ + (wr * 8 + 2 * i) * 1024 + kk * 512);   \
-    }                                                                                              \
+    const unsigned char* st_ = smem + ((K) % kStages) * kStageBytes + lane_off + (KK) * 512;       \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
+      FB[j] = *reinterpret_cast<const bf16x8_t*>(st_ + (kRowTiles + wt * 4 + 2 * j) * 1024);       \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
+      FA[i] = *reinterpret_cast<const bf16x8_t*>(st_ + (wr * 8 + 2 * i) * 1024);                   \
   }
-#define MOE_MMA_STEP(A, B)                                                                         \
-  _Pragma("unroll") for (int kk = 0; kk < 2; ++kk)                                                 \
+#define MOE_MMA_HALF(FA, FB)                                                                       \
   _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
-  _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(A[kk][i], B[kk][j], acc[i][j]);
-// One step K (its fragments in CA/CB): make step K+1 available -- wait until
-// at most VM of this wavefront's loads (the steps issued after K+1) are in
-// flight, wait for its own reads of step K, bare barrier, refill step K's
-// stage with step K+3 when ISSUE -- then run step K's 16 MFMAs with step
-// K+1's 12 fragment reads interleaved.
-#define MOE_STEP(K, CA, CB, NA, NB, VM, ISSUE, NEXT)                                               \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(FA[i], FB[j], acc[i][j]);
+// 8 MFMAs with the 6 fragment reads of the other half (and the ring loads)
+// between them
+#define MOE_INTERLEAVE(LOADS)                                                                      \
+  _Pragma("unroll") for (int g_ = 0; g_ < 6; ++g_) {                                               \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* 1 MFMA */                                \
+    if (g_ < (LOADS)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0); /* 1 ring load */        \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* 1 LDS read */                            \
+  }                                                                                                \
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+// One step K: read (K, 1) during the MFMAs of (K, 0); then make step K+1
+// available -- wait until at most VM of this wavefront's loads (the steps
+// issued after K+1) are in flight and its reads of step K are done, bare
+// barrier, refill step K's stage with step K+4 when ISSUE -- and read
+// (K+1, 0) during the MFMAs of (K, 1).
+#define MOE_STEP(K, VM, ISSUE, NEXT)                                                               \
   {                                                                                                \
+    MOE_READ_HALF(K, 1, ya, yb)                                                                    \
+    MOE_MMA_HALF(xa, xb)                                                                           \
+    MOE_INTERLEAVE(0)                                                                              \
     if (NEXT) {                                                                                    \
       __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));                                                  \
-      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0); /* this wavefront's reads of step K done */       \
-      __builtin_amdgcn_s_barrier(); /* step K+1 landed; everyone has read step K */                \
-      if (ISSUE) issue((K) + kStages); /* into step K's buffer */                                  \
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);                                                   \
+      __builtin_amdgcn_s_barrier();                                                                \
+      if (ISSUE) issue((K) + kStages);                                                             \
+      MOE_READ_HALF((K) + 1, 0, xa, xb)                                                            \
     }                                                                                              \
-    MOE_MMA_STEP(CA, CB)                                                                           \
-    if (NEXT) {                                                                                    \
-      MOE_READ_STEP((K) + 1, NA, NB)                                                               \
-      _Pragma("unroll") for (int g_ = 0; g_ < 4; ++g_) {                                           \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0); /* 1 MFMA */                            \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0); /* 1 LDS read */                        \
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                         \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
-        __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);                                         \
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                         \
-      }                                                                                            \
-    }                                                                                              \
+    MOE_MMA_HALF(ya, yb)                                                                           \
+    if (NEXT) { MOE_INTERLEAVE((ISSUE) ? kLoads : 0) }                                             \
   }
 
-  // KT is even and >= 8 (H and I are multiples of 128).  Steps 0..KT-4 refill
-  // the ring (issue step k+3) and wait until one later step may stay in
-  // flight; steps KT-3..KT-1 drain it.  Step k uses register set k % 2.
+  // KT is a multiple of 4 (H and I are multiples of 128).  Steps 0..KT-5
+  // refill the ring (issue step k+4) and wait until two later steps may stay
+  // in flight; steps KT-4..KT-1 drain it.
+  static_assert(kLoads <= 6, "ring loads are placed between the MFMAs of a half step");
 #pragma unroll
   for (int s = 0; s < kStages; ++s) issue(s);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kLoads));  // step 0 landed, 1 and 2 may be in flight
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kLoads));  // step 0 landed, 1..3 may be in flight
   __builtin_amdgcn_s_barrier();
-  MOE_READ_STEP(0, a0, b0)
-  MOE_STEP(0, a0, b0, a1, b1, kLoads, true, true)
-  for (int k = 1; k < KT - kStages; k += 2) {
-    MOE_STEP(k, a1, b1, a0, b0, kLoads, true, true)
-    MOE_STEP(k + 1, a0, b0, a1, b1, kLoads, true, true)
+  MOE_READ_HALF(0, 0, xa, xb)
+  if (KT >= 8) {
+    for (int k = 0; k < KT - kStages; ++k) MOE_STEP(k, 2 * kLoads, true, true)
+    MOE_STEP(KT - 4, 2 * kLoads, false, true)
+  } else {  // KT == 4: every step is in the ring already
+    MOE_STEP(0, 2 * kLoads, false, true)
   }
-  MOE_STEP(KT - 3, a1, b1, a0, b0, kLoads, false, true)
-  MOE_STEP(KT - 2, a0, b0, a1, b1, 0, false, true)
-  MOE_STEP(KT - 1, a1, b1, a0, b0, 0, false, false)
+  MOE_STEP(KT - 3, kLoads, false, true)
+  MOE_STEP(KT - 2, 0, false, true)
+  MOE_STEP(KT - 1, 0, false, false)
 #undef MOE_STEP
-#undef MOE_MMA_STEP
-#undef MOE_READ_STEP
+#undef MOE_INTERLEAVE
+#undef MOE_MMA_HALF
+#undef MOE_READ_HALF
 
   // epilogue: lane holds, of each 32 x 32 block, column (token) lane%32 and
   // rows 8g + 4(lane/32) + r for g, r in 0..3 (element 4g + r)
@@ -306,35 +316,35 @@ __global__ __launch_bounds__(kGemmThreads, 2) void k_grouped_gemm(Dims d, GemmPa
 
 // Combine of a prefill block from bf16 gate-weighted expert rows: one
 // wavefront per token row, m = sum of the shared rows then the routed rows in
-// ascending expert order (fp32, fixed order), x' = round(x + m).  Every row
-// of a token is requested before the first is added.
+// ascending expert order (fp32, fixed order), x' = round(x + m).  A token's
+// routed rows are rows t*k .. t*k+k-1 whatever their experts, so every row is
+// requested at once together with the selection (one memory round trip); the
+// selection, uniform over the wavefront, then only decides the order of the
+// adds, by uniform branches over register-resident rows.
 constexpr int kCombineRows = 4;   // token rows (wavefronts) per workgroup
 constexpr int kCombineChunks = 3; // 8-element chunks per lane: H <= 1536
+constexpr int kCombineShared = 4; // most shared experts
+
+__device__ __forceinline__ void add_bf16x8(float (&m)[8], const uint4& v) {
+  const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    m[2 * e] = __fadd_rn(m[2 * e], __uint_as_float(w4[e] << 16));
+    m[2 * e + 1] = __fadd_rn(m[2 * e + 1], __uint_as_float(w4[e] & 0xffff0000u));
+  }
+}
+
 __global__ __launch_bounds__(kCombineRows * kWave) void k_combine_bf16(Dims d, CombineParams p) {
   const int lane = threadIdx.x % kWave;
   const int t = blockIdx.x * kCombineRows + threadIdx.x / kWave;
   if (t >= p.T) return;
-  const int H = d.H, k = d.k, nch = H / 8;
-  // the token's routed slots by ascending expert
-  int ids[kMaxTopK], js[kMaxTopK];
-  for (int j = 0; j < k; ++j) {
-    ids[j] = p.idx[t * k + j];
-    js[j] = j;
-  }
-  for (int a = 1; a < k; ++a) {
-    const int ia = ids[a], ja = js[a];
-    int b = a - 1;
-    while (b >= 0 && ids[b] > ia) {
-      ids[b + 1] = ids[b];
-      js[b + 1] = js[b];
-      --b;
-    }
-    ids[b + 1] = ia;
-    js[b + 1] = ja;
-  }
-  const int nrows = d.S + k;
+  const int H = d.H, k = d.k, S = d.S, nch = H / 8;
+  // lane j < k holds the expert of routed slot j (requested first: loads
+  // complete in order, and it is the first value needed)
+  const int my_e = p.idx[static_cast<int64_t>(t) * k + min(lane, k - 1)];
   uint4 xv[kCombineChunks];
-  uint4 yv[kCombineChunks][kMaxTopK + 4];
+  uint4 ys[kCombineChunks][kCombineShared];
+  uint4 yr[kCombineChunks][kMaxTopK];
   const bf16_t* xr = reinterpret_cast<const bf16_t*>(p.x_in) + static_cast<int64_t>(t) * H;
 #pragma unroll
   for (int c = 0; c < kCombineChunks; ++c) {
@@ -342,18 +352,38 @@ __global__ __launch_bounds__(kCombineRows * kWave) void k_combine_bf16(Dims d, C
     if (ch < nch) xv[c] = *reinterpret_cast<const uint4*>(xr + 8 * ch);
   }
 #pragma unroll
-  for (int r = 0; r < kMaxTopK + 4; ++r) {
-    if (r < nrows) {
-      const int64_t row = r < d.S ? static_cast<int64_t>(p.T) * k + static_cast<int64_t>(r) * p.T + t
-                                  : static_cast<int64_t>(t) * k + js[r - d.S];
-      const bf16_t* yr = p.yb + row * H;
+  for (int r = 0; r < kCombineShared; ++r) {
+    if (r < S) {
+      const bf16_t* yrow = p.yb + (static_cast<int64_t>(p.T) * k + static_cast<int64_t>(r) * p.T + t) * H;
 #pragma unroll
       for (int c = 0; c < kCombineChunks; ++c) {
         const int ch = lane + c * kWave;
-        if (ch < nch) yv[c][r] = *reinterpret_cast<const uint4*>(yr + 8 * ch);
+        if (ch < nch) ys[c][r] = *reinterpret_cast<const uint4*>(yrow + 8 * ch);
       }
     }
   }
+#pragma unroll
+  for (int j = 0; j < kMaxTopK; ++j) {
+    if (j < k) {
+      const bf16_t* yrow = p.yb + (static_cast<int64_t>(t) * k + j) * H;
+#pragma unroll
+      for (int c = 0; c < kCombineChunks; ++c) {
+        const int ch = lane + c * kWave;
+        if (ch < nch) yr[c][j] = *reinterpret_cast<const uint4*>(yrow + 8 * ch);
+      }
+    }
+  }
+  // order[q]: the routed slot holding the q-th smallest expert of the token
+  // (the experts of a token are distinct)
+  int rank = 0;
+  for (int jj = 0; jj < k; ++jj) rank += __shfl(my_e, jj, kWave) < my_e ? 1 : 0;
+  int order[kMaxTopK];
+#pragma unroll
+  for (int q = 0; q < kMaxTopK; ++q) {
+    const unsigned long long m = __ballot(lane < k && rank == q);
+    order[q] = __builtin_amdgcn_readfirstlane(m ? static_cast<int>(__builtin_ctzll(m)) : 0);
+  }
+
   bf16_t* xo = reinterpret_cast<bf16_t*>(p.x_out) + static_cast<int64_t>(t) * H;
   float* mo = p.m_out ? p.m_out + static_cast<int64_t>(t) * H : nullptr;
 #pragma unroll
@@ -364,15 +394,15 @@ __global__ __launch_bounds__(kCombineRows * kWave) void k_combine_bf16(Dims d, C
 #pragma unroll
     for (int e = 0; e < 8; ++e) m[e] = 0.0f;
 #pragma unroll
-    for (int r = 0; r < kMaxTopK + 4; ++r) {
-      if (r < nrows) {
-        const uint32_t w4[4] = {yv[c][r].x, yv[c][r].y, yv[c][r].z, yv[c][r].w};
+    for (int r = 0; r < kCombineShared; ++r)
+      if (r < S) add_bf16x8(m, ys[c][r]);
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          m[2 * e] = __fadd_rn(m[2 * e], __uint_as_float(w4[e] << 16));
-          m[2 * e + 1] = __fadd_rn(m[2 * e + 1], __uint_as_float(w4[e] & 0xffff0000u));
-        }
-      }
+    for (int q = 0; q < kMaxTopK; ++q) {
+      if (q >= k) break;
+      const int j = order[q];
+#pragma unroll
+      for (int jj = 0; jj < kMaxTopK; ++jj)
+        if (jj == j) add_bf16x8(m, yr[c][jj]);
     }
     const uint32_t x4[4] = {xv[c].x, xv[c].y, xv[c].z, xv[c].w};
     uint32_t o4[4];
@@ -405,7 +435,7 @@ hipError_t launch_tile_list(const Dims& d, const GemmTileParams& p, hipStream_t 
 }
 
 hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipStream_t s) {
-  // the step loop runs in pairs (H and I are multiples of 128)
+  // the step schedule needs a multiple of 4 steps (H and I multiples of 128)
   if (d.I % 128 != 0 || d.H % 256 != 0) return hipErrorInvalidValue;
   const int n_ft = up ? d.I / 128 : d.H / 256;
   const int64_t items = static_cast<int64_t>(gemm_max_tiles(d, p.T)) * n_ft;
@@ -423,7 +453,8 @@ hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipSt
 
 hipError_t launch_combine_bf16(const Dims& d, const CombineParams& p, hipStream_t s) {
   if (p.T <= 0) return hipSuccess;
-  if (d.H % 8 != 0 || d.H / 8 > kCombineChunks * kWave || d.S + d.k > kMaxTopK + 4) return hipErrorInvalidValue;
+  if (d.H % 8 != 0 || d.H / 8 > kCombineChunks * kWave || d.S > kCombineShared || d.k > kMaxTopK || d.k < 1)
+    return hipErrorInvalidValue;
   hipLaunchKernelGGL(k_combine_bf16, dim3((p.T + kCombineRows - 1) / kCombineRows), dim3(kCombineRows * kWave), 0,
                      s, d, p);
   return hipGetLastError();
