@@ -230,7 +230,19 @@ def test_sparse_dispatch_equals_dense_all_experts_times_mask(dtype, E, k, S):
     x = rng.standard_normal((T, H)).astype(np.float32)
     r = O.moe_block(x, lw, shp)
     xd, md = O.moe_block_dense(x, lw, shp)
-    np.testing.assert_allclose(r.m, md, rtol=2e-6, atol=2e-7)
+    if dtype == "f32":
+        np.testing.assert_allclose(r.m, md, rtol=2e-6, atol=2e-7)
+    else:
+        # The dense path runs each expert's products over all T rows, the
+        # sparse one over the expert's own rows: BLAS blocks the two sums
+        # differently, so an activation within an ulp of a bf16 rounding
+        # boundary (the SwiGLU rounding point) can round the other way on one
+        # side.  One such flip moves m by 2^-8 |a| |W_d| w (~1e-6 here); a
+        # dropped expert or a wrong gate moves a row by a large fraction.
+        off = np.abs(r.m - md) > 2e-7 + 2e-6 * np.abs(md)
+        assert off.mean() < 1e-2
+        row_rel = np.abs(r.m - md).max(axis=1) / np.abs(md).max(axis=1)
+        assert row_rel.max() < 1e-3
     if dtype == "bf16":
         # R3 may land on the other side of a bf16 tie only if m moved by an ulp
         assert np.mean(r.x_out != xd) < 1e-3
