@@ -499,6 +499,13 @@ int run_blocks(moe_verify_ctx* c, const moe::api::Workspace& W, const void* hidd
       nr.sort = moe::SortParams{idx, pp.cnt, pp.off, pp.perm, pp.active, pp.n_active, pp.desc, 1};
     }
     MOE_HIP(moe::launch_norm_router(d, nr, s));
+    if (use_gemm(c, T)) {
+      // the permutation kernel also builds the grouped GEMM's tile table
+      pp.tiles = W.tiles;
+      pp.n_tiles = W.n_tiles;
+      pp.tile_T = T;
+      pp.n_shared = static_cast<int>(g.n_shared);
+    }
     if (!fused_sort) MOE_HIP(moe::launch_permute(d, pp, s));
 
     moe::ExpertParams ep{};
@@ -517,8 +524,6 @@ int run_blocks(moe_verify_ctx* c, const moe::api::Workspace& W, const void* hidd
     ep.T = T;
     if (use_gemm(c, T)) {
       // prefill-sized: grouped GEMM over (slot, feature tile, token tile) items
-      moe::GemmTileParams tp{pp.cnt, pp.off, T, W.tiles, W.n_tiles};
-      MOE_HIP(moe::launch_tile_list(d, tp, s));
       moe::GemmParams gp{};
       gp.xhat = W.xhat;
       gp.w_gate = ep.w_gate;

@@ -541,8 +541,169 @@ __global__ __launch_bounds__(kThreads) void k_norm_router(Dims d, NormRouterPara
   counting_sort_block(d, p.sort, T * k, reinterpret_cast<int*>(smem), sel);
 }
 
+// Prefill-sized steps (bf16, more than 256 rows, no combine): RMSNorm and
+// top-k routing of 16 rows per 256-thread workgroup, several workgroups per
+// CU (the 1024-thread kernel above fits one per CU, so its rows' memory
+// round trips and reductions ran back to back).  Wavefront w normalises rows
+// w, w + 4, w + 8, w + 12 (all four rows' loads issued first) and then
+// computes the logits of expert tile w over the whole reduction, quarter by
+// quarter with the next quarter's router fragments in flight; the quarters
+// are added in the same fixed order as above, so the logits, selections and
+// gate weights are bit-identical to the 1024-thread kernel's.  Logits meet
+// through LDS, and each wavefront ranks its four rows' experts as above.
+constexpr int kPfThreads = 256;
+constexpr int kPfWaves = kPfThreads / kWave;
+constexpr int kPfRowsPerWave = kRows / kPfWaves;
+
+template <int KQ>  // H / 128: k-steps per reduction quarter
+__global__ __launch_bounds__(kPfThreads) void k_router_rows(Dims d, NormRouterParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  float* zs = reinterpret_cast<float*>(smem);                     // [16 rows][64 experts]
+  bf16_t* tile = reinterpret_cast<bf16_t*>(smem + kRows * 64 * sizeof(float));  // [H/32][64 lanes][8]
+  const int H = d.H, k = d.k, T = p.T;
+  const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int t0 = blockIdx.x * kRows;
+  const int nchunks = H / 4;
+  constexpr int CPL = (KQ + 1) / 2;  // 4-element chunks per lane: ceil(H / 256)
+
+  // this wavefront's rows and the gain, then its expert tile's first quarter
+  // of router fragments (loads complete in order: the rows arrive first)
+  Vec4<bf16_t> xv[kPfRowsPerWave][CPL], gv[CPL];
+#pragma unroll
+  for (int q = 0; q < kPfRowsPerWave; ++q) {
+    const int t = min(t0 + wave + q * kPfWaves, T - 1);
+    const bf16_t* xin = reinterpret_cast<const bf16_t*>(p.x_in) + static_cast<int64_t>(t) * H;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = min(lane + c * kWave, nchunks - 1);
+      xv[q][c] = *reinterpret_cast<const Vec4<bf16_t>*>(xin + 4 * ch);
+    }
+  }
+#pragma unroll
+  for (int c = 0; c < CPL; ++c) {
+    const int ch = min(lane + c * kWave, nchunks - 1);
+    gv[c] = *reinterpret_cast<const Vec4<bf16_t>*>(reinterpret_cast<const bf16_t*>(p.gamma) + 4 * ch);
+  }
+  const int et = wave;  // expert tile of this wavefront (E <= 64)
+  const bool has_tile = et * 16 < d.E;
+  const bf16_t* wr = reinterpret_cast<const bf16_t*>(p.router) + static_cast<int64_t>(et) * (H / kKStep) * kFragElems +
+                     lane * 8;
+  bf16x8_t ra[2][KQ];
+#pragma unroll
+  for (int i = 0; i < KQ; ++i) ra[0][i] = load_frag(wr + i * kFragElems);
+
+  // ------------------------------------------------------------ phase 1
+#pragma unroll
+  for (int q = 0; q < kPfRowsPerWave; ++q) {
+    const int n = wave + q * kPfWaves, t = t0 + n;
+    float x[CPL][4];
+    float ss = 0.0f;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + c * kWave;
+      float part = 0.0f;
+      if (ch < nchunks) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          x[c][i] = bf16_to_f32(xv[q][c].v[i]);
+          part = __fadd_rn(part, __fmul_rn(x[c][i], x[c][i]));
+        }
+      }
+      ss = __fadd_rn(ss, part);
+    }
+    ss = wave_sum(ss);
+    const float rms = sqrtf(ss / static_cast<float>(H) + d.eps);
+    bf16_t* xh = reinterpret_cast<bf16_t*>(p.xhat) + static_cast<int64_t>(t) * H;
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = lane + c * kWave;
+      if (ch < nchunks) {
+        float v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = Storage<bf16_t>::round(__fmul_rn(x[c][i] / rms, bf16_to_f32(gv[c].v[i])));
+        if (t < T) store4<bf16_t>(xh + 4 * ch, v);
+        // operand tile kt = h/32; lane n + 16*((h%32)/8); element h%8 (rows
+        // past T are zero: their logits are never used)
+        const int h = 4 * ch, kt = h / 32, ln = n + 16 * ((h % 32) / 8);
+        if (t >= T) v[0] = v[1] = v[2] = v[3] = 0.0f;
+        store4<bf16_t>(tile + (kt * kWave + ln) * 8 + (h % 8), v);
+      }
+    }
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------ phase 2
+  // quarter kq of the reduction on ring slot kq & 1, the next quarter's
+  // fragments requested before this quarter's MFMAs; the quarter sums are
+  // added in quarter order as the 1024-thread kernel adds its four waves'
+  f32x4_t z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int kq = 0; kq < 4; ++kq) {
+    if (kq + 1 < 4) {
+#pragma unroll
+      for (int i = 0; i < KQ; ++i) ra[(kq + 1) & 1][i] = load_frag(wr + ((kq + 1) * KQ + i) * kFragElems);
+    }
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < KQ; ++i) acc = mfma16(ra[kq & 1][i], load_frag(tile + ((kq * KQ + i) * kWave + lane) * 8), acc);
+    if (kq == 0) {
+      z = acc;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) z[i] = __fadd_rn(z[i], acc[i]);
+    }
+  }
+  // lane holds z[expert 16*et + 4*(lane/16) + i][row lane%16]
+  if (has_tile) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zs[(lane % 16) * 64 + et * 16 + 4 * (lane / 16) + i] = z[i];
+  }
+  __syncthreads();
+
+  // ------------------------------------------------------------ phase 3
+#pragma unroll 1
+  for (int q = 0; q < kPfRowsPerWave; ++q) {
+    const int n = wave + q * kPfWaves, t = t0 + n;
+    if (t >= T) break;
+    const float zl = lane < d.E ? zs[n * 64 + lane] : 0.0f;
+    // rank of each expert (lane) by (logit desc, expert asc), as above
+    const uint64_t key = lane < d.E ? argmax_key(zl, static_cast<uint32_t>(lane)) : 0ull;
+    const uint32_t klo = static_cast<uint32_t>(key), khi = static_cast<uint32_t>(key >> 32);
+    int rank = 0;
+#pragma unroll
+    for (int e = 0; e < kMaxExperts; ++e) {
+      const uint64_t ke = (static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(khi, e))) << 32) |
+                          static_cast<uint64_t>(static_cast<uint32_t>(__builtin_amdgcn_readlane(klo, e)));
+      rank += ke > key ? 1 : 0;
+    }
+    const bool chosen = lane < d.E && rank < k;
+    const unsigned long long first = __ballot(chosen && rank == 0);
+    const float z0 = __shfl(zl, __ffsll(static_cast<long long>(first)) - 1, kWave);
+    const float ex = chosen ? expf(zl - z0) : 0.0f;
+    float den = 0.0f;
+#pragma unroll
+    for (int j = 0; j < kMaxTopK; ++j) {
+      if (j < k) {
+        const unsigned long long m = __ballot(chosen && rank == j);
+        den = __fadd_rn(den, __shfl(ex, __ffsll(static_cast<long long>(m)) - 1, kWave));
+      }
+    }
+    if (chosen) {
+      p.idx_out[t * k + rank] = lane;
+      p.w_out[t * k + rank] = ex / den;
+    }
+  }
+}
+
 template <typename ST, int KQ>
 hipError_t launch_kq(const Dims& d, const NormRouterParams& p, hipStream_t s) {
+  if constexpr (sizeof(ST) == 2) {
+    if (p.T > 256 && !p.combine && p.norm && p.route && !p.sort.fused && d.E <= kMaxExperts) {
+      const size_t smem = kRows * 64 * sizeof(float) + static_cast<size_t>(d.H) * 32;
+      hipLaunchKernelGGL(k_router_rows<KQ>, dim3((p.T + kRows - 1) / kRows), dim3(kPfThreads), smem, s, d, p);
+      return hipGetLastError();
+    }
+  }
   // 16 rows per workgroup when one workgroup takes the whole step (fused sort)
   // or the step is prefill-sized; otherwise one (split path, eight wavefronts
   // per row) or four, so that a verify step of a few hundred rows spreads its

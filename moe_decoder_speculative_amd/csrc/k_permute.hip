@@ -73,6 +73,37 @@ __global__ __launch_bounds__(kPermThreads) void k_permute(int E, PermuteParams p
   }
   __syncthreads();
 
+  if (e == 0 && wave == 1 && p.tiles) {
+    // the grouped GEMM's tile table from the same histogram: lane e counts
+    // expert e's token tiles
+    const int c = lane < E ? hist[lane] : 0;
+    int off = c;  // inclusive prefix of the counts, then of the tiles
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(off, o, kWave);
+      if (lane >= o) off += v;
+    }
+    off -= c;
+    const int mine = (c + kGemmTokens - 1) / kGemmTokens;
+    int incl = mine;
+#pragma unroll
+    for (int o = 1; o < kWave; o <<= 1) {
+      const int v = __shfl_up(incl, o, kWave);
+      if (lane >= o) incl += v;
+    }
+    const int T = p.tile_T, S = p.n_shared;
+    const int per_shared = (T + kGemmTokens - 1) / kGemmTokens;
+    const int n_shared = S * per_shared;
+    for (int i = lane; i < n_shared; i += kWave) {
+      const int slot = i / per_shared, m0 = (i % per_shared) * kGemmTokens;
+      p.tiles[i] = make_int4(E + slot, slot, m0, min(kGemmTokens, T - m0));
+    }
+    if (lane < E) {
+      int n = n_shared + incl - mine;
+      for (int m0 = 0; m0 < c; m0 += kGemmTokens) p.tiles[n++] = make_int4(lane, -1 - off, m0, min(kGemmTokens, c - m0));
+    }
+    if (lane == kWave - 1) *p.n_tiles = n_shared + incl;
+  }
   if (wave == 0) {
     const int c = lane < E ? hist[lane] : 0;
     int incl = c;

@@ -41,7 +41,7 @@ namespace moe {
 
 namespace {
 
-constexpr int kBT = 256;          // tokens per item
+constexpr int kBT = kGemmTokens;  // tokens per item
 constexpr int kRowTiles = 16;     // MFMA row tiles per item (256 rows)
 constexpr int kTokTiles = kBT / kTile;
 constexpr int kStages = 4;        // LDS ring depth (one 32-wide k-step per stage, 32 KiB each)
@@ -52,33 +52,6 @@ constexpr int kGemmWaves = kGemmThreads / kWave;
 constexpr int kLoadsA = kRowTiles / kGemmWaves;  // weight fragments a wavefront stages per step
 constexpr int kLoadsB = kTokTiles / kGemmWaves;  // token fragments a wavefront stages per step
 constexpr int kLoads = kLoadsA + kLoadsB;
-
-// Tile table: one entry per (slot, token tile), shared slots first, then the
-// routed experts in ascending order.  Built on the device after the
-// permutation by one wavefront (lane e counts expert e's tiles).
-__global__ __launch_bounds__(64) void k_tile_list(Dims d, GemmTileParams p) {
-  const int lane = threadIdx.x;
-  const int per_shared = (p.T + kBT - 1) / kBT;
-  const int c = lane < d.E ? p.cnt[lane] : 0;
-  const int mine = (c + kBT - 1) / kBT;
-  int incl = mine;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int v = __shfl_up(incl, o, kWave);
-    if (lane >= o) incl += v;
-  }
-  const int n_shared = d.S * per_shared;
-  for (int i = lane; i < n_shared; i += kWave) {
-    const int slot = i / per_shared, m0 = (i % per_shared) * kBT;
-    p.tiles[i] = make_int4(d.E + slot, slot, m0, min(kBT, p.T - m0));
-  }
-  if (lane < d.E) {
-    const int base = p.off[lane];
-    int n = n_shared + incl - mine;
-    for (int m0 = 0; m0 < c; m0 += kBT) p.tiles[n++] = make_int4(lane, -1 - base, m0, min(kBT, c - m0));
-  }
-  if (lane == kWave - 1) *p.n_tiles = n_shared + incl;
-}
 
 // OUT: 0 act (up), 1 fp32 y (down), 2 bf16 gate-weighted y (down)
 template <bool UP, int OUT>
@@ -428,11 +401,6 @@ int gemm_max_tiles(const Dims& d, int T) {
 }
 
 size_t gemm_lds_bytes() { return static_cast<size_t>(kStages) * kStageBytes; }
-
-hipError_t launch_tile_list(const Dims& d, const GemmTileParams& p, hipStream_t s) {
-  hipLaunchKernelGGL(k_tile_list, dim3(1), dim3(64), 0, s, d, p);
-  return hipGetLastError();
-}
 
 hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipStream_t s) {
   // the step schedule needs a multiple of 4 steps (H and I multiples of 128)

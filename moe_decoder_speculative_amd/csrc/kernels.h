@@ -61,6 +61,12 @@ struct PermuteParams {
   int* n_active;   // [1]
   int4* desc;      // [E] routed slot i: (expert, tokens, first pair in perm, 0) of active[i];
                    //     (-1, 0, 0, 0) past n_active -- one read tells an expert workgroup its work
+  // grouped-GEMM tile table, optional (see kGemmTokens): written by the
+  // first workgroup from the same histogram when `tiles` is set
+  int4* tiles;
+  int* n_tiles;
+  int tile_T;      // tokens of the block (the shared experts' rows)
+  int n_shared;    // shared experts (slots of the tile table before the routed ones)
 };
 hipError_t launch_permute(const Dims& d, const PermuteParams& p, hipStream_t s);
 
@@ -131,13 +137,11 @@ hipError_t launch_attention_split(const Dims& d, const AttnParams& p, hipStream_
 hipError_t launch_attention_combine(const AttnParams& p, hipStream_t s);
 
 // Grouped GEMM for prefill-sized token counts (MFMA, LDS-staged tiles).
-struct GemmTileParams {
-  const int* cnt;        // [E]
-  const int* off;        // [E+1]
-  int T;
-  int4* tiles;           // [gemm_max_tiles]: (expert, slot or -1-offset, first token, tokens)
-  int* n_tiles;          // [1]
-};
+// Grouped-GEMM tile table: one entry per (slot, token tile of kGemmTokens),
+// shared slots first, then the routed experts in ascending order; entry =
+// (expert weight index, shared slot or -1 - offset into perm, first token,
+// tokens).  Built by the permutation kernel.
+constexpr int kGemmTokens = 256;
 struct GemmParams {
   const void* xhat;      // [T][H] bf16
   const void* w_gate;    // tiled, this layer (see ExpertParams)
@@ -156,7 +160,6 @@ struct GemmParams {
 int gemm_max_tiles(const Dims& d, int T);
 int64_t gemm_act_rows(const Dims& d, int T);  // rows of the tiled activation buffer
 size_t gemm_lds_bytes();
-hipError_t launch_tile_list(const Dims& d, const GemmTileParams& p, hipStream_t s);
 hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipStream_t s);
 
 // Combine of a block whose expert rows are bf16 and already gate-weighted:
