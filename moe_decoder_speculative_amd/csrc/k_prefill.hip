@@ -52,6 +52,13 @@ constexpr int kGemmWaves = kGemmThreads / kWave;
 constexpr int kLoadsA = kRowTiles / kGemmWaves;  // weight fragments a wavefront stages per step
 constexpr int kLoadsB = kTokTiles / kGemmWaves;  // token fragments a wavefront stages per step
 constexpr int kLoads = kLoadsA + kLoadsB;
+// Down epilogue of a prefill block: the item's 256 tokens x 256 features in
+// bf16, staged in the (then idle) LDS ring with rows padded by 8 bytes (the
+// staging writes of 32 token columns then fall in distinct banks), plus the
+// item's 256 pair ids.
+constexpr int kStagePitch = 256 + 4;  // bf16 elements per staged token row
+constexpr size_t kEpiLds = static_cast<size_t>(kBT) * kStagePitch * 2 + kBT * sizeof(int);
+constexpr size_t kRingLds = static_cast<size_t>(kStages) * kStageBytes;
 
 // OUT: 0 act (up), 1 fp32 y (down), 2 bf16 gate-weighted y (down)
 template <bool UP, int OUT>
@@ -217,7 +224,17 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm(Dims d, GemmPa
   static_assert(kLoads <= 6, "ring loads are placed between the MFMAs of a half step");
 #pragma unroll
   for (int s = 0; s < kStages; ++s) issue(s);
-  __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kLoads));  // step 0 landed, 1..3 may be in flight
+  // the pairs' gate weights, requested now (behind the ring's first steps)
+  // rather than at the epilogue, where they were a dependent round trip
+  // (unconditional, clamped into the routed pairs: the wait counts below are
+  // constants; a shared item uses weight 1 and ignores them; the loop's first
+  // waits then also cover these two loads, which only makes them stricter)
+  float gw[2] = {1.0f, 1.0f};
+  if constexpr (OUT == 2) {
+#pragma unroll
+    for (int n = 0; n < 2; ++n) gw[n] = p.gate_w[min(max(out_pair[n], 0), p.T * d.k - 1)];
+  }
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kLoads + (OUT == 2 ? 2 : 0)));  // step 0 landed, 1..3 may be in flight
   __builtin_amdgcn_s_barrier();
   MOE_READ_HALF(0, 0, xa, xb)
   if (KT >= 8) {
@@ -261,27 +278,53 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm(Dims d, GemmPa
           *reinterpret_cast<uint2*>(dst + g * 16 * 8) = v;
         }
       }
+  } else if constexpr (OUT == 2) {
+    // gate-weighted rows through LDS: every wavefront has finished reading
+    // the ring, its 128 x 64 block goes to the staged [token][feature] tile,
+    // then each wavefront writes 32 whole token rows (512 contiguous bytes,
+    // 8 per lane) instead of 16-byte pieces of 32 rows per store
+    bf16_t* stg = reinterpret_cast<bf16_t*>(smem);
+    int* prs = reinterpret_cast<int*>(smem + static_cast<size_t>(kBT) * kStagePitch * 2);
+    __syncthreads();
+#pragma unroll
+    for (int n = 0; n < 2; ++n) {
+      const int tcol = wt * 64 + n * 32 + lane % 32;
+      if (wr == 0 && lane < 32) prs[tcol] = out_pair[n];
+#pragma unroll
+      for (int bl = 0; bl < 4; ++bl)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int fcol = wr * 128 + bl * 32 + 8 * g + 4 * (lane / 32);
+          const f32x16_t& c = acc[bl][n];
+          const float w = shared ? 1.0f : gw[n];
+          uint2 v;
+          v.x = pack_bf16x2(w * c[4 * g], w * c[4 * g + 1]);
+          v.y = pack_bf16x2(w * c[4 * g + 2], w * c[4 * g + 3]);
+          *reinterpret_cast<uint2*>(stg + tcol * kStagePitch + fcol) = v;
+        }
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int i = 0; i < kBT / kGemmWaves; ++i) {
+      const int tok = wave * (kBT / kGemmWaves) + i;
+      const int pr = prs[tok];
+      if (pr >= 0)
+        *reinterpret_cast<uint2*>(p.yb + static_cast<int64_t>(pr) * d.H + ft * 256 + lane * 4) =
+            *reinterpret_cast<const uint2*>(stg + tok * kStagePitch + lane * 4);
+    }
   } else {
 #pragma unroll
     for (int n = 0; n < 2; ++n) {
       const int pr = out_pair[n];
       if (pr < 0) continue;
-      const float gw = (OUT == 2 && !shared) ? p.gate_w[pr] : 1.0f;
 #pragma unroll
       for (int bl = 0; bl < 4; ++bl)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
           const int feat = ft * 256 + wr * 128 + bl * 32 + 8 * g + 4 * (lane / 32);
           const f32x16_t& c = acc[bl][n];
-          if constexpr (OUT == 2) {
-            uint2 v;
-            v.x = pack_bf16x2(gw * c[4 * g], gw * c[4 * g + 1]);
-            v.y = pack_bf16x2(gw * c[4 * g + 2], gw * c[4 * g + 3]);
-            *reinterpret_cast<uint2*>(p.yb + static_cast<int64_t>(pr) * d.H + feat) = v;
-          } else {
-            *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(pr) * d.H + feat) =
-                make_float4(c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
-          }
+          *reinterpret_cast<float4*>(p.y + static_cast<int64_t>(pr) * d.H + feat) =
+              make_float4(c[4 * g], c[4 * g + 1], c[4 * g + 2], c[4 * g + 3]);
         }
     }
   }
@@ -400,7 +443,7 @@ int gemm_max_tiles(const Dims& d, int T) {
   return d.S * ((T + kBT - 1) / kBT) + (T * d.k) / kBT + d.E;
 }
 
-size_t gemm_lds_bytes() { return static_cast<size_t>(kStages) * kStageBytes; }
+size_t gemm_lds_bytes() { return kRingLds > kEpiLds ? kRingLds : kEpiLds; }
 
 hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipStream_t s) {
   // the step schedule needs a multiple of 4 steps (H and I multiples of 128)
