@@ -7,10 +7,11 @@
 // each loads its quarter of the weight tile straight into registers with
 // coalesced 1 KiB reads (weights are pre-tiled in MFMA operand order), keeps it
 // there, and loops over the expert's tokens 16 at a time (tokens gathered from
-// the permutation; columns past the expert's tokens repeat its last token and
-// are never stored), issuing 16x16x32 bf16 MFMAs; with several token tiles the
-// next tile's activation fragments are requested before the current tile's
-// MFMAs.  The four partial sums are added through LDS.  For steps sorted by
+// the permutation; columns past the expert's tokens repeat its last token, so
+// they compute that token's values bit for bit and store them to its row
+// again), issuing 16x16x32 bf16 MFMAs; with several token tiles the next
+// tile's activation fragments are requested before the current tile's MFMAs.
+// The four partial sums are added through LDS.  For steps sorted by
 // the permutation kernel the slots are launched busiest first (the active
 // list is ordered by token count), so the longest workgroups do not trail
 // the kernel; the shared experts, which see every token, split their token
@@ -67,6 +68,56 @@ __device__ __forceinline__ int slot_pair(const Dims& d, const ExpertParams& p, c
 
 // ---------------------------------------------------------------- bf16 ----
 
+// Token tiles t, t + s, ... (below nt) of one workgroup: tile t + s's rows
+// are requested before tile t's MFMAs and the pairs they need one tile
+// earlier still, so that no tile waits for a pair and then for its rows;
+// nothing is requested past the last tile.  On entry tile t's rows are in b
+// (its lane's pair in pair) and the pairs of tile t + s in pr1 (requested).
+// pair_at(tile) requests the lane's pair of a tile, rows(tile, pr, b) its
+// rows, do_tile(pair, b) consumes a tile.  Every store of do_tile is made by
+// every lane (no branch around it): the compiler can then count the memory
+// operations in flight exactly, and waiting for a tile's rows does not mean
+// waiting for the previous tile's stores.
+template <int KW, class PairAt, class Rows, class DoTile>
+__device__ __forceinline__ void token_tiles(int t, int s, int nt, int pair, bf16x8_t (&b)[KW], int pr1,
+                                            PairAt pair_at, Rows rows, DoTile do_tile) {
+  for (;;) {
+    if (t + s >= nt) {
+      do_tile(pair, b);
+      return;
+    }
+    const int pr2 = pair_at(t + 2 * s);  // clamped: a valid read past the end
+    bf16x8_t bn[KW];
+    rows(t + s, pr1, bn);
+    do_tile(pair, b);
+    pair = pr1;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) b[i] = bn[i];
+    pr1 = pr2;
+    t += s;
+  }
+}
+
+// token_tiles with the lane's pair of a tile read from the permutation
+// (routed slot) or computed (shared slot) without a branch: a shared slot
+// reads a word of `any` (valid memory) and multiplies it by zero.  A register
+// loaded on one path and computed on the other would make the compiler wait
+// for every load in flight where the paths meet.
+template <int KW, class Rows, class DoTile>
+__device__ __forceinline__ void slot_tiles(const Dims& d, const ExpertParams& p, const SlotInfo& si, const void* any,
+                                           int lane, int t, int s, int nt, int pair, bf16x8_t (&b)[KW], int pr1,
+                                           Rows rows, DoTile do_tile) {
+  const bool shared = si.shared >= 0;
+  const int* src = shared ? static_cast<const int*>(any) : p.perm + si.base;
+  const int mul = shared ? 0 : 1, add = shared ? p.T * d.k + si.shared * p.T : 0;
+  token_tiles<KW>(t, s, nt, pair, b, pr1,
+                  [&](int tl) {
+                    const int n = min(tl * kTile + lane % kTile, si.ntok - 1);
+                    return src[n * mul] * mul + (add + n) * (1 - mul);
+                  },
+                  rows, do_tile);
+}
+
 // Workgroup b -> (slot, row tile r, chunk c, chunks n) for R row tiles.  The
 // shared experts see all T tokens, the most of any slot, and their workgroups
 // would run several times longer than the rest (latency-bound, one token tile
@@ -115,6 +166,8 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
   // requested while the weights are in flight instead of after them
   const int n0 = c * kTile + lane % kTile, nc0 = min(n0, si.ntok - 1);
   const int pr0 = slot_pair(d, p, si, nc0);
+  // and those of the workgroup's next tile (clamped: a valid read)
+  const int pr1 = slot_pair(d, p, si, min(n0 + split_ * kTile, si.ntok - 1));
   const int64_t tile = (static_cast<int64_t>(si.expert) * RT + rt) * KT + kt0;
   const bf16_t* g = reinterpret_cast<const bf16_t*>(p.w_gate) + tile * kFragElems + lane * 8;
   const bf16_t* u = reinterpret_cast<const bf16_t*>(p.w_up) + tile * kFragElems + lane * 8;
@@ -126,19 +179,15 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
   }
 
   // activation fragments of a token tile (column lane % 16) given the pair of
-  // its n-th token (nc = n clamped); rows past the slot's tokens repeat its
-  // last token and are never stored
-  auto load_rows = [&](int n, int nc, int pr, int& pair, bf16x8_t (&b)[KW]) {
-    pair = n < si.ntok ? pr : -1;
+  // its n-th token clamped to the last (nc); a column past the slot's tokens
+  // repeats its last token
+  auto load_rows = [&](int nc, int pr, bf16x8_t (&b)[KW]) {
     const int tok = si.shared >= 0 ? nc : pr / d.k;
     const bf16_t* xr = xh + static_cast<int64_t>(tok) * d.H + kt0 * kKStep + (lane / kTile) * 8;
 #pragma unroll
     for (int i = 0; i < KW; ++i) b[i] = load_frag(xr + i * kKStep);
   };
-  auto load_tile = [&](int tile0, int& pair, bf16x8_t (&b)[KW]) {
-    const int n = tile0 + lane % kTile, nc = min(n, si.ntok - 1);
-    load_rows(n, nc, slot_pair(d, p, si, nc), pair, b);
-  };
+  auto rows = [&](int tl, int pr, bf16x8_t (&b)[KW]) { load_rows(min(tl * kTile + lane % kTile, si.ntok - 1), pr, b); };
   auto do_tile = [&](int pair, const bf16x8_t (&b)[KW]) {
     f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -157,33 +206,20 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
       const int L = threadIdx.x % kWave, i = threadIdx.x / kWave;
       const int col = L % kTile, row = 4 * (L / kTile) + i;
       const int pr = pairs[col];
-      if (pr >= 0) {
-        const float gs = ((red[0][0][L][i] + red[1][0][L][i]) + red[2][0][L][i]) + red[3][0][L][i];
-        const float us = ((red[0][1][L][i] + red[1][1][L][i]) + red[2][1][L][i]) + red[3][1][L][i];
-        act[static_cast<int64_t>(pr) * d.I + rt * kTile + row] = f32_to_bf16(silu_mul(gs, us));
-      }
+      const float gs = ((red[0][0][L][i] + red[1][0][L][i]) + red[2][0][L][i]) + red[3][0][L][i];
+      const float us = ((red[0][1][L][i] + red[1][1][L][i]) + red[2][1][L][i]) + red[3][1][L][i];
+      act[static_cast<int64_t>(pr) * d.I + rt * kTile + row] = f32_to_bf16(silu_mul(gs, us));
     }
     __syncthreads();
   };
 
-  int pair;
   bf16x8_t b[KW];
-  load_rows(n0, nc0, pr0, pair, b);
+  load_rows(nc0, pr0, b);
   if (c + split_ >= nt) {
-    do_tile(pair, b);
+    do_tile(pr0, b);
     return;
   }
-  // several token tiles: the next tile's fragments are requested before this
-  // tile's MFMAs (unconditionally; past the last tile they are never used)
-  for (int t = c; t < nt; t += split_) {
-    int pair_n;
-    bf16x8_t bn[KW];
-    load_tile((t + split_) * kTile, pair_n, bn);
-    do_tile(pair, b);
-    pair = pair_n;
-#pragma unroll
-    for (int i = 0; i < KW; ++i) b[i] = bn[i];
-  }
+  slot_tiles<KW>(d, p, si, p.xhat, lane, c, split_, nt, pr0, b, pr1, rows, do_tile);
 }
 
 // Epilogue of the down kernel when it serves as a plain linear layer over
@@ -240,6 +276,7 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
   // the first token tile's pairs before the weights (see the up kernel)
   const int n0 = c * kTile + lane % kTile;
   const int pr0 = slot_pair(d, p, si, min(n0, si.ntok - 1));
+  const int pr1 = slot_pair(d, p, si, min(n0 + split_ * kTile, si.ntok - 1));
   bf16x8_t a[RPW][KW];
 #pragma unroll
   for (int r = 0; r < RPW; ++r) {
@@ -250,20 +287,16 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
   }
 
   // activation fragments of a token tile (column lane % 16) given the pair of
-  // its n-th token; rows past the slot's tokens repeat its last pair and are
-  // never stored
-  auto load_rows = [&](int n, int pr, int& pair, bf16x8_t (&b)[KW]) {
-    pair = n < si.ntok ? pr : -1;
+  // its n-th token clamped to the last (nc); a column past the slot's tokens
+  // repeats its last pair
+  auto load_rows = [&](int nc, int pr, bf16x8_t (&b)[KW]) {
     // a linear layer's slots all read the token's own row
-    const int arow = EPI == 0 ? pr : min(n, si.ntok - 1);
+    const int arow = EPI == 0 ? pr : nc;
     const bf16_t* ar = act + static_cast<int64_t>(arow) * d.I + kt0 * kKStep + (lane / kTile) * 8;
 #pragma unroll
     for (int i = 0; i < KW; ++i) b[i] = load_frag(ar + i * kKStep);
   };
-  auto load_tile = [&](int tile0, int& pair, bf16x8_t (&b)[KW]) {
-    const int n = tile0 + lane % kTile;
-    load_rows(n, slot_pair(d, p, si, min(n, si.ntok - 1)), pair, b);
-  };
+  auto rows = [&](int tl, int pr, bf16x8_t (&b)[KW]) { load_rows(min(tl * kTile + lane % kTile, si.ntok - 1), pr, b); };
   auto do_tile = [&](int pair, const bf16x8_t (&b)[KW]) {
     f32x4_t c[RPW];
 #pragma unroll
@@ -277,14 +310,15 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
     if (wave == 0 && lane < kTile) pairs[lane] = pair;
     __syncthreads();
     if constexpr (EPI == 0) {
-      for (int q = threadIdx.x; q < RPW * kWave * 4; q += kBlock) {
+      static_assert(RPW * kWave * 4 % kBlock == 0, "whole passes of the workgroup over the outputs");
+#pragma unroll
+      for (int j = 0; j < RPW * kWave * 4 / kBlock; ++j) {
+        const int q = threadIdx.x + j * kBlock;
         const int r = q / (kWave * 4), L = (q / 4) % kWave, i = q % 4;
         const int col = L % kTile, row = 4 * (L / kTile) + i;
         const int pr = pairs[col];
-        if (pr >= 0) {
-          const float v = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
-          p.y[static_cast<int64_t>(pr) * d.H + (rb * RPW + r) * kTile + row] = v;
-        }
+        const float v = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
+        p.y[static_cast<int64_t>(pr) * d.H + (rb * RPW + r) * kTile + row] = v;
       }
     } else {
       // feature pairs (row, row + 1) of one token per thread
@@ -292,35 +326,22 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
         const int r = q / (kWave * 2), L = (q / 2) % kWave, i = 2 * (q % 2);
         const int col = L % kTile, row = 4 * (L / kTile) + i;
         const int pr = pairs[col];
-        if (pr >= 0) {
-          const float v0 = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
-          const float v1 = ((red[0][r][L][i + 1] + red[1][r][L][i + 1]) + red[2][r][L][i + 1]) + red[3][r][L][i + 1];
-          const int n = pr - si.shared * p.T;  // token of the shared-slot row (no routed slots)
-          linear_epilogue<EPI>(d, p, e, si.shared, n, (rb * RPW + r) * kTile + row, v0, v1);
-        }
+        const float v0 = ((red[0][r][L][i] + red[1][r][L][i]) + red[2][r][L][i]) + red[3][r][L][i];
+        const float v1 = ((red[0][r][L][i + 1] + red[1][r][L][i + 1]) + red[2][r][L][i + 1]) + red[3][r][L][i + 1];
+        const int n = pr - si.shared * p.T;  // token of the shared-slot row (no routed slots)
+        linear_epilogue<EPI>(d, p, e, si.shared, n, (rb * RPW + r) * kTile + row, v0, v1);
       }
     }
     __syncthreads();
   };
 
-  int pair;
   bf16x8_t b[KW];
-  load_rows(n0, pr0, pair, b);
+  load_rows(min(n0, si.ntok - 1), pr0, b);
   if (c + split_ >= nt) {
-    do_tile(pair, b);
+    do_tile(pr0, b);
     return;
   }
-  // several token tiles: the next tile's fragments are requested before this
-  // tile's MFMAs (unconditionally; past the last tile they are never used)
-  for (int t = c; t < nt; t += split_) {
-    int pair_n;
-    bf16x8_t bn[KW];
-    load_tile((t + split_) * kTile, pair_n, bn);
-    do_tile(pair, b);
-    pair = pair_n;
-#pragma unroll
-    for (int i = 0; i < KW; ++i) b[i] = bn[i];
-  }
+  slot_tiles<KW>(d, p, si, p.act, lane, c, split_, nt, pr0, b, pr1, rows, do_tile);
 }
 
 // ------------------------------------------------------------- float32 ----
