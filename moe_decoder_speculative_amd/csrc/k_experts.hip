@@ -15,7 +15,7 @@
 // the permutation kernel the slots are launched busiest first (the active
 // list is ordered by token count), so the longest workgroups do not trail
 // the kernel; the shared experts, which see every token, split their token
-// tiles over up to four workgroups (see split_index).
+// tiles over up to two workgroups (see split_index).
 //   up:   a[pair][i] = round(silu(Wg x)[i] * (Wu x)[i])        (pairs of the slot)
 //   down: y[pair][h] = (Wd a)[h]                                 (float32)
 // Shared experts occupy slots 0..S-1 and see every token.  The page "Jina AI
@@ -385,9 +385,11 @@ __global__ __launch_bounds__(kBlock) void k_down_f32(Dims d, ExpertParams p) {
   }
 }
 
-// Ways to split a shared expert's T tokens over workgroups: at most two
-// token tiles per workgroup, at most four ways.
-int token_split(int T) { return std::min(4, std::max(1, (T + 2 * kTile - 1) / (2 * kTile))); }
+// Ways to split a shared expert's T tokens over workgroups: two once there
+// are more than two token tiles.  With the token-tile loop pipelined a tile
+// costs about one activation round trip, and four ways (a quarter of the
+// first workgroups then fetch nothing from HBM) measured slower than two.
+int token_split(int T) { return std::min(2, std::max(1, (T + 2 * kTile - 1) / (2 * kTile))); }
 // grid for R row tiles: the shared part (whole groups of 8 pairs, `split`
 // ways), then one workgroup per routed (slot, row tile) -- for at most T*k
 // routed slots, as many as T tokens can activate (the rest would only read
