@@ -2,11 +2,14 @@
 //
 // At decode sizes the experts are bound by streaming their weights from HBM:
 // each selected expert's 3 x I x H weights are read once per step, whatever
-// the number of its tokens.  One workgroup owns (expert slot, tile of 16
-// output rows).  Its four wavefronts split the reduction dimension in four and
-// each loads its quarter of the weight tile straight into registers with
-// coalesced 1 KiB reads (weights are pre-tiled in MFMA operand order), keeps it
-// there, and loops over the expert's tokens 16 at a time (tokens gathered from
+// the number of its tokens.  One workgroup owns (expert slot, RPW tiles of 16
+// output rows: two for the gate/up projection, four for the down projection
+// above 16 rows, as many as fit in 256 registers, so that two workgroups per
+// CU keep the most weight bytes in flight).  Its four wavefronts split the
+// reduction dimension in four and each loads its quarter of the weight tiles
+// straight into registers with coalesced 1 KiB reads (weights are pre-tiled in
+// MFMA operand order), keeps them there, and loops over the expert's tokens 16
+// at a time (tokens gathered from
 // the permutation; columns past the expert's tokens repeat its last token, so
 // they compute that token's values bit for bit and store them to its row
 // again), issuing 16x16x32 bf16 MFMAs; with several token tiles the next
@@ -145,14 +148,17 @@ __device__ __forceinline__ void split_index(const Dims& d, int R, int b, int spl
   }
 }
 
-template <int KW>  // k-steps per wavefront: H / 32 / 4
-__global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int split) {
-  __shared__ float red[4][2][kWave][4];
+// KW: k-steps per wavefront (H / 32 / 4); RPW: row tiles per workgroup (with
+// two, the launch bound holds the kernel to 256 registers: two wavefronts per
+// SIMD)
+template <int KW, int RPW>
+__global__ __launch_bounds__(kBlock, RPW == 1 ? 1 : 2) void k_up_mfma(Dims d, ExpertParams p, int split) {
+  __shared__ float red[4][RPW][2][kWave][4];
   __shared__ int pairs[kTile];
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int RT = d.I / kTile, KT = d.H / kKStep;
-  int slot, rt, c, split_;
-  split_index(d, RT, blockIdx.x, split, slot, rt, c, split_);
+  const int RB = d.I / (kTile * RPW), KT = d.H / kKStep;
+  int slot, rb, c, split_;
+  split_index(d, RB, blockIdx.x, split, slot, rb, c, split_);
   if (slot < d.S && c * kTile >= p.T) return;  // a chunk past the shared tokens
   SlotInfo si;
   if (!slot_info(d, p, slot, si)) return;
@@ -168,14 +174,17 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
   const int pr0 = slot_pair(d, p, si, nc0);
   // and those of the workgroup's next tile (clamped: a valid read)
   const int pr1 = slot_pair(d, p, si, min(n0 + split_ * kTile, si.ntok - 1));
-  const int64_t tile = (static_cast<int64_t>(si.expert) * RT + rt) * KT + kt0;
-  const bf16_t* g = reinterpret_cast<const bf16_t*>(p.w_gate) + tile * kFragElems + lane * 8;
-  const bf16_t* u = reinterpret_cast<const bf16_t*>(p.w_up) + tile * kFragElems + lane * 8;
-  bf16x8_t ag[KW], au[KW];
+  bf16x8_t ag[RPW][KW], au[RPW][KW];
 #pragma unroll
-  for (int i = 0; i < KW; ++i) {
-    ag[i] = load_frag(g + i * kFragElems);
-    au[i] = load_frag(u + i * kFragElems);
+  for (int r = 0; r < RPW; ++r) {
+    const int64_t tile = (static_cast<int64_t>(si.expert) * (d.I / kTile) + rb * RPW + r) * KT + kt0;
+    const bf16_t* g = reinterpret_cast<const bf16_t*>(p.w_gate) + tile * kFragElems + lane * 8;
+    const bf16_t* u = reinterpret_cast<const bf16_t*>(p.w_up) + tile * kFragElems + lane * 8;
+#pragma unroll
+    for (int i = 0; i < KW; ++i) {
+      ag[r][i] = load_frag(g + i * kFragElems);
+      au[r][i] = load_frag(u + i * kFragElems);
+    }
   }
 
   // activation fragments of a token tile (column lane % 16) given the pair of
@@ -189,26 +198,30 @@ __global__ __launch_bounds__(kBlock) void k_up_mfma(Dims d, ExpertParams p, int 
   };
   auto rows = [&](int tl, int pr, bf16x8_t (&b)[KW]) { load_rows(min(tl * kTile + lane % kTile, si.ntok - 1), pr, b); };
   auto do_tile = [&](int pair, const bf16x8_t (&b)[KW]) {
-    f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < KW; ++i) {
-      cg = mfma16(ag[i], b[i], cg);
-      cu = mfma16(au[i], b[i], cu);
-    }
+    for (int r = 0; r < RPW; ++r) {
+      f32x4_t cg = {0.f, 0.f, 0.f, 0.f}, cu = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      red[wave][0][lane][i] = cg[i];
-      red[wave][1][lane][i] = cu[i];
+      for (int i = 0; i < KW; ++i) {
+        cg = mfma16(ag[r][i], b[i], cg);
+        cu = mfma16(au[r][i], b[i], cu);
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        red[wave][r][0][lane][i] = cg[i];
+        red[wave][r][1][lane][i] = cu[i];
+      }
     }
     if (wave == 0 && lane < kTile) pairs[lane] = pair;
     __syncthreads();
-    {
+#pragma unroll
+    for (int r = 0; r < RPW; ++r) {
       const int L = threadIdx.x % kWave, i = threadIdx.x / kWave;
       const int col = L % kTile, row = 4 * (L / kTile) + i;
       const int pr = pairs[col];
-      const float gs = ((red[0][0][L][i] + red[1][0][L][i]) + red[2][0][L][i]) + red[3][0][L][i];
-      const float us = ((red[0][1][L][i] + red[1][1][L][i]) + red[2][1][L][i]) + red[3][1][L][i];
-      act[static_cast<int64_t>(pr) * d.I + rt * kTile + row] = f32_to_bf16(silu_mul(gs, us));
+      const float gs = ((red[0][r][0][L][i] + red[1][r][0][L][i]) + red[2][r][0][L][i]) + red[3][r][0][L][i];
+      const float us = ((red[0][r][1][L][i] + red[1][r][1][L][i]) + red[2][r][1][L][i]) + red[3][r][1][L][i];
+      act[static_cast<int64_t>(pr) * d.I + (rb * RPW + r) * kTile + row] = f32_to_bf16(silu_mul(gs, us));
     }
     __syncthreads();
   };
@@ -401,22 +414,40 @@ int split_grid(const Dims& d, int R, int split, int T) {
 
 template <int KW>
 hipError_t up_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
+  // two row tiles per workgroup (twice the weights in flight per CU at two
+  // workgroups per CU) while their fragments fit in 256 registers
+  constexpr int RPW = KW <= 10 ? 2 : 1;
   const int split = token_split(p.T);
-  const int grid = split_grid(d, d.I / kTile, split, p.T);
-  hipLaunchKernelGGL(k_up_mfma<KW>, dim3(grid), dim3(kBlock), 0, s, d, p, split);
+  if ((d.I / kTile) % RPW == 0) {
+    const int grid = split_grid(d, d.I / (kTile * RPW), split, p.T);
+    hipLaunchKernelGGL((k_up_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p, split);
+  } else {
+    const int grid = split_grid(d, d.I / kTile, split, p.T);
+    hipLaunchKernelGGL((k_up_mfma<KW, 1>), dim3(grid), dim3(kBlock), 0, s, d, p, split);
+  }
   return hipGetLastError();
 }
 
+template <int KW, int RPW>
+void down_rpw(const Dims& d, const ExpertParams& p, hipStream_t s) {
+  const int split = token_split(p.T);
+  const int grid = split_grid(d, d.H / (kTile * RPW), split, p.T);
+  hipLaunchKernelGGL((k_down_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p, split, EpiParams{});
+}
+
+// Four row tiles per workgroup once a slot can hold more than one token tile
+// and their fragments fit in 256 registers (two at most 16 rows: there a
+// step is short enough that spreading its few slots' weights over more
+// workgroups wins).
 template <int KW>
 hipError_t down_kw(const Dims& d, const ExpertParams& p, hipStream_t s) {
-  constexpr int RPW = 2;
-  const int split = token_split(p.T);
-  if ((d.H / kTile) % RPW == 0) {
-    const int grid = split_grid(d, d.H / (kTile * RPW), split, p.T);
-    hipLaunchKernelGGL((k_down_mfma<KW, RPW>), dim3(grid), dim3(kBlock), 0, s, d, p, split, EpiParams{});
+  const int tiles = d.H / kTile;
+  if (KW <= 10 && p.T > kTile && tiles % 4 == 0) {
+    down_rpw<KW, 4>(d, p, s);
+  } else if (tiles % 2 == 0) {
+    down_rpw<KW, 2>(d, p, s);
   } else {
-    const int grid = split_grid(d, d.H / kTile, split, p.T);
-    hipLaunchKernelGGL((k_down_mfma<KW, 1>), dim3(grid), dim3(kBlock), 0, s, d, p, split, EpiParams{});
+    down_rpw<KW, 1>(d, p, s);
   }
   return hipGetLastError();
 }
