@@ -30,7 +30,11 @@
 // Items are numbered slot-major, token tile, feature tile, and handed out so
 // that each XCD works through a contiguous range of them: the workgroups that
 // share a token tile or a weight tile run together on one XCD and hit in its
-// L2.  Shared experts occupy slots 0..S-1.  The 64 routed + 2 shared experts
+// L2.  With a reduction of 16 steps or more (H >= 512) the gate+up GEMM runs
+// as a persistent kernel (k_gemm_up_persist) whose ring carries on from one
+// item into the next; the down GEMM, whose epilogue stages its rows in the
+// ring, keeps one item per workgroup.  Shared experts occupy slots 0..S-1.
+// The 64 routed + 2 shared experts
 // with top-6 routing follow the page "Jina AI releases lightweight OCR model
 // with built-in speculative decoding", section "Lean architecture with a
 // compressed encoder"; a page holds at most 1,156 visual tokens (same
@@ -330,6 +334,260 @@ __global__ __launch_bounds__(kGemmThreads, 1) void k_grouped_gemm(Dims d, GemmPa
   }
 }
 
+// Gate+up GEMM as a persistent kernel: one workgroup per CU works through the
+// items of its XCD's range (items c, c + 32, c + 64, ... of the range for the
+// XCD's c-th workgroup), and the LDS ring runs on from one item into the next:
+// the last four steps of an item issue the first four steps of the next, so
+// those loads are in flight during the epilogue, and a new item starts
+// without a launch, a lookup or an empty ring.  What the next item's loads
+// need is fetched one item ahead through the same direct-to-LDS path as the
+// operands -- its tile-table entry at step 0, its token pairs at step 4 (once
+// the entry is in), read back at step 8 -- so the only vector memory
+// operations in flight are ring loads, those two fetches and the epilogue's
+// stores, and every wait in the loop is an exact constant; a lookup into
+// registers would make the compiler wait for it with the ring loads behind it.
+// Same items, same arithmetic and the same activation layout as
+// k_grouped_gemm<true, 0>, except that padding token columns are stored too
+// (their zero rows give zero activations in rows no result reads), so the
+// epilogue's store count is fixed.
+constexpr int kMetaBytes = 512;   // per wavefront: a tile-table entry (256 B) and 64 token pairs (256 B)
+constexpr size_t kPersistLds = kRingLds + kGemmWaves * kMetaBytes;
+constexpr int kUpEpiStores = 16;  // global stores per lane of one up epilogue (2 x 2 x 4, none skipped)
+constexpr int kPersistWgs = 256;  // one workgroup per CU
+constexpr int kPersistMinSteps = 16;  // steps 0..8 are scheduled one by one; the next item's loads start at KT-4
+
+__global__ __launch_bounds__(kGemmThreads, 1) void k_gemm_up_persist(Dims d, GemmParams p) {
+  extern __shared__ __align__(16) unsigned char smem[];
+  const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  const int wr = wave / (kGemmWaves / 2), wt = wave % (kGemmWaves / 2);
+  const int n_ft = d.I / 128;
+  const int n_items = *p.n_tiles * n_ft;
+  const int chunk = (n_items + kXcds - 1) / kXcds;
+  const int xcd = blockIdx.x % kXcds, stride = gridDim.x / kXcds;
+  const int item_end = min((xcd + 1) * chunk, n_items);
+  int item = xcd * chunk + blockIdx.x / kXcds;
+  if (item >= item_end) return;
+
+  const int KT = d.H / kKStep;
+  const bf16_t* wg = reinterpret_cast<const bf16_t*>(p.w_gate);
+  const bf16_t* wu = reinterpret_cast<const bf16_t*>(p.w_up);
+  const bf16_t* src = reinterpret_cast<const bf16_t*>(p.xhat);
+  const int rpe = d.I / kTile;  // weight row tiles per expert
+  unsigned char* meta = smem + kRingLds + wave * kMetaBytes;
+
+  // weight fragments kLoadsA*wave .. +kLoadsA of an item (8 gate + 8 up row
+  // tiles of feature tile ft) and the lane's row offsets of the token
+  // fragments kLoadsB*wave .. +kLoadsB (64 contiguous bytes per row and step)
+  auto weights = [&](int expert, int ft, const bf16_t* (&w)[kLoadsA]) {
+#pragma unroll
+    for (int q = 0; q < kLoadsA; ++q) {
+      const int r = wave * kLoadsA + q, half = r / 8, qq = r % 8;
+      w[q] = ((qq / 4) ? wu : wg) + static_cast<int64_t>(expert * rpe + ft * 8 + half * 4 + qq % 4) * KT * kFragElems;
+    }
+  };
+  auto row_off = [&](bool shared, int m0, int ntok, int t, int pair) -> uint32_t {
+    int row = p.xhat_zero_row;  // padding tokens read an all-zero row
+    if (t < ntok) row = shared ? m0 + t : pair / d.k;
+    return static_cast<uint32_t>(row) * d.H + (lane / kTile) * 8;
+  };
+  auto issue = [&](const bf16_t* const (&w)[kLoadsA], const uint32_t (&to)[kLoadsB], int kt) {
+    unsigned char* st = smem + (kt % kStages) * kStageBytes;
+#pragma unroll
+    for (int q = 0; q < kLoadsA; ++q)
+      __builtin_amdgcn_global_load_lds((void*)((w[q] + kt * kFragElems) + lane * 8),
+                                       (lds_ptr_t)(st + (wave * kLoadsA + q) * 1024), 16, 0, 0);
+#pragma unroll
+    for (int q = 0; q < kLoadsB; ++q)
+      __builtin_amdgcn_global_load_lds((void*)((src + kt * kKStep) + to[q]),
+                                       (lds_ptr_t)(st + (kRowTiles + wave * kLoadsB + q) * 1024), 16, 0, 0);
+  };
+  // one-item-ahead fetches into the wavefront's meta area: the 4 words of a
+  // tile-table entry (lane i loads word i % 4; clamped to a valid entry), and
+  // the pairs of the wavefront's 32 tokens of an item (lane i the pair of
+  // token 32 * wave + i % 32, clamped into the item's tokens; a shared item
+  // needs none and reads a valid word)
+  auto fetch_entry = [&](int it) {
+    const int* e = reinterpret_cast<const int*>(p.tiles + min(it, n_items - 1) / n_ft) + lane % 4;
+    __builtin_amdgcn_global_load_lds((void*)e, (lds_ptr_t)meta, 4, 0, 0);
+  };
+  auto fetch_pairs = [&](bool shared, int base, int m0, int ntok) {
+    const int t = min(wave * 32 + lane % 32, ntok - 1);
+    const int* e = p.perm + (shared ? 0 : base + m0 + t);
+    __builtin_amdgcn_global_load_lds((void*)e, (lds_ptr_t)(meta + 256), 4, 0, 0);
+  };
+
+  // the current item's loads; the first item's lookups are ordinary loads
+  const bf16_t* cw[kLoadsA];
+  uint32_t ct[kLoadsB];
+  {
+    const int4 tile = p.tiles[item / n_ft];
+    const bool shared = tile.y >= 0;
+    const int base = shared ? 0 : -1 - tile.y;
+    weights(tile.x, item % n_ft, cw);
+#pragma unroll
+    for (int q = 0; q < kLoadsB; ++q) {
+      const int t = (wave * kLoadsB + q) * kTile + lane % kTile;
+      const int pair = (!shared && t < tile.w) ? p.perm[base + tile.z + t] : 0;
+      ct[q] = row_off(shared, tile.z, tile.w, t, pair);
+    }
+  }
+  const bf16_t* nw[kLoadsA];
+  uint32_t nt[kLoadsB];
+  bool n_shared = false;
+  int n_base = 0, n_m0 = 0, n_ntok = 1, n_expert = 0;
+
+  const int lane_off = ((lane >> 4) & 1) * 1024 + ((lane & 15) + 16 * (lane >> 5)) * 16;
+  f32x16_t acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+  bf16x8_t xa[4], xb[2], ya[4], yb[2];
+
+#define MOE_READ_HALF(K, KK, FA, FB)                                                               \
+  {                                                                                                \
+    const unsigned char* st_ = smem + ((K) % kStages) * kStageBytes + lane_off + (KK) * 512;       \
+    _Pragma("unroll") for (int j = 0; j < 2; ++j)                                                  \
+      FB[j] = *reinterpret_cast<const bf16x8_t*>(st_ + (kRowTiles + wt * 4 + 2 * j) * 1024);       \
+    _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                  \
+      FA[i] = *reinterpret_cast<const bf16x8_t*>(st_ + (wr * 8 + 2 * i) * 1024);                   \
+  }
+#define MOE_MMA_HALF(FA, FB)                                                                       \
+  _Pragma("unroll") for (int i = 0; i < 4; ++i)                                                    \
+  _Pragma("unroll") for (int j = 0; j < 2; ++j) acc[i][j] = mfma32(FA[i], FB[j], acc[i][j]);
+#define MOE_INTERLEAVE(LOADS)                                                                      \
+  _Pragma("unroll") for (int g_ = 0; g_ < 6; ++g_) {                                               \
+    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                                             \
+    if (g_ < (LOADS)) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);                           \
+    __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                                             \
+  }                                                                                                \
+  __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+// One step K as in k_grouped_gemm, with the refill (and whatever rides with
+// it) given as the statement ISSUE; LOADS: vector memory operations it issues
+#define MOE_STEP(K, VM, LOADS, ISSUE, NEXT)                                                        \
+  {                                                                                                \
+    MOE_READ_HALF(K, 1, ya, yb)                                                                    \
+    MOE_MMA_HALF(xa, xb)                                                                           \
+    MOE_INTERLEAVE(0)                                                                              \
+    if (NEXT) {                                                                                    \
+      __builtin_amdgcn_s_waitcnt(waitcnt_vm(VM));                                                  \
+      __builtin_amdgcn_s_waitcnt(waitcnt_lgkm0);                                                   \
+      __builtin_amdgcn_s_barrier();                                                                \
+      ISSUE;                                                                                       \
+      MOE_READ_HALF((K) + 1, 0, xa, xb)                                                            \
+    }                                                                                              \
+    MOE_MMA_HALF(ya, yb)                                                                           \
+    if (NEXT) { MOE_INTERLEAVE(LOADS) }                                                            \
+  }
+
+  // Wait counts.  At step K's wait, the operations younger than step K+1's
+  // loads may stay in flight: steps K+2 and K+3 (2 kLoads); at steps 0..2 of
+  // an item after the first also the previous epilogue's stores (issued after
+  // this item's steps 0..3); the entry and pair fetches (one operation each,
+  // at steps 0 and 4) are left out of the counts, which only makes the three
+  // waits after each of them stricter by one operation.
+  constexpr int kVm = 2 * kLoads, kVmEpi = 2 * kLoads + kUpEpiStores;
+  for (int s = 0; s < kStages; ++s) issue(cw, ct, s);
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kLoads));  // step 0 landed, 1..3 may be in flight
+  __builtin_amdgcn_s_barrier();
+  MOE_READ_HALF(0, 0, xa, xb)
+  bool first = true;
+  for (;;) {
+    const int nxt = item + stride;
+    const bool has_next = nxt < item_end;
+    const int tix = item / n_ft, ft = item % n_ft;
+    if (first) {
+      MOE_STEP(0, kVm, kLoads + 1, (issue(cw, ct, 4), fetch_entry(nxt)), true)
+      MOE_STEP(1, kVm, kLoads, issue(cw, ct, 5), true)
+      MOE_STEP(2, kVm, kLoads, issue(cw, ct, 6), true)
+    } else {
+      MOE_STEP(0, kVmEpi, kLoads + 1, (issue(cw, ct, 4), fetch_entry(nxt)), true)
+      MOE_STEP(1, kVmEpi, kLoads, issue(cw, ct, 5), true)
+      MOE_STEP(2, kVmEpi, kLoads, issue(cw, ct, 6), true)
+    }
+    MOE_STEP(3, kVm, kLoads, issue(cw, ct, 7), true)
+    // step 4: the entry fetched at step 0 is in (it is older than step 5)
+    MOE_STEP(4, kVm, kLoads + 1,
+             {
+               issue(cw, ct, 8);
+               asm volatile("" ::: "memory");
+               const int e = *reinterpret_cast<const int*>(meta + 4 * (lane % 4));
+               n_expert = __builtin_amdgcn_readlane(e, 0);
+               const int ey = __builtin_amdgcn_readlane(e, 1);
+               n_shared = ey >= 0;
+               n_base = n_shared ? 0 : -1 - ey;
+               n_m0 = __builtin_amdgcn_readlane(e, 2);
+               n_ntok = __builtin_amdgcn_readlane(e, 3);
+               fetch_pairs(n_shared, n_base, n_m0, n_ntok);
+             },
+             true)
+    MOE_STEP(5, kVm, kLoads, issue(cw, ct, 9), true)
+    MOE_STEP(6, kVm, kLoads, issue(cw, ct, 10), true)
+    MOE_STEP(7, kVm, kLoads, issue(cw, ct, 11), true)
+    // step 8: the pairs fetched at step 4 are in (older than step 9)
+    MOE_STEP(8, kVm, kLoads,
+             {
+               issue(cw, ct, 12);
+               asm volatile("" ::: "memory");
+               weights(n_expert, nxt % n_ft, nw);
+               _Pragma("unroll") for (int q = 0; q < kLoadsB; ++q) {
+                 const int t = (wave * kLoadsB + q) * kTile + lane % kTile;
+                 const int pair = *reinterpret_cast<const int*>(meta + 256 + 4 * (q * kTile + lane % kTile));
+                 nt[q] = row_off(n_shared, n_m0, n_ntok, t, pair);
+               }
+             },
+             true)
+    for (int k = 9; k < KT - kStages; ++k) MOE_STEP(k, kVm, kLoads, issue(cw, ct, k + kStages), true)
+    // the last four steps always issue an item's first four steps: the next
+    // one's, or after the last item those of the clamped entry fetched above
+    // (valid memory, never read), so both cases share one schedule
+    MOE_STEP(KT - 4, kVm, kLoads, issue(nw, nt, 0), true)
+    MOE_STEP(KT - 3, kVm, kLoads, issue(nw, nt, 1), true)
+    MOE_STEP(KT - 2, kVm, kLoads, issue(nw, nt, 2), true)
+    MOE_STEP(KT - 1, kVm, kLoads, issue(nw, nt, 3), true)  // reads the next item's (0, 0)
+
+    // epilogue as k_grouped_gemm<true, 0>: a = round(silu(g) * u) in
+    // operand-tile order at row 256 tix + token; all 16 stores made
+    bf16_t* act = reinterpret_cast<bf16_t*>(p.act);
+    const int IT = d.I / kKStep;
+#pragma unroll
+    for (int bl = 0; bl < 2; ++bl)
+#pragma unroll
+      for (int n = 0; n < 2; ++n) {
+        const int rt = tix * kTokTiles + wt * 4 + n * 2 + (lane % 32) / 16;
+        const int ctile = ft * 4 + wr * 2 + bl;
+        bf16_t* dst = act + (static_cast<int64_t>(rt) * IT + ctile) * kFragElems + (lane % 16) * 8 + 4 * (lane / 32);
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const f32x16_t& gt = acc[bl][n];
+          const f32x16_t& up = acc[bl + 2][n];
+          uint2 v;
+          v.x = pack_bf16x2(silu_mul(gt[4 * g], up[4 * g]), silu_mul(gt[4 * g + 1], up[4 * g + 1]));
+          v.y = pack_bf16x2(silu_mul(gt[4 * g + 2], up[4 * g + 2]), silu_mul(gt[4 * g + 3], up[4 * g + 3]));
+          *reinterpret_cast<uint2*>(dst + g * 16 * 8) = v;
+        }
+      }
+    if (!has_next) break;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) acc[i][j] = f32x16_t{};
+#pragma unroll
+    for (int q = 0; q < kLoadsA; ++q) cw[q] = nw[q];
+#pragma unroll
+    for (int q = 0; q < kLoadsB; ++q) ct[q] = nt[q];
+    item = nxt;
+    first = false;
+  }
+  // the ring loads of the last four steps land before the workgroup's LDS is
+  // released
+  __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+#undef MOE_STEP
+#undef MOE_INTERLEAVE
+#undef MOE_MMA_HALF
+#undef MOE_READ_HALF
+}
+
 // Combine of a prefill block from bf16 gate-weighted expert rows: one
 // wavefront per token row, m = sum of the shared rows then the routed rows in
 // ascending expert order (fp32, fixed order), x' = round(x + m).  A token's
@@ -443,7 +701,10 @@ int gemm_max_tiles(const Dims& d, int T) {
   return d.S * ((T + kBT - 1) / kBT) + (T * d.k) / kBT + d.E;
 }
 
-size_t gemm_lds_bytes() { return kRingLds > kEpiLds ? kRingLds : kEpiLds; }
+size_t gemm_lds_bytes() {
+  const size_t a = kRingLds > kEpiLds ? kRingLds : kEpiLds;
+  return a > kPersistLds ? a : kPersistLds;
+}
 
 hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipStream_t s) {
   // the step schedule needs a multiple of 4 steps (H and I multiples of 128)
@@ -453,7 +714,9 @@ hipError_t launch_grouped_gemm(const Dims& d, const GemmParams& p, int up, hipSt
   const int64_t grid = (items + kXcds - 1) / kXcds * kXcds;
   const size_t smem = gemm_lds_bytes();
   const dim3 g(static_cast<unsigned>(grid)), b(kGemmThreads);
-  if (up)
+  if (up && d.H / kKStep >= kPersistMinSteps) {
+    hipLaunchKernelGGL(k_gemm_up_persist, dim3(kPersistWgs), b, kPersistLds, s, d, p);
+  } else if (up)
     hipLaunchKernelGGL((k_grouped_gemm<true, 0>), g, b, smem, s, d, p);
   else if (p.yb)
     hipLaunchKernelGGL((k_grouped_gemm<false, 2>), g, b, smem, s, d, p);

@@ -240,6 +240,15 @@ def test_block_forward_grouped_gemm_small(T):
     _prefill_case_check(workloads.build_case(w), f"gemm small T{T}")
 
 
+@pytest.mark.parametrize("H,I,T", [(512, 896, 2048), (512, 128, 600), (1280, 256, 1500)])
+def test_block_forward_persistent_up_gemm(H, I, T):
+    """Gate+up GEMM as the persistent kernel (reductions of 16 or more steps):
+    up to a few items per workgroup carried through one LDS ring, ragged last
+    token tiles, shared and routed items mixed within a workgroup's range."""
+    w = workloads.small_bf16(B=T, K=0, L=1, H=H, I=I, seed_id=90 + H + I).with_(has_lm_head=False, drafts="none")
+    _prefill_case_check(workloads.build_case(w), f"persistent up H{H} I{I} T{T}")
+
+
 def test_verify_step_on_the_grouped_gemm_path():
     """A verify step of 520 rows (130 sequences x 4) over two blocks runs its
     experts on the grouped GEMM with float32 expert rows, combined by the next
