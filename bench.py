@@ -665,7 +665,9 @@ def main():
         ev.destroy(e)
 
     if prefill:
-        kname, kfile = "k_grouped_gemm<up>", "k_prefill.hip"
+        # the gate+up GEMM: the persistent kernel from 16 reduction steps (H >= 512)
+        kname = "k_gemm_up_persist" if w.H >= 512 else "k_grouped_gemm<up>"
+        kfile = "k_prefill.hip"
         kflops = (w.T * w.k + w.S * w.T) * 2 * (2 * w.I * w.H)
         achieved = kflops / (kern_avg_ms * 1e-3) / 1e12
         roof = {"bound": "mfma", "achieved": achieved, "peak": MFMA_BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
