@@ -8,7 +8,9 @@
 // CU keep the most weight bytes in flight).  Its four wavefronts split the
 // reduction dimension in four and each loads its quarter of the weight tiles
 // straight into registers with coalesced 1 KiB reads (weights are pre-tiled in
-// MFMA operand order), keeps them there, and loops over the expert's tokens 16
+// MFMA operand order; non-temporal, being read once per step, so the stream
+// does not evict the activation rows every token tile re-reads from L2),
+// keeps them there, and loops over the expert's tokens 16
 // at a time (tokens gathered from
 // the permutation; columns past the expert's tokens repeat its last token, so
 // they compute that token's values bit for bit and store them to its row
@@ -182,8 +184,8 @@ __global__ __launch_bounds__(kBlock, RPW == 1 ? 1 : 2) void k_up_mfma(Dims d, Ex
     const bf16_t* u = reinterpret_cast<const bf16_t*>(p.w_up) + tile * kFragElems + lane * 8;
 #pragma unroll
     for (int i = 0; i < KW; ++i) {
-      ag[r][i] = load_frag(g + i * kFragElems);
-      au[r][i] = load_frag(u + i * kFragElems);
+      ag[r][i] = load_frag_stream(g + i * kFragElems);
+      au[r][i] = load_frag_stream(u + i * kFragElems);
     }
   }
 
@@ -296,7 +298,7 @@ __global__ __launch_bounds__(kBlock) void k_down_mfma(Dims d, ExpertParams p, in
     const int64_t tile = (static_cast<int64_t>(si.expert) * (d.H / kTile) + rb * RPW + r) * KT + kt0;
     const bf16_t* w = reinterpret_cast<const bf16_t*>(p.w_down) + tile * kFragElems + lane * 8;
 #pragma unroll
-    for (int i = 0; i < KW; ++i) a[r][i] = load_frag(w + i * kFragElems);
+    for (int i = 0; i < KW; ++i) a[r][i] = load_frag_stream(w + i * kFragElems);
   }
 
   // activation fragments of a token tile (column lane % 16) given the pair of

@@ -5,6 +5,8 @@
 //     (shared + gate-weighted routed expert outputs in a fixed order, the
 //     residual add and its rounding) and applies the final RMSNorm;
 //  2. an LM-head kernel streams the vocabulary matrix from HBM exactly once
+//     (non-temporal loads: read once, it should not evict the activation
+//     fragments and keys the workgroups keep re-reading from L2)
 //     and folds each token's best (logit, lowest id) into one of kKeySlots
 //     64-bit keys with an atomicMax (logits are never written):
 //       * up to 16 tokens: k_lmhead_stream, persistent, two 256-thread
@@ -136,7 +138,7 @@ __global__ __launch_bounds__(kBlock) void k_lmhead_mfma(Dims d, LmHeadParams p) 
 #pragma unroll
   for (int r = 0; r < R; ++r)
 #pragma unroll
-    for (int kk = 0; kk < KC; ++kk) a_cur[r][kk] = load_frag(a_ptr(r, kk));
+    for (int kk = 0; kk < KC; ++kk) a_cur[r][kk] = load_frag_stream(a_ptr(r, kk));
   stage_store(0, st);
   __syncthreads();
 
@@ -147,7 +149,7 @@ __global__ __launch_bounds__(kBlock) void k_lmhead_mfma(Dims d, LmHeadParams p) 
 #pragma unroll
       for (int r = 0; r < R; ++r)
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk) a_nxt[r][kk] = load_frag(a_ptr(r, (c + 1) * KC + kk));
+        for (int kk = 0; kk < KC; ++kk) a_nxt[r][kk] = load_frag_stream(a_ptr(r, (c + 1) * KC + kk));
     }
     const bf16_t* bb = bl + (c & 1) * kStage * 8;
 #pragma unroll
@@ -422,7 +424,7 @@ __global__ __launch_bounds__(kBlock, 2) void k_lmhead_stream(Dims d, LmHeadParam
     for (int r = 0; r < RPW; ++r) {
       const bf16_t* w = lm + (static_cast<int64_t>(u * RPW + r) * KT + kt0) * kFragElems + lane * 8;
 #pragma unroll
-      for (int i = 0; i < KQ; ++i) a[r][i] = load_frag(w + i * kFragElems);
+      for (int i = 0; i < KQ; ++i) a[r][i] = load_frag_stream(w + i * kFragElems);
     }
   };
 
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadP
 #pragma unroll
     for (int r = 0; r < R; ++r) {
       const int vt = min(a_u * kUnitTiles + wave * R + r, n_tiles - 1);
-      a[r] = load_frag(lm + (static_cast<int64_t>(vt) * KT + a_kt) * kFragElems + lane * 8);
+      a[r] = load_frag_stream(lm + (static_cast<int64_t>(vt) * KT + a_kt) * kFragElems + lane * 8);
     }
     if (++a_kt == KT) {
       a_kt = 0;
