@@ -55,16 +55,12 @@ __device__ __forceinline__ bf16x8_t load_frag(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8_t, v);
 }
 // The same 16-byte loads with the non-temporal hint, for data a step reads
-// once (decode expert weights, LM-head rows, KV-cache rows): streamed through
+// once in whole lines (decode expert weights, LM-head rows): streamed through
 // the caches at low priority, they no longer push out what the step reads
 // again and again (activation rows, pair lists, the router matrix).
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ bf16x8_t load_frag_stream(const bf16_t* p) {
   return __builtin_bit_cast(bf16x8_t, __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p)));
-}
-__device__ __forceinline__ uint4 load_stream16(const bf16_t* p) {
-  const u32x4_t v = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(p));
-  return make_uint4(v.x, v.y, v.z, v.w);
 }
 __device__ __forceinline__ bf16x8_t zero_frag() {
   return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0));

@@ -5,8 +5,10 @@
 // At decode sizes attention is a stream over the KV cache (512 B per position
 // and head), so the work is split over positions: workgroup (g, h, b) takes
 // the 64-position tiles g*4 + w, g*4 + w + 4G, ... of sequence b and head h,
-// one tile per wavefront at a time, every load of a tile issued first (cache
-// rows with the non-temporal hint: each is read once per step):
+// one tile per wavefront at a time, every load of a tile issued first (with
+// the default cache policy: a key row's 128-byte lines are read in two halves
+// by two loads, and with the non-temporal hint a line could leave the cache
+// between them -- 10 % more HBM traffic, no faster):
 //   scores: 16 MFMAs 16x16x32 per tile with the keys as the A operand (bf16
 //           rows as cached, 16 B a lane) and the bf16 queries as B (columns
 //           >= K1 zero), float32 accumulation;
@@ -99,14 +101,15 @@ __global__ __launch_bounds__(kBlock) void k_attn_split(AttnParams p) {
     for (int pt = 0; pt < 4; ++pt) {
       const bf16_t* krow = kc + static_cast<int64_t>(min(t0 + pt * 16 + lane % 16, len - 1)) * kHeadDim;
 #pragma unroll
-      for (int ks = 0; ks < 4; ++ks) kf[pt][ks] = load_stream16(krow + ks * 32 + (lane / 16) * 8);
+      for (int ks = 0; ks < 4; ++ks) kf[pt][ks] = *reinterpret_cast<const uint4*>(krow + ks * 32 + (lane / 16) * 8);
     }
     // value rows 4 i + lane / 16, 16 bytes a lane: 16 loads cover the tile, so
     // a tile's 32 loads stay under the per-wavefront limit of loads in flight
     uint4 vv[kPosTile / 4];
 #pragma unroll
     for (int i = 0; i < kPosTile / 4; ++i)
-      vv[i] = load_stream16(vc + static_cast<int64_t>(min(t0 + 4 * i + lane / 16, len - 1)) * kHeadDim + 8 * (lane % 16));
+      vv[i] = *reinterpret_cast<const uint4*>(
+          vc + static_cast<int64_t>(min(t0 + 4 * i + lane / 16, len - 1)) * kHeadDim + 8 * (lane % 16));
     // scores: sc[pt][i] = q_jq . k at position t0 + 16 pt + 4 (lane / 16) + i
     f32x4_t sc[4];
 #pragma unroll
