@@ -20,7 +20,8 @@
 // the permutation kernel the slots are launched busiest first (the active
 // list is ordered by token count), so the longest workgroups do not trail
 // the kernel; the shared experts, which see every token, split their token
-// tiles over up to two workgroups (see split_index).
+// tiles over more workgroups only beyond eight tiles (see split_index and
+// token_split).
 //   up:   a[pair][i] = round(silu(Wg x)[i] * (Wu x)[i])        (pairs of the slot)
 //   down: y[pair][h] = (Wd a)[h]                                 (float32)
 // Shared experts occupy slots 0..S-1 and see every token.  The page "Jina AI
@@ -400,11 +401,18 @@ __global__ __launch_bounds__(kBlock) void k_down_f32(Dims d, ExpertParams p) {
   }
 }
 
-// Ways to split a shared expert's T tokens over workgroups: two once there
-// are more than two token tiles.  With the token-tile loop pipelined a tile
-// costs about one activation round trip, and four ways (a quarter of the
-// first workgroups then fetch nothing from HBM) measured slower than two.
-int token_split(int T) { return std::min(2, std::max(1, (T + 2 * kTile - 1) / (2 * kTile))); }
+// Ways to split a shared expert's T tokens over workgroups: one up to eight
+// token tiles (128 rows), then as many as keep a workgroup at eight tiles, at
+// most four.  With the token-tile loop pipelined and the weights streamed
+// non-temporally (the activation rows stay in L2) a tile costs well under one
+// HBM round trip, and at 128 rows one workgroup per (shared slot, row tile)
+// beat two (the second fetches its weights from L2 and then only runs tiles).
+int token_split(int T) { return std::min(4, std::max(1, (T + 8 * kTile - 1) / (8 * kTile))); }
+// A linear layer's few slots (three for q/k/v, one for the output
+// projection) give too few workgroups to fill the chip at one per (slot, row
+// tile): a way per two token tiles, at most four (one attention layer at
+// batch 32 took 286 us with one way, 274 us with two, 269 us with four).
+int linear_split(int T) { return std::min(4, std::max(1, (T + 2 * kTile - 1) / (2 * kTile))); }
 // grid for R row tiles: the shared part (whole groups of 8 pairs, `split`
 // ways), then one workgroup per routed (slot, row tile) -- for at most T*k
 // routed slots, as many as T tokens can activate (the rest would only read
@@ -460,7 +468,7 @@ template <int EPI>
 hipError_t linear_launch(const Dims& d, const ExpertParams& p, const EpiParams& e, hipStream_t s) {
   constexpr int RPW = 2;
   if (d.E != 0 || d.k != 0 || d.I != d.H || d.H % (kTile * RPW) != 0 || d.H % kHeadDim != 0) return hipErrorInvalidValue;
-  const int split = token_split(p.T);
+  const int split = linear_split(p.T);
   const int grid = split_grid(d, d.H / (kTile * RPW), split, p.T);
   switch (d.I / (kKStep * 4)) {
     case 2: hipLaunchKernelGGL((k_down_mfma<2, RPW, EPI>), dim3(grid), dim3(kBlock), 0, s, d, p, split, e); break;
