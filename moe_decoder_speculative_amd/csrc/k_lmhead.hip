@@ -13,7 +13,8 @@
 //         workgroups per CU; the four wavefronts split the reduction and the
 //         next unit's weight tiles are loaded while the current one is reduced;
 //       * 17..128 tokens: k_lmhead_wide, persistent, one 512-thread workgroup
-//         per CU with register rings of weight and activation fragments;
+//         per CU with a register ring of weight fragments and the activation
+//         fragments staged in LDS four k-steps at a time;
 //       * more: k_lmhead_mfma, activation fragments staged in LDS;
 //  3. k_accept reduces the key copies into the greedy picks, leaves them at
 //     zero for the next step and runs the acceptance: the longest prefix of
@@ -491,46 +492,43 @@ __global__ __launch_bounds__(kBlock, 2) void k_lmhead_stream(Dims d, LmHeadParam
 
 // ------------------------------------------------- 17..128 tokens ----
 // One 512-thread workgroup per CU, persistent over units of 8R row tiles
-// (R = 2: with R = 4 the accumulators and rings of 8 token tiles spill, and
-// at 2 token tiles R = 4 -- 16 KiB in flight per wavefront -- was slower: a
-// draft call's head 64.5 -> 68.8 % of the HBM peak with R = 2); wavefront
-// w owns the unit's row tiles Rw..Rw+R-1 over the whole reduction, so its
-// accumulators (R row tiles x NT token tiles) never leave registers.  Per
-// 32-wide k-step g:
-//  * weight fragments go straight to registers from a ring of P = 4 steps in
-//    flight per wavefront (PR = 8 KiB, 64 KiB per CU), which keeps HBM busy
-//    through the barriers (at 8 token tiles a ring of
-//    8 steps, 128 KiB in flight per CU, only lengthened the queues: the
-//    head took 72.6 us at 128 tokens against 70.3 us with 4);
-//  * the activation fragments of all NT token tiles (NT KiB, shared by the 8
-//    wavefronts) come from a double-buffered LDS stage; wavefront w loads
-//    token tile w % NT of step g into a ring of P registers P steps ahead and
-//    writes it to the LDS stage during step g - 1.  One barrier per step.
-// All loads are ordinary register loads, so the compiler's own wait counts
-// are exact.
+// (R = 2: with R = 4 the accumulators and rings of 8 token tiles spill);
+// wavefront w owns the unit's row tiles Rw..Rw+R-1 over the whole
+// reduction, so its accumulators (R row tiles x NT token tiles) never leave
+// registers.  The k-steps go in groups of four:
+//  * weight fragments go straight to registers from a ring of four steps
+//    per wavefront (8 KiB, 64 KiB per CU), each slot refilled with the next
+//    group's step as soon as it is used (a ring of eight steps measured no
+//    better);
+//  * the activation fragments of all NT token tiles for the group's four
+//    steps (4 x NT KiB, shared by the 8 wavefronts) come from a
+//    double-buffered LDS stage; wavefront w loads token tile w % NT of the
+//    four steps of group q + 2 at the start of group q and writes them to
+//    the stage during group q + 1.  One barrier per group: with one per step
+//    (the previous design) a late weight fragment of one wavefront held the
+//    other seven back every step, and the B = 32 head took 70.5 against
+//    64.9 us.
+// Every load is unconditional (rows past the matrix clamped, activation
+// steps wrapping) and the loop is entered in the state it leaves, so the
+// compiler's own wait counts are exact.
 constexpr int kWideThreads = 512;
 constexpr int kWideWaves = kWideThreads / kWave;
 constexpr int kWideStageBytes = kWideWaves * 1024;  // one fragment slot per wavefront
+constexpr int kWideGroupBytes = 4 * kWideStageBytes;  // four steps of fragment slots (one LDS stage)
 
-template <int NT, int R, int P>
+template <int NT, int R>
 __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadParams p) {
   static_assert(NT >= 1 && NT <= kWideWaves, "one activation fragment per wavefront and step");
-  static_assert(P == 4 || P == 8, "weight ring of one or two groups of four steps");
   constexpr int kUnitTiles = kWideWaves * R;
-  __shared__ __align__(16) unsigned char bring[2 * kWideStageBytes];
+  __shared__ __align__(16) unsigned char bring[2 * kWideGroupBytes];
   __shared__ uint64_t wbest[kWideWaves][NT * kTile];
-  // the wavefront index as a scalar: addresses and branches that depend only
-  // on it stay scalar
   const int lane = threadIdx.x % kWave, wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   const int H = d.H, KT = H / kKStep;
   const int n_tiles = d.Vpad / kTile;
   const int n_units = (n_tiles + kUnitTiles - 1) / kUnitTiles;
-  const int total = ((n_units - 1 - static_cast<int>(blockIdx.x)) / static_cast<int>(gridDim.x) + 1) * KT;
+  const int groups = ((n_units - 1 - static_cast<int>(blockIdx.x)) / static_cast<int>(gridDim.x) + 1) * KT / 4;
   const bf16_t* lm = reinterpret_cast<const bf16_t*>(p.lm);
 
-  // Weight fragments of this workgroup's steps in order (step g: its
-  // (g / KT)-th unit, k-step g % KT), through a scalar cursor.  Row tiles past
-  // the matrix are clamped to its last tile (results discarded).
   int a_u = blockIdx.x, a_kt = 0;
   auto load_a_next = [&](bf16x8_t (&a)[R]) {
 #pragma unroll
@@ -543,20 +541,21 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadP
       a_u += gridDim.x;
     }
   };
-  // activation fragment (token tile w % NT) of step g for wavefront w, into
-  // slot w of a stage (slots >= NT are never read: every wavefront runs the
-  // same code, which keeps the loads free of branches and the compiler's wait
-  // counts exact).  Rows past T repeat row T - 1 (results discarded).
   const int btok = min((wave % NT) * kTile + lane % kTile, p.T - 1);
   const bf16_t* bsrc = reinterpret_cast<const bf16_t*>(p.xf) + static_cast<int64_t>(btok) * H + (lane / kTile) * 8;
-  int b_kt = 0;  // k-step of the next activation fragment to load
-  auto load_b_next = [&]() -> bf16x8_t {
-    const bf16x8_t v = load_frag(bsrc + b_kt * kKStep);
-    if (++b_kt == KT) b_kt = 0;
-    return v;
+  int b_kt = 0;
+  auto load_b_group = [&](bf16x8_t (&pb)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      pb[j] = load_frag(bsrc + b_kt * kKStep);
+      if (++b_kt == KT) b_kt = 0;
+    }
   };
-  auto put_b = [&](int g, const bf16x8_t& v) {
-    *reinterpret_cast<bf16x8_t*>(bring + (g & 1) * kWideStageBytes + wave * 1024 + lane * 16) = v;
+  auto put_b_group = [&](int q, const bf16x8_t (&pb)[4]) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      *reinterpret_cast<bf16x8_t*>(bring + (q & 1) * kWideGroupBytes + j * kWideStageBytes + wave * 1024 + lane * 16) =
+          pb[j];
   };
 
   f32x4_t acc[R][NT];
@@ -564,17 +563,10 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadP
   for (int r = 0; r < R; ++r)
 #pragma unroll
     for (int nt = 0; nt < NT; ++nt) acc[r][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  // End of a unit: each lane folds its R x 4 rows of every token tile into
-  // one candidate (largest logit; on equal logits the first, which is the
-  // lowest row) and merges its key into the lane's running best; lanes and
-  // wavefronts meet once, after the last unit.  In the unit holding the end
-  // of the vocabulary, rows past V take -inf and a lane whose candidate is
-  // such a row contributes no key.
   uint64_t lbest[NT];
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) lbest[nt] = 0ull;
-  int cur_u = blockIdx.x;  // unit being accumulated
+  int cur_u = blockIdx.x;
   auto fold_unit = [&](auto masked) {
     constexpr bool kMasked = decltype(masked)::value;
     const int row0 = (cur_u * kUnitTiles + wave * R) * kTile + 4 * (lane / kTile);
@@ -601,85 +593,47 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadP
       for (int r = 0; r < R; ++r) acc[r][nt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
     }
   };
-  auto unit_end = [&]() {
-    if ((cur_u + 1) * kUnitTiles * kTile > d.V) {
-      fold_unit(std::true_type{});
-    } else {
-      fold_unit(std::false_type{});
-    }
-    cur_u += gridDim.x;
-  };
 
-  // activation ring first: slot j holds the fragment of a step g = j mod P
-  //    (loaded for every g < total + P: rows repeat, so reads stay in bounds);
-  // the first step then waits for its own fragment, not for the weight ring
-  bf16x8_t pb[P];
+  // prologue in the loop's steady order: group 0's activations (written to
+  // stage 0 now), group 1's (written during group 0), then the weights of
+  // group 0's four steps
+  bf16x8_t pb[4], a[4][R];
+  load_b_group(pb);
+  bf16x8_t pn[4];
+  load_b_group(pn);
 #pragma unroll
-  for (int j = 0; j < P; ++j) pb[j] = load_b_next();
-  // weight ring primed, unconditionally (a conditional load would make the
-  // compiler's wait before the first stage write drain the whole ring): steps
-  // past the workgroup's last read clamped rows and are never used, and the
-  // refills below only run for steps that exist
-  bf16x8_t a[P][R];
+  for (int j = 0; j < 4; ++j) load_a_next(a[j]);
+  put_b_group(0, pb);
 #pragma unroll
-  for (int j = 0; j < P; ++j) load_a_next(a[j]);
-  put_b(0, pb[0]);
-  pb[0] = load_b_next();
+  for (int j = 0; j < 4; ++j) pb[j] = pn[j];
   lds_barrier();
 
-  // Step G on ring slot J = G mod P: stage G is in LDS.  Write step G+1's
-  // fragment (slot J+1) to the other stage and refill that slot with step
-  // G+1+P; MFMAs on stage G with weight slot J, refilled with step G+P;
-  // barrier.  The two rings have the same depth: loads complete in order, so
-  // waiting for step G+1's fragment (issued P-1 steps earlier) leaves the
-  // weight loads of the P-1 steps after it in flight.  In a steady group (ST
-  // = true, a literal) the step and every refill exist; otherwise each is
-  // tested at run time.  Activation loads past the last step read valid rows
-  // and are never used.
-#define MOE_WIDE_STEP(G, J, ST)                                                                    \
-  if ((ST) || (G) < total) {                                                                       \
-    if ((ST) || (G) + 1 < total) put_b((G) + 1, pb[((J) + 1) % P]);                                \
-    pb[((J) + 1) % P] = load_b_next();                                                             \
-    const unsigned char* st_ = bring + ((G) & 1) * kWideStageBytes + lane * 16;                    \
-    _Pragma("unroll") for (int nt = 0; nt < NT; ++nt) {                                            \
-      const bf16x8_t b_ = *reinterpret_cast<const bf16x8_t*>(st_ + nt * 1024);                     \
-      _Pragma("unroll") for (int r = 0; r < R; ++r)                                                \
-        acc[r][nt] = mfma16(a[J][r], b_, acc[r][nt]);                                              \
-    }                                                                                              \
-    if ((ST) || (G) + P < total) load_a_next(a[J]);                                                \
-    lds_barrier();                                                                                 \
+  for (int q = 0; q < groups; ++q) {
+    // group q + 1's activations to the other stage (read by nobody since the
+    // last barrier), then group q + 2's requested
+    put_b_group(q + 1, pb);
+    load_b_group(pb);
+    const unsigned char* st = bring + (q & 1) * kWideGroupBytes + lane * 16;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+#pragma unroll
+      for (int nt = 0; nt < NT; ++nt) {
+        const bf16x8_t b_ = *reinterpret_cast<const bf16x8_t*>(st + j * kWideStageBytes + nt * 1024);
+#pragma unroll
+        for (int r = 0; r < R; ++r) acc[r][nt] = mfma16(a[j][r], b_, acc[r][nt]);
+      }
+      load_a_next(a[j]);  // the next group's step j (clamped past the end)
+    }
+    if (((q + 1) * 4) % KT == 0) {
+      if ((cur_u + 1) * kUnitTiles * kTile > d.V)
+        fold_unit(std::true_type{});
+      else
+        fold_unit(std::false_type{});
+      cur_u += gridDim.x;
+    }
+    lds_barrier();
   }
-  // Four steps on ring slots J..J+3 (KT is a multiple of 4, so a unit can
-  // only end after a fourth step).
-#define MOE_WIDE_QUAD(G, J, ST)                                                                    \
-  {                                                                                                \
-    MOE_WIDE_STEP(G, J, ST)                                                                        \
-    MOE_WIDE_STEP((G) + 1, (J) + 1, ST)                                                            \
-    MOE_WIDE_STEP((G) + 2, (J) + 2, ST)                                                            \
-    MOE_WIDE_STEP((G) + 3, (J) + 3, ST)                                                            \
-    if (((ST) || (G) + 4 <= total) && ((G) + 4) % KT == 0) unit_end();                             \
-  }
-  // A group: P steps, one pass over the ring slots.
-#define MOE_WIDE_GROUP(G, ST)                                                                      \
-  {                                                                                                \
-    MOE_WIDE_QUAD(G, 0, ST)                                                                        \
-    if (P == 8) MOE_WIDE_QUAD((G) + 4, 4 % P, ST)                                                  \
-  }
-  // The first steady group is peeled so that the loop is only entered in the
-  // state it leaves (the compiler's wait counts at the loop head hold for
-  // every path into it).
-  int g = 0;
-  if (total >= 2 * P) {
-    MOE_WIDE_GROUP(0, true)
-    for (g = P; g + 2 * P <= total; g += P) MOE_WIDE_GROUP(g, true)
-  }
-  for (; g < total; g += P) MOE_WIDE_GROUP(g, false)
-#undef MOE_WIDE_GROUP
-#undef MOE_WIDE_QUAD
-#undef MOE_WIDE_STEP
 
-  // lanes l, l + 16, l + 32, l + 48 hold token l % 16's candidates of the
-  // wavefront's rows; then the wavefronts' bests meet in LDS
 #pragma unroll
   for (int nt = 0; nt < NT; ++nt) {
     uint64_t best = lbest[nt];
@@ -701,13 +655,12 @@ __global__ __launch_bounds__(kWideThreads, 1) void k_lmhead_wide(Dims d, LmHeadP
   }
 }
 
-template <int NT, int R, int P>
+template <int NT, int R>
 hipError_t lm_wide_nt(const Dims& d, const LmHeadParams& p, hipStream_t s) {
-  // persistent: one workgroup per CU
   constexpr int kUnitTiles = kWideWaves * R;
   const unsigned units = (d.Vpad / kTile + kUnitTiles - 1) / kUnitTiles;
   const unsigned grid = units < static_cast<unsigned>(d.n_cu) ? units : static_cast<unsigned>(d.n_cu);
-  hipLaunchKernelGGL((k_lmhead_wide<NT, R, P>), dim3(grid), dim3(kWideThreads), 0, s, d, p);
+  hipLaunchKernelGGL((k_lmhead_wide<NT, R>), dim3(grid), dim3(kWideThreads), 0, s, d, p);
   return hipGetLastError();
 }
 
@@ -773,9 +726,9 @@ hipError_t launch_lmhead(const Dims& d, const LmHeadParams& p, hipStream_t s) {
     }
   }
   const int nt = (p.T + kTile - 1) / kTile;
-  if (nt <= 2) return lm_wide_nt<2, 2, 4>(d, p, s);
-  if (nt <= 4) return lm_wide_nt<4, 2, 4>(d, p, s);
-  if (nt <= 8) return lm_wide_nt<8, 2, 4>(d, p, s);
+  if (nt <= 2) return lm_wide_nt<2, 2>(d, p, s);
+  if (nt <= 4) return lm_wide_nt<4, 2>(d, p, s);
+  if (nt <= 8) return lm_wide_nt<8, 2>(d, p, s);
   return lm_nt<8, 4, 2>(d, p, s);
 }
 
