@@ -8,6 +8,8 @@ the full-size one-layer workloads; a cache of 32,768 positions (the largest
 accepted) at full width; and sampled sequences of the 12-layer batch-32 step
 with attention (a complete verify forward of the pages' decoder shape).  Bar: tests/parity.py, check_attn_step_teacher_forced.
 """
+import functools
+
 import numpy as np
 import pytest
 
@@ -43,6 +45,13 @@ def _prefix(w, positions, seqs=None):
             vc[i, :, :positions[b]] = O.as_f32(v)
         kv0.append((kc, vc))
     return kv0, bits
+
+
+@functools.lru_cache(maxsize=1)
+def _stack_weights(w):
+    """Weights of a workload, kept for the next test of the same workload (the
+    12-layer ones take a minute or two to generate)."""
+    return synth.gen_weights(w)
 
 
 def _ash(w):
@@ -202,6 +211,66 @@ def test_attention_stack12_b32_sampled():
 
 
 @pytest.mark.slow
+def test_attn_stack12_margin_sequences_end_to_end():
+    """The 12-layer step with attention, end to end against the oracle's own
+    step: single-row sequences (K = 0, greedy decoding through the whole
+    stack) whose every layer's top-k gap and head gap exceed 1.5 times the
+    MoE-only stack's drift schedule along the oracle's trajectory
+    (tests/golden/attn_stack12_b32_zipf_seqs.json, written from the oracle
+    and the seeded generators only), each with its own cache part-way
+    through a page.  Every layer's expert sets and the picks bit for bit."""
+    _torch()
+    import json
+    import os
+    with open(os.path.join(workloads.GOLDEN, "attn_stack12_b32_zipf_seqs.json")) as f:
+        spec = json.load(f)
+    base = synth.WORKLOADS[spec["workload"]]
+    seqs = spec["sequences"]
+    n = len(seqs)
+    cands = [int(q["candidate"]) for q in seqs]
+    positions = np.array([int(q["length"]) for q in seqs], np.int32)
+    w = base.with_(name=base.name + "_margin_seqs", B=n, K=0, T=n)
+    parity.say(f"[attn margin] {w.name}: B={n} K=0 L={w.L} P={w.P} candidates {cands} positions "
+               f"{positions.tolist()} entry=moe_verify_step_kv")
+    weights = _stack_weights(base)
+    noise = synth.HiddenNoise(base)
+    offset = synth.hidden_offset(base, weights, noise)
+    chunk = spec["chunk"]
+    raw = np.concatenate([noise.draw(chunk) for _ in range(max(cands) // chunk + 1)])[cands]
+    hidden = synth.to_storage(raw + offset, w.dtype)
+    caches = []
+    for l in range(w.L):
+        kc = np.zeros((n, w.n_heads, w.P, 128), np.float32)
+        vc = np.zeros_like(kc)
+        for i, c in enumerate(cands):
+            k, v = synth.kv_prefix(base, l, c, int(positions[i]))
+            kc[i, :, :positions[i]] = O.as_f32(k)
+            vc[i, :, :positions[i]] = O.as_f32(v)
+        caches.append((kc, vc))
+    shp = workloads.shape_of(w)
+    ref = A.verify_step_attn(shp, _ash(w), weights, hidden, np.zeros((n, 0), np.int32), positions,
+                             [(k.copy(), v.copy()) for k, v in caches], n, 0)
+    for l, blk in enumerate(ref.blocks):  # the schedule holds along the oracle's own trajectory
+        assert O.topk_margin(blk.z, shp.k).min() >= spec["router_margin"][l], f"layer {l}: margin below schedule"
+    vm = VerifyModel(w, weights, max_tokens=n, max_seqs=n)
+    try:
+        for l in range(w.L):
+            for i, c in enumerate(cands):
+                k, v = synth.kv_prefix(base, l, c, int(positions[i]))
+                vm.kv_write(l, i, k, v)
+        out = _gpu_step(vm, w, hidden, None, positions, n, 0)
+    finally:
+        vm.close()
+    for l, blk in enumerate(ref.blocks):
+        assert np.array_equal(np.sort(out["topk_idx"][l], 1), np.sort(blk.idx, 1)), f"layer {l}: expert sets differ"
+    assert np.array_equal(out["tstar"], ref.tstar), f"picks differ: {out['tstar']} vs {ref.tstar}"
+    assert np.array_equal(out["counts"], ref.counts) and np.array_equal(out["committed"].reshape(-1),
+                                                                       ref.committed.reshape(-1))
+    parity.say(f"[attn margin] ok: {n} sequences x {w.L} layers, expert sets and picks equal to the oracle's "
+               f"own step ({n}/{n})")
+
+
+@pytest.mark.slow
 def test_attention_near_max_positions():
     """The largest cache the library accepts -- 32,768 positions, the pages'
     position limit -- at full width (10 heads of 128): one sequence whose
@@ -216,7 +285,7 @@ def _full(w, sample, positions=None):
     seqs = list(range(w.B)) if sample is None else sample
     parity.say(f"[attn full] {w.name}: B={w.B} K={w.K} L={w.L} P={w.P} sampled sequences {seqs} "
                f"positions {positions[seqs].tolist()}")
-    weights = synth.gen_weights(w)
+    weights = _stack_weights(w)
     noise = synth.HiddenNoise(w)
     hidden = synth.to_storage(noise.draw(w.T) + synth.hidden_offset(w, weights, noise), w.dtype)
     K1 = w.K + 1
