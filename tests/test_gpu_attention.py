@@ -220,38 +220,12 @@ def test_attn_stack12_margin_sequences_end_to_end():
     and the seeded generators only), each with its own cache part-way
     through a page.  Every layer's expert sets and the picks bit for bit."""
     _torch()
-    import json
-    import os
-    with open(os.path.join(workloads.GOLDEN, "attn_stack12_b32_zipf_seqs.json")) as f:
-        spec = json.load(f)
-    base = synth.WORKLOADS[spec["workload"]]
-    seqs = spec["sequences"]
-    n = len(seqs)
-    cands = [int(q["candidate"]) for q in seqs]
-    positions = np.array([int(q["length"]) for q in seqs], np.int32)
-    w = base.with_(name=base.name + "_margin_seqs", B=n, K=0, T=n)
+    case = workloads.attn_margin_seqs_case(_stack_weights)  # asserts the schedule along the oracle's trajectory
+    w, base, weights, hidden, positions, cands, ref = (case.w, case.base, case.weights, case.hidden,
+                                                       case.positions, case.cands, case.ref)
+    n = len(cands)
     parity.say(f"[attn margin] {w.name}: B={n} K=0 L={w.L} P={w.P} candidates {cands} positions "
                f"{positions.tolist()} entry=moe_verify_step_kv")
-    weights = _stack_weights(base)
-    noise = synth.HiddenNoise(base)
-    offset = synth.hidden_offset(base, weights, noise)
-    chunk = spec["chunk"]
-    raw = np.concatenate([noise.draw(chunk) for _ in range(max(cands) // chunk + 1)])[cands]
-    hidden = synth.to_storage(raw + offset, w.dtype)
-    caches = []
-    for l in range(w.L):
-        kc = np.zeros((n, w.n_heads, w.P, 128), np.float32)
-        vc = np.zeros_like(kc)
-        for i, c in enumerate(cands):
-            k, v = synth.kv_prefix(base, l, c, int(positions[i]))
-            kc[i, :, :positions[i]] = O.as_f32(k)
-            vc[i, :, :positions[i]] = O.as_f32(v)
-        caches.append((kc, vc))
-    shp = workloads.shape_of(w)
-    ref = A.verify_step_attn(shp, _ash(w), weights, hidden, np.zeros((n, 0), np.int32), positions,
-                             [(k.copy(), v.copy()) for k, v in caches], n, 0)
-    for l, blk in enumerate(ref.blocks):  # the schedule holds along the oracle's own trajectory
-        assert O.topk_margin(blk.z, shp.k).min() >= spec["router_margin"][l], f"layer {l}: margin below schedule"
     vm = VerifyModel(w, weights, max_tokens=n, max_seqs=n)
     try:
         for l in range(w.L):

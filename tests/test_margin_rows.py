@@ -62,3 +62,22 @@ def test_stack12_margin_rows_survive_a_second_float32_evaluation():
     # end-to-end bar for that residual sits above this spread
     spread = parity.rowwise_rel_err(x, case.ref.hidden_out).max()
     assert spread <= 3e-2 < parity.STACK12_HIDDEN_TOL, spread
+
+
+@pytest.mark.slow
+def test_attn_stack12_margin_sequences_meet_their_schedule():
+    """The stored single-row sequences of the 12-layer step with attention
+    reproduce, from their stream positions and cache seeds, rows whose every
+    layer's top-k gap and the head's arg-max gap meet the stored schedule
+    along the oracle's own trajectory; the schedule is 1.5 times the MoE-only
+    stack's at every layer and at the head."""
+    import json
+    import os
+    with open(os.path.join(workloads.GOLDEN, "attn_stack12_b32_zipf_seqs.json")) as f:
+        spec = json.load(f)
+    moe = json.load(open(os.path.join(workloads.GOLDEN, "stack12_b32_zipf_rows.json")))
+    assert np.allclose(spec["router_margin"], 1.5 * np.asarray(moe["router_margin"]))
+    assert np.isclose(spec["head_margin"], 1.5 * moe["head_margin"])
+    case = workloads.attn_margin_seqs_case()      # asserts the schedule
+    assert len(case.cands) == len(set(case.cands)) >= 6
+    assert np.all(case.positions + 1 <= case.w.P)

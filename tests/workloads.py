@@ -133,3 +133,55 @@ def margin_rows_case(name: str) -> Case:
     drafts = synth.make_drafts(w, ref.tstar.reshape(B, K + 1))
     ref.committed, ref.counts = oracle.accept_prefix(ref.tstar.reshape(B, K + 1), drafts)
     return Case(w, shp, weights, hidden, drafts, ref, 0)
+
+
+@dataclass
+class AttnSeqCase:
+    w: synth.Workload            # the workload reshaped to the stored sequences (B = n, K = 0)
+    base: synth.Workload         # the workload the sequences were drawn from
+    weights: dict
+    hidden: np.ndarray           # [n, H] storage dtype
+    positions: np.ndarray        # [n] cache length of each sequence
+    cands: list                  # candidate (stream position and cache seed) of each sequence
+    ref: object                  # the oracle's step (attn_oracle.AttnStepResult)
+
+
+def attn_margin_seqs_case(gen_weights=synth.gen_weights) -> AttnSeqCase:
+    """The 12-layer step with attention on the single-row sequences written by
+    tests/golden/make_attn_margin_rows.py (oracle and seeded generators only):
+    hidden row c of the workload's noise stream, the cache of sequence c at
+    its stored length.  Asserts the stored gap schedule (every layer's top-k
+    gap, the head's arg-max gap) along the oracle's own trajectory."""
+    from oracle import attn_oracle as A
+    with open(os.path.join(GOLDEN, "attn_stack12_b32_zipf_seqs.json")) as f:
+        spec = json.load(f)
+    base = synth.WORKLOADS[spec["workload"]]
+    seqs = spec["sequences"]
+    n = len(seqs)
+    cands = [int(q["candidate"]) for q in seqs]
+    positions = np.array([int(q["length"]) for q in seqs], np.int32)
+    w = base.with_(name=base.name + "_margin_seqs", B=n, K=0, T=n)
+    weights = gen_weights(base)
+    noise = synth.HiddenNoise(base)
+    offset = synth.hidden_offset(base, weights, noise)
+    chunk = spec["chunk"]
+    raw = np.concatenate([noise.draw(chunk) for _ in range(max(cands) // chunk + 1)])[cands]
+    hidden = synth.to_storage(raw + offset, w.dtype)
+    caches = []
+    for l in range(w.L):
+        kc = np.zeros((n, w.n_heads, w.P, 128), np.float32)
+        vc = np.zeros_like(kc)
+        for i, c in enumerate(cands):
+            k, v = synth.kv_prefix(base, l, c, int(positions[i]))
+            kc[i, :, :positions[i]] = oracle.as_f32(k)
+            vc[i, :, :positions[i]] = oracle.as_f32(v)
+        caches.append((kc, vc))
+    shp = shape_of(w)
+    ash = A.AttnShape(H=w.H, n_heads=w.n_heads, d_head=128, P=w.P, theta=w.rope_theta, eps=w.eps, dtype=w.dtype)
+    ref = A.verify_step_attn(shp, ash, weights, hidden, np.zeros((n, 0), np.int32), positions, caches, n, 0)
+    for l, blk in enumerate(ref.blocks):
+        assert oracle.topk_margin(blk.z, w.k).min() >= spec["router_margin"][l], f"layer {l}: margin below schedule"
+    lg = oracle.lm_head_logits(ref.hidden_out, weights["final_gamma"], weights["lm_head"], w.eps,
+                               oracle.storage_round(w.dtype))
+    assert oracle.argmax_margin(lg).min() >= spec["head_margin"], "head margin below schedule"
+    return AttnSeqCase(w, base, weights, hidden, positions, cands, ref)
